@@ -1,0 +1,62 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU)
+and check that the oracle's pins (tests/test_oracle.py) reject it.
+
+This is evidence that the pins constrain every part of the oracle: a
+mistake that survived would mean some part of it is unpinned.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (original text in oracle/attention.py, planted mistake)
+MUTATIONS = [
+    ("s = scale * (q[r0:r1] @ k.T)", "s = (q[r0:r1] @ k.T)"),                     # dropped scale
+    ("lse2[idx] = (m[:, 0] + np.log(l[:, 0])) / _LN2",
+     "lse2[idx] = (m[:, 0] + np.log(l[:, 0]))"),                                   # natural-log LSE
+    ("+ (lk - lq) + 1, 0, lk)", "+ 1, 0, lk)"),                                    # top-left causal
+    ("+ (lk - lq) + 1, 0, lk)", "+ (lk - lq), 0, lk)"),                            # diagonal excluded
+    ("by_req_head.setdefault((b, h // group), []).append(n)\n    for (b, g), members in by_req_head.items():\n        lk = int(seq_lens[b])",
+     "by_req_head.setdefault((b, h % hkv), []).append(n)\n    for (b, g), members in by_req_head.items():\n        lk = int(seq_lens[b])"),  # interleaved GQA map
+    ("physical = int(block_table_row[logical])", "physical = logical"),           # logical as physical page
+    ("o[idx] = (e @ v) / l", "o[idx] = (e @ v)"),                                  # missing normalisation
+    ("e = np.exp(s - m)", "e = np.exp(m - s)"),                                    # flipped sign
+    ("np.exp2(exp.astype(np.float64) - 7.0)", "np.exp2(exp.astype(np.float64) - 8.0)"),  # FNUZ-style bias
+    ("np.exp2(lse_parts - top_safe[None, :])", "np.exp(lse_parts - top_safe[None, :])"),  # merge in wrong base
+    ("alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)",
+     "alpha = np.where(np.isfinite(m), 1.0, 0.0)"),                                # recurrence without rescale
+    ("rows.append(cache[physical, :take, head, :width])",
+     "rows.append(cache[physical, :page_size, head, :width][:take])"),             # harmless: must survive
+]
+
+
+def _run_pins(tmp_root):
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                           os.path.join("tests", "test_oracle.py")],
+                          cwd=tmp_root, env=env, capture_output=True, text=True, timeout=600)
+
+
+@pytest.mark.parametrize("idx", range(len(MUTATIONS)))
+def test_planted_mistake_is_caught(idx, tmp_path):
+    original, planted = MUTATIONS[idx]
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    (tmp_path / "tests").mkdir()
+    for name in ("conftest.py", "test_oracle.py"):
+        shutil.copy(os.path.join(ROOT, "tests", name), tmp_path / "tests" / name)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    src_path = tmp_path / "oracle" / "attention.py"
+    src = src_path.read_text()
+    assert original in src, "mutation anchor not found; update the list"
+    src_path.write_text(src.replace(original, planted, 1))
+    result = _run_pins(tmp_path)
+    harmless = idx == len(MUTATIONS) - 1
+    if harmless:
+        assert result.returncode == 0, result.stdout[-2000:]
+    else:
+        assert result.returncode != 0, f"planted mistake survived the pins: {planted!r}"
