@@ -1,0 +1,197 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one attn_decode_paged call (split kernel + LSE merge, every row of
+the path) on the Qwen3-14B-shaped paged decode: batch 64, one query token,
+40 query / 8 KV heads, head_dim 128, page_size 128, seq_lens uniform on
+[256, 8192], bf16. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(names: list[str]) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "softmax_attention_paged_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, sources: list[str]) -> dict | None:
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
+    WRITE_SIZE), stored under profiles/; only used while the kernel sources
+    are unchanged since the measurement."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(sources):
+        return None
+    return rec
+
+
+def time_events(fn, steps: int, stream) -> float:
+    """Average milliseconds per call of fn, HIP events on `stream`."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(case, budget_s: float = 20.0) -> dict:
+    """The fp64 oracle on the host cores, over whole requests of the same
+    workload until about budget_s of work (at least one request)."""
+    import numpy as np
+    import oracle
+    import torch
+    from threadpoolctl import threadpool_info
+
+    q = oracle.widen_bf16(case.q.view(torch.int16).numpy().view(np.uint16))
+    kc = case.k_cache.view(torch.int16).numpy().view(np.uint16)
+    vc = case.v_cache.view(torch.int16).numpy().view(np.uint16)
+    bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
+    b_n, q_len, hq, _ = case.q.shape
+    row_bytes = 2 * case.k_cache.shape[2] * case.k_cache.shape[3] * 2
+    t0 = time.perf_counter()
+    done_bytes, done_req = 0, 0
+    for b in range(b_n):
+        rows = [(b, t, h) for t in range(q_len) for h in range(hq)]
+        oracle.decode_paged_rows(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal,
+                                 case.head_dim_v, rows, "bf16")
+        done_bytes += int(sl[b]) * row_bytes
+        done_req += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_req} of {b_n} requests ({done_bytes / 1e6:.1f} MB of KV), {dt:.1f} s, "
+                      f"fp64 numpy, BLAS pool of {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=2)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+    import softmax_attention_paged_amd as sap
+    from softmax_attention_paged_amd import inputs
+
+    log("generating inputs ...")
+    case = inputs.qwen3_14b_decode(seed=args.seed)
+    dev = torch.device("cuda:0")
+    c = case.to(dev)
+    b_n, q_len, hq, d = case.q.shape
+    tokens = int(case.seq_lens.sum())
+    kv_bytes = case.kv_read_bytes()
+    alg_bytes = kv_bytes + case.q.numel() * 2 + b_n * q_len * hq * (case.head_dim_v * 2 + 4)
+    flops = tokens * q_len * hq * 2 * (d + case.head_dim_v)
+
+    params = sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                               max_seq_len=c.max_seq_len, softmax_scale=c.scale)
+    plan = sap.decode_plan(params)
+    ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((b_n, q_len, hq, case.head_dim_v), dtype=torch.bfloat16, device=dev)
+    log(f"plan {plan}")
+
+    def step():
+        sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
+                         softmax_scale=c.scale, workspace=ws, out=out)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_events(step, args.steps, stream)
+    # The merge alone on the same partials, to separate the split kernel.
+    s, r = plan["num_splits"], b_n * q_len * hq
+    merge_ms = 0.0
+    if s > 1:
+        o_parts = ws[: s * r * case.head_dim_v * 4].view(torch.float32).view(s, r, case.head_dim_v)
+        lse_parts = ws[s * r * case.head_dim_v * 4: s * r * (case.head_dim_v + 1) * 4].view(torch.float32).view(s, r)
+        mout = torch.empty((r, case.head_dim_v), dtype=torch.bfloat16, device=dev)
+        mlse = torch.empty((r,), dtype=torch.float32, device=dev)
+
+        def merge():
+            sap.merge_lse(o_parts, lse_parts, out=mout, return_lse=False)
+
+        for _ in range(3):
+            merge()
+        merge_ms = time_events(merge, args.steps, stream)
+        del mlse
+    split_ms = ms - merge_ms
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    achieved = alg_bytes / (split_ms * 1e-3) / 1e9
+    sources = ["decode_gqa.hip", "device_common.h", "attn_internal.h"]
+    traffic = load_traffic("decode_gqa_qwen3_14b", sources)
+    line = {
+        "metric": "decode KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "batch": b_n, "q_len": q_len, "num_q_heads": hq,
+                   "num_kv_heads": case.k_cache.shape[2], "head_dim": d, "page_size": case.page_size,
+                   "total_kv_tokens": tokens, "kv_bytes": kv_bytes, "seed": args.seed,
+                   "num_splits": plan["num_splits"], "split_tokens": plan["split_tokens"],
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_gqa_kernel<128>", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_ms, 5),
+                     "merge_avg_launch_ms": round(merge_ms, 5)},
+        "decode_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,222 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) fused softmax-attention forward library.
+ *
+ * What the library computes, for every query row of every head: the softmax
+ * attention o = softmax(scale * q K^T) V over the keys the row may see, and
+ * its base-2 log-sum-exp lse2 = log2(sum_j exp(scale * <q, k_j>))
+ * ("Flywheel Attention: Attention Kernels Built for the TPU", section 1;
+ * "Writing Page Attention with PyPTO", section 1.1; "TokenSpeed-MLA",
+ * kernel capability summary and packed-query paragraph for base-2 LSE).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     keeps none of them after the call returns. Scalars are host values.
+ *   - Work is enqueued on the caller's HIP stream; no call synchronises,
+ *     allocates or frees memory, or reads device memory on the host, so the
+ *     calls may be captured in a HIP graph. The caller keeps every buffer
+ *     alive until the stream has executed the work.
+ *   - Every entry point returns attn_status_t and never aborts, throws or
+ *     prints. Arguments are validated on the host before anything is
+ *     enqueued; on an error nothing is enqueued and attn_last_error() holds
+ *     a one-line reason (thread-local, valid until the next call on that
+ *     thread).
+ *   - Device-array CONTENTS are preconditions, not checked: block_table
+ *     entries a request uses must lie in [0, num_pages); seq_lens and
+ *     cu_seqlens must respect the max_* bounds passed alongside. Violating
+ *     them is undefined behaviour (the kernel would read another request's
+ *     pages: "Writing Page Attention with PyPTO", section 5.2 callout).
+ *   - Table entries past a request's last page, and the slots of its last
+ *     page past its length, are never read ("Writing Page Attention with
+ *     PyPTO", section 9: the tail has two boundaries); their contents,
+ *     NaN included, cannot change the output.
+ *   - Query head h reads KV head h / (num_q_heads / num_kv_heads)
+ *     ("Writing Page Attention with PyPTO", sections 1.2-1.3).
+ *   - A causal row is aligned bottom-right: with Lq query rows and Lk keys,
+ *     row i sees keys j <= Lk - Lq + i ("TokenSpeed-MLA", prefill command
+ *     with bottom-right alignment, and the window_left row bound).
+ *   - A row that sees no key gets o = 0 and lse = -inf ("TokenSpeed-MLA",
+ *     section "SM107 decode").
+ *   - Strides are in ELEMENTS of the stored type. The last dimension of
+ *     every tensor is contiguous, and every row start is 16-byte aligned.
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,          /* null pointer, bad size, inconsistent shapes  */
+  ATTN_ERR_UNSUPPORTED = 2,          /* valid request this build has no kernel for     */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < attn_decode_workspace_size() */
+  ATTN_ERR_HIP = 4                   /* a kernel launch failed                         */
+} attn_status_t;
+
+typedef enum {
+  ATTN_BF16 = 0,       /* bfloat16                                                  */
+  ATTN_FP8_E4M3 = 1,   /* OCP FP8 E4M3 ("fn": no infinities), one scale per tensor  */
+  ATTN_FP32 = 2
+} attn_dtype_t;
+
+/* ------------------------------------------------------------------------
+ * Ragged prefill over dense or paged KV ("TokenSpeed-MLA", kernel capability
+ * summary, MLA Prefill: Q [sum q_lens, h_q, d_qk], K [sum kv_lens, h_k, d_qk],
+ * V [sum kv_lens, h_k, d_v]; the query and key packings may differ).
+ *
+ *   q      bf16 [total_q, Hq, Dqk], strides q_stride_tok / q_stride_head.
+ *   k, v   dense mode (block_table == NULL): bf16 [total_kv, Hkv, D], request
+ *          b owns rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1; the *_page
+ *          strides are ignored.
+ *          paged mode (block_table != NULL): bf16 [num_pages, page_size, Hkv,
+ *          D]; token j of request b is slot j % page_size of page
+ *          block_table[b * block_table_stride + j / page_size]; request b has
+ *          seq_lens_kv[b] keys ("Writing Page Attention with PyPTO", sections
+ *          1.2 and 5.2).
+ *   cu_seqlens_q   int32 [batch + 1], request b owns query rows
+ *                  cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
+ *   max_seqlen_q, max_seqlen_kv   host upper bounds of the per-request lengths.
+ *   causal         0 or 1 (bottom-right aligned).
+ *   o      bf16 [total_q, Hq, Dv], strides o_stride_tok / o_stride_head.
+ *   lse    optional float32 [total_q, Hq] contiguous, base 2; NULL to skip.
+ * Supported: Dqk == Dv in {64, 128, 256}; Hq % Hkv == 0; page_size a power of
+ * two >= 16 (paged mode).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *q;
+  int64_t q_stride_tok, q_stride_head;
+  const void *k, *v;
+  int64_t k_stride_page, k_stride_tok, k_stride_head;
+  int64_t v_stride_page, v_stride_tok, v_stride_head;
+  const int32_t *cu_seqlens_q;
+  const int32_t *cu_seqlens_kv;      /* dense mode only */
+  const int32_t *seq_lens_kv;        /* paged mode only */
+  const int32_t *block_table;        /* NULL selects dense mode */
+  int32_t block_table_stride;        /* elements between consecutive rows of block_table */
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t max_seqlen_q, max_seqlen_kv;
+  float softmax_scale;
+  int32_t causal;
+  void *o;
+  int64_t o_stride_tok, o_stride_head;
+  float *lse;
+} attn_prefill_params;
+
+/* Enqueue ragged prefill. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,
+ * ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP. */
+attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Paged decode with split-KV partials merged by log-sum-exp ("TokenSpeed-MLA",
+ * sections "Decode performance" and "Key Optimization ... Group q_seqlen and
+ * num_heads into BMM1 M"; "Writing Page Attention with PyPTO", sections 1-9).
+ *
+ *   q          bf16 [batch, q_len, Hq, Dqk] contiguous.
+ *   k_cache    [num_pages, page_size, Hkv, Dqk] in kv_dtype, strides k_stride_*.
+ *   v_cache    [num_pages, page_size, Hkv, >= Dv] in kv_dtype, strides
+ *              v_stride_*; V is the first Dv entries of each row. For an
+ *              MLA-shaped latent cache pass the same pointer and strides as
+ *              k_cache with Hkv = 1, Dqk = 576, Dv = 512: K is the whole row
+ *              and V its first 512 entries, read once for both.
+ *   kv_dtype   ATTN_BF16, or ATTN_FP8_E4M3 with per-tensor dequantisation
+ *              scales k_scale / v_scale (value = code * scale); must be 1.0
+ *              for bf16. An MLA-shaped FP8 cache needs k_scale == v_scale.
+ *   seq_lens   int32 [batch]: keys of each request (0 allowed).
+ *   block_table int32, row b at block_table + b * block_table_stride.
+ *   max_seq_len host upper bound of seq_lens; plans the split count.
+ *   q_len      1..4 query tokens per request; row (t, h) of a causal request
+ *              sees keys j <= seq_len - q_len + t.
+ *   num_splits 0 lets the planner choose; otherwise the number of KV splits.
+ *   workspace  device scratch of at least attn_decode_workspace_size(p)
+ *              bytes (may be NULL when that is 0); contents undefined after.
+ *   o          bf16 [batch, q_len, Hq, Dv] contiguous.
+ *   lse        optional float32 [batch, q_len, Hq], base 2; NULL to skip.
+ * Supported: (Dqk, Dv) in {(64,64), (128,128), (256,256)} with bf16 KV and
+ * (576, 512) with Hkv == 1 and bf16 or FP8 KV; Hq % Hkv == 0; page_size a
+ * power of two >= 16.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *q;
+  const void *k_cache, *v_cache;
+  int64_t k_stride_page, k_stride_tok, k_stride_head;
+  int64_t v_stride_page, v_stride_tok, v_stride_head;
+  attn_dtype_t kv_dtype;
+  float k_scale, v_scale;
+  const int32_t *seq_lens;
+  const int32_t *block_table;
+  int32_t block_table_stride;
+  int32_t batch, q_len, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+  int32_t page_size, num_pages, max_seq_len;
+  float softmax_scale;
+  int32_t causal;
+  int32_t num_splits;
+  void *workspace;
+  size_t workspace_bytes;
+  void *o;
+  float *lse;
+} attn_decode_params;
+
+/* How attn_decode_paged will decompose a call (host-only; no device access). */
+typedef struct {
+  int32_t group;          /* G = Hq / Hkv: query heads per KV head                     */
+  int32_t fold;           /* F: query tokens folded with the G heads into MFMA rows     */
+  int32_t q_groups;       /* q_len / F: row blocks per (request, KV head)               */
+  int32_t rows_per_unit;  /* G * F rows computed together                               */
+  int32_t num_splits;     /* S: KV splits per (request, KV head, q-group)               */
+  int32_t split_tokens;   /* keys per split (the last one of a request may be shorter)  */
+  int64_t num_units;      /* workgroups of the split kernel                             */
+  size_t workspace_bytes; /* S * R * (Dv + 1) * 4 with R = batch * q_len * Hq; 0 if S==1 */
+} attn_decode_plan_info;
+
+/* Fill *info with the plan for p. Only shapes and scalars are examined (data
+ * pointers may be NULL). ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_UNSUPPORTED. */
+attn_status_t attn_decode_plan(const attn_decode_params *p, attn_decode_plan_info *info);
+
+/* Workspace bytes attn_decode_paged needs for p (0 when one split suffices or
+ * the shapes are invalid). Only shapes and scalars are examined. */
+size_t attn_decode_workspace_size(const attn_decode_params *p);
+
+/* Enqueue the split kernel and, when S > 1, the merge. Returns ATTN_OK,
+ * ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL
+ * or ATTN_ERR_HIP. */
+attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Merge split partials by log-sum-exp ("TokenSpeed-MLA", section "Decode
+ * performance": a second kernel reduces the split-KV partial results; section
+ * "FP8 split-KV partial storage": partials and log-sum-exp in FP32).
+ *
+ *   o_parts    float32 [num_splits, num_rows, head_dim_v]: per split, the
+ *              output normalised over that split's keys.
+ *   lse_parts  float32 [num_splits, num_rows]: base-2 log-sum-exp of each
+ *              split's scores; -inf marks a split with no key (its o_parts
+ *              row is then not read).
+ *   o          [num_rows, head_dim_v] in o_dtype (ATTN_BF16 or ATTN_FP32):
+ *              sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i.
+ *   lse_out    optional float32 [num_rows]: M + log2(sum_i 2^(lse_i - M)).
+ * A row whose splits are all -inf gets o = 0 and lse = -inf.
+ * Supported: 1 <= num_splits <= 256; head_dim_v a multiple of 4, <= 1024.
+ * ---------------------------------------------------------------------- */
+attn_status_t attn_merge_lse(const float *o_parts, const float *lse_parts,
+                             int32_t num_splits, int64_t num_rows, int32_t head_dim_v,
+                             void *o, attn_dtype_t o_dtype, float *lse_out,
+                             hipStream_t stream);
+
+/* Static name of a status code. */
+const char *attn_status_string(attn_status_t s);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

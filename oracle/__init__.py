@@ -12,6 +12,7 @@ from .attention import (  # noqa: F401
     NEG_INF,
     widen_bf16,
     widen_e4m3fn,
+    widen,
     attention_rows,
     gather_paged_rows,
     decode_paged,

@@ -85,6 +85,18 @@ def widen_e4m3fn(codes: np.ndarray, scale: float = 1.0) -> np.ndarray:
     return val * float(scale)
 
 
+def widen(x: np.ndarray, kv_format: str = "f64", kv_scale: float = 1.0) -> np.ndarray:
+    """Values of stored data: "f64" (already values), "bf16" (uint16 bit
+    patterns) or "e4m3fn" (uint8 codes times kv_scale)."""
+    if kv_format == "f64":
+        return np.asarray(x, dtype=np.float64)
+    if kv_format == "bf16":
+        return widen_bf16(x)
+    if kv_format == "e4m3fn":
+        return widen_e4m3fn(x, kv_scale)
+    raise ValueError(kv_format)
+
+
 # ---------------------------------------------------------------------------
 # The definition.
 # ---------------------------------------------------------------------------
@@ -161,13 +173,15 @@ def gather_paged_rows(cache: np.ndarray, block_table_row: np.ndarray, seq_len: i
 def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                       block_table: np.ndarray, seq_lens: np.ndarray, page_size: int,
                       scale: float, causal: bool, head_dim_v: int,
-                      rows: list[tuple[int, int, int]]) -> tuple[np.ndarray, np.ndarray]:
+                      rows: list[tuple[int, int, int]], kv_format: str = "f64",
+                      kv_scale: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
     """Decode attention for selected (batch, query token, query head) rows.
 
-    q: [B, q_len, Hq, Dqk] float64; k_cache: [P, ps, Hkv, Dqk] float64;
-    v_cache: [P, ps, Hkv, >=Dv] float64 (V is its first head_dim_v entries);
-    block_table: [B, max_pages] ints; seq_lens: [B] ints.
-    Returns o [len(rows), Dv] and lse2 [len(rows)].
+    q: [B, q_len, Hq, Dqk] float64; k_cache: [P, ps, Hkv, Dqk];
+    v_cache: [P, ps, Hkv, >=Dv] (V is its first head_dim_v entries); caches
+    hold values (kv_format "f64") or raw storage ("bf16", "e4m3fn" with
+    kv_scale), widened after gathering; block_table: [B, max_pages] ints;
+    seq_lens: [B] ints. Returns o [len(rows), Dv] and lse2 [len(rows)].
     """
     _, q_len, hq, _ = q.shape
     hkv = k_cache.shape[2]
@@ -179,8 +193,9 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         by_req_head.setdefault((b, h // group), []).append(n)
     for (b, g), members in by_req_head.items():
         lk = int(seq_lens[b])
-        k = gather_paged_rows(k_cache, block_table[b], lk, page_size, g)
-        v = gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v)
+        k = widen(gather_paged_rows(k_cache, block_table[b], lk, page_size, g), kv_format, kv_scale)
+        v = widen(gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v),
+                  kv_format, kv_scale)
         qr = np.stack([q[rows[n][0], rows[n][1], rows[n][2]] for n in members])
         t = np.array([rows[n][1] for n in members], dtype=np.int64)
         bound = causal_key_bound(t, q_len, lk) if causal else np.full(len(members), lk)
@@ -191,13 +206,13 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size, scale,
-                 causal, head_dim_v):
+                 causal, head_dim_v, kv_format="f64", kv_scale=1.0):
     """Decode attention for every row: returns o [B, q_len, Hq, Dv] and
     lse2 [B, q_len, Hq]."""
     b_n, q_len, hq, _ = q.shape
     rows = [(b, t, h) for b in range(b_n) for t in range(q_len) for h in range(hq)]
     o, lse2 = decode_paged_rows(q, k_cache, v_cache, block_table, seq_lens, page_size,
-                                scale, causal, head_dim_v, rows)
+                                scale, causal, head_dim_v, rows, kv_format, kv_scale)
     return o.reshape(b_n, q_len, hq, head_dim_v), lse2.reshape(b_n, q_len, hq)
 
 
@@ -230,9 +245,10 @@ def prefill_dense(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, causal):
 
 
 def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
-                       page_size, scale, causal, head_dim_v, rows):
+                       page_size, scale, causal, head_dim_v, rows, kv_format="f64"):
     """Ragged prefill over a paged cache for selected (query token, head) rows,
-    where the query token index is global in the packed Q."""
+    where the query token index is global in the packed Q. Caches hold values
+    or raw bf16 bits (kv_format "bf16"), widened after gathering."""
     hq = q.shape[1]
     hkv = k_cache.shape[2]
     group = hq // hkv
@@ -246,8 +262,8 @@ def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_tab
     for (b, g), members in by_req_head.items():
         lq = int(cu[b + 1] - cu[b])
         lk = int(seq_lens_kv[b])
-        k = gather_paged_rows(k_cache, block_table[b], lk, page_size, g)
-        v = gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v)
+        k = widen(gather_paged_rows(k_cache, block_table[b], lk, page_size, g), kv_format)
+        v = widen(gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v), kv_format)
         qr = np.stack([q[rows[n][0], rows[n][1]] for n in members])
         i = np.array([rows[n][0] - cu[b] for n in members], dtype=np.int64)
         bound = causal_key_bound(i, lq, lk) if causal else np.full(len(members), lk)
@@ -258,13 +274,13 @@ def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_tab
 
 
 def prefill_paged(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
-                  page_size, scale, causal, head_dim_v):
+                  page_size, scale, causal, head_dim_v, kv_format="f64"):
     """Ragged prefill over a paged cache for every row: o [Tq, Hq, Dv],
     lse2 [Tq, Hq]."""
     tq, hq, _ = q.shape
     rows = [(t, h) for t in range(tq) for h in range(hq)]
     o, lse2 = prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv,
-                                 block_table, page_size, scale, causal, head_dim_v, rows)
+                                 block_table, page_size, scale, causal, head_dim_v, rows, kv_format)
     return o.reshape(tq, hq, head_dim_v), lse2.reshape(tq, hq)
 
 

@@ -1,0 +1,9 @@
+"""MI355X-native fused softmax attention forward (prefill, paged decode with
+split-KV + log-sum-exp merge) behind a C ABI; see include/attn.h.
+
+The Python layer only marshals torch tensors into the C ABI. The HIP library
+must be built in-tree first (python -m softmax_attention_paged_amd.build).
+"""
+
+from .api import decode_paged, decode_params, decode_plan, default_scale, merge_lse, prefill  # noqa: F401
+from ._ffi import AttnError, LIB_PATH, load  # noqa: F401

@@ -1,0 +1,188 @@
+"""Torch-facing binding of the C ABI (include/attn.h).
+
+Argument marshalling only: every function here checks tensor metadata, takes
+data_ptr()s and strides, allocates outputs/workspace with torch (plumbing) and
+calls the HIP library on torch's current stream. Nothing is computed here,
+and there is no fallback path: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _ffi
+
+_BF16 = torch.bfloat16
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _kv_code(cache: torch.Tensor, kv_dtype: str | None) -> int:
+    if cache.dtype == _BF16:
+        return _ffi.ATTN_BF16
+    if cache.dtype in (torch.float8_e4m3fn, torch.uint8):
+        _need(cache.dtype == torch.float8_e4m3fn or kv_dtype == "fp8_e4m3",
+              "uint8 caches need kv_dtype='fp8_e4m3'")
+        return _ffi.ATTN_FP8_E4M3
+    raise ValueError(f"unsupported cache dtype {cache.dtype}")
+
+
+def _as_4d_cache(cache: torch.Tensor) -> torch.Tensor:
+    # A latent cache [pages, page_size, D] is the 4-D layout with one KV head.
+    return cache.unsqueeze(2) if cache.dim() == 3 else cache
+
+
+# --------------------------------------------------------------------------
+# Decode
+# --------------------------------------------------------------------------
+
+def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
+                  causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
+                  num_splits=0, workspace=None, out=None, lse=None) -> _ffi.DecodeParams:
+    """Fill the C parameter struct from tensors (no device access)."""
+    k4 = _as_4d_cache(k_cache)
+    v4 = _as_4d_cache(v_cache if v_cache is not None else k_cache)
+    b, q_len, hq, dqk = q.shape
+    dv = head_dim_v if head_dim_v is not None else v4.shape[3]
+    p = _ffi.DecodeParams()
+    p.q = _ptr(q)
+    p.k_cache, p.v_cache = _ptr(k4), _ptr(v4)
+    p.k_stride_page, p.k_stride_tok, p.k_stride_head = k4.stride(0), k4.stride(1), k4.stride(2)
+    p.v_stride_page, p.v_stride_tok, p.v_stride_head = v4.stride(0), v4.stride(1), v4.stride(2)
+    p.kv_dtype = _kv_code(k4, kv_dtype)
+    p.k_scale, p.v_scale = float(k_scale), float(v_scale)
+    p.seq_lens, p.block_table = _ptr(seq_lens), _ptr(block_table)
+    p.block_table_stride = block_table.stride(0)
+    p.batch, p.q_len, p.num_q_heads, p.num_kv_heads = b, q_len, hq, k4.shape[2]
+    p.head_dim_qk, p.head_dim_v = dqk, dv
+    p.page_size, p.num_pages, p.max_seq_len = k4.shape[1], k4.shape[0], int(max_seq_len)
+    p.softmax_scale, p.causal, p.num_splits = float(softmax_scale), int(bool(causal)), int(num_splits)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p.o, p.lse = _ptr(out), _ptr(lse)
+    return p
+
+
+def decode_plan(params: _ffi.DecodeParams) -> dict:
+    info = _ffi.DecodePlanInfo()
+    _ffi.check(_ffi.load().attn_decode_plan(ctypes.byref(params), ctypes.byref(info)), "attn_decode_plan")
+    return {name: getattr(info, name) for name, _ in _ffi.DecodePlanInfo._fields_}
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
+                 causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
+                 num_splits=0, workspace=None, out=None, return_lse=False):
+    """Paged decode (split-KV + LSE merge). Returns out, or (out, lse).
+
+    q [B, q_len, Hq, Dqk] bf16; caches [pages, page_size, Hkv, D] (or a 3-D
+    latent cache, pass v_cache=None and head_dim_v=512); block_table
+    [B, max_pages] int32; seq_lens [B] int32.
+    """
+    _need(q.is_cuda and q.dtype == _BF16 and q.is_contiguous(), "q must be a contiguous bf16 CUDA tensor")
+    _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
+    _need(block_table.stride(1) == 1 and seq_lens.is_contiguous(), "block_table rows and seq_lens must be contiguous")
+    b, q_len, hq, _ = q.shape
+    k4 = _as_4d_cache(k_cache)
+    dv = head_dim_v if head_dim_v is not None else _as_4d_cache(v_cache if v_cache is not None else k_cache).shape[3]
+    if out is None:
+        out = torch.empty((b, q_len, hq, dv), dtype=_BF16, device=q.device)
+    _need(out.dtype == _BF16 and out.is_contiguous(), "out must be contiguous bf16")
+    lse = torch.empty((b, q_len, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    p = decode_params(q, k_cache, v_cache, block_table, seq_lens, max_seq_len=max_seq_len,
+                      softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
+                      k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=workspace,
+                      out=out, lse=lse)
+    lib = _ffi.load()
+    if workspace is None:
+        need = lib.attn_decode_workspace_size(ctypes.byref(p))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            p.workspace, p.workspace_bytes = workspace.data_ptr(), need
+    _ffi.check(lib.attn_decode_paged(ctypes.byref(p), _stream(q.device)), "attn_decode_paged")
+    del k4
+    return (out, lse) if return_lse else out
+
+
+# --------------------------------------------------------------------------
+# Prefill
+# --------------------------------------------------------------------------
+
+def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale, causal=False,
+            cu_seqlens_kv=None, seq_lens_kv=None, block_table=None, out=None, return_lse=False):
+    """Ragged prefill over dense (cu_seqlens_kv) or paged (block_table +
+    seq_lens_kv) KV. q [Tq, Hq, D] bf16; dense k/v [Tk, Hkv, D]; paged k/v
+    [pages, page_size, Hkv, D]. Returns out [Tq, Hq, Dv], or (out, lse)."""
+    _need(q.is_cuda and q.dtype == _BF16 and q.stride(2) == 1, "q must be bf16 CUDA with contiguous channels")
+    _need(k.dtype == _BF16 and v.dtype == _BF16, "k and v must be bf16")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous(), "cu_seqlens_q must be contiguous int32")
+    paged = block_table is not None
+    tq, hq, dqk = q.shape
+    dv = v.shape[-1]
+    hkv = k.shape[2] if paged else k.shape[1]
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=_BF16, device=q.device)
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    p = _ffi.PrefillParams()
+    p.q, p.q_stride_tok, p.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
+    p.k, p.v = k.data_ptr(), v.data_ptr()
+    if paged:
+        _need(block_table.dtype == torch.int32 and block_table.stride(1) == 1, "block_table must be int32 rows")
+        _need(seq_lens_kv is not None and seq_lens_kv.dtype == torch.int32, "paged mode needs int32 seq_lens_kv")
+        p.k_stride_page, p.k_stride_tok, p.k_stride_head = k.stride(0), k.stride(1), k.stride(2)
+        p.v_stride_page, p.v_stride_tok, p.v_stride_head = v.stride(0), v.stride(1), v.stride(2)
+        p.seq_lens_kv, p.block_table = seq_lens_kv.data_ptr(), block_table.data_ptr()
+        p.block_table_stride, p.page_size, p.num_pages = block_table.stride(0), k.shape[1], k.shape[0]
+    else:
+        _need(cu_seqlens_kv is not None and cu_seqlens_kv.dtype == torch.int32, "dense mode needs int32 cu_seqlens_kv")
+        p.k_stride_tok, p.k_stride_head = k.stride(0), k.stride(1)
+        p.v_stride_tok, p.v_stride_head = v.stride(0), v.stride(1)
+        p.cu_seqlens_kv = cu_seqlens_kv.data_ptr()
+    p.cu_seqlens_q = cu_seqlens_q.data_ptr()
+    p.batch = cu_seqlens_q.numel() - 1
+    p.num_q_heads, p.num_kv_heads, p.head_dim_qk, p.head_dim_v = hq, hkv, dqk, dv
+    p.max_seqlen_q, p.max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
+    p.softmax_scale, p.causal = float(softmax_scale), int(bool(causal))
+    p.o, p.o_stride_tok, p.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
+    p.lse = _ptr(lse)
+    _ffi.check(_ffi.load().attn_prefill(ctypes.byref(p), _stream(q.device)), "attn_prefill")
+    return (out, lse) if return_lse else out
+
+
+# --------------------------------------------------------------------------
+# Merge
+# --------------------------------------------------------------------------
+
+def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out_dtype=_BF16, out=None,
+              return_lse=True):
+    """Merge split partials o_parts [S, R, Dv] fp32 / lse_parts [S, R] fp32
+    (base 2). Returns (o [R, Dv], lse [R]) or o."""
+    _need(o_parts.dtype == torch.float32 and lse_parts.dtype == torch.float32, "partials must be fp32")
+    _need(o_parts.is_contiguous() and lse_parts.is_contiguous(), "partials must be contiguous")
+    s, r, dv = o_parts.shape
+    _need(tuple(lse_parts.shape) == (s, r), "lse_parts must be [S, R]")
+    if out is None:
+        out = torch.empty((r, dv), dtype=out_dtype, device=o_parts.device)
+    code = {torch.bfloat16: _ffi.ATTN_BF16, torch.float32: _ffi.ATTN_FP32}[out.dtype]
+    lse = torch.empty((r,), dtype=torch.float32, device=o_parts.device) if return_lse else None
+    _ffi.check(_ffi.load().attn_merge_lse(o_parts.data_ptr(), lse_parts.data_ptr(), s, r, dv,
+                                          out.data_ptr(), code, _ptr(lse), _stream(o_parts.device)),
+               "attn_merge_lse")
+    return (out, lse) if return_lse else out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

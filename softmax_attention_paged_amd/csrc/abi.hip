@@ -1,0 +1,411 @@
+// C-ABI entry points: host-side validation, planning and dispatch.
+//
+// Nothing here touches device memory: arguments are checked from host
+// scalars and pointer values only, the plan depends only on host scalars
+// (never on device seq_lens), and the kernels are enqueued on the caller's
+// stream. That keeps every call free of synchronisation and capturable.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "attn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+attn_status_t fail(attn_status_t s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+attn_status_t ok() {
+  g_last_error[0] = '\0';
+  return ATTN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+  int s = 0;
+  while ((int64_t(1) << s) < x) ++s;
+  return s;
+}
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_mla_shape(const attn_decode_params *p) {
+  return p->head_dim_qk == 576 && p->head_dim_v == 512;
+}
+
+// Largest F dividing q_len with rows_per_head * F <= capacity ("TokenSpeed-MLA",
+// section "Key Optimization ... Group q_seqlen and num_heads into BMM1 M").
+int fold_factor(int heads, int q_len, int capacity) {
+  int best = 1;
+  for (int f = 1; f <= q_len; ++f)
+    if (q_len % f == 0 && heads * f <= capacity) best = f;
+  return best;
+}
+
+struct DecodePlan {
+  bool mla;
+  int group, fold, q_groups, rows, splits, split_tokens;
+  int64_t units;
+  size_t workspace;
+};
+
+attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->q_len < 1 || p->q_len > 4)
+    return fail(ATTN_ERR_UNSUPPORTED, "q_len %d outside 1..4", p->q_len);
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
+    return fail(ATTN_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                p->num_q_heads, p->num_kv_heads);
+  if (!pow2(p->page_size) || p->page_size < 16)
+    return fail(ATTN_ERR_UNSUPPORTED, "page_size %d is not a power of two >= 16", p->page_size);
+  if (p->num_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", p->num_pages);
+  if (p->max_seq_len < 0) return fail(ATTN_ERR_INVALID_ARG, "max_seq_len %d < 0", p->max_seq_len);
+  if ((int64_t)p->max_seq_len > (int64_t)p->num_pages * p->page_size)
+    return fail(ATTN_ERR_INVALID_ARG, "max_seq_len %d exceeds num_pages * page_size", p->max_seq_len);
+  if (p->block_table_stride < cdiv(p->max_seq_len, p->page_size))
+    return fail(ATTN_ERR_INVALID_ARG, "block_table_stride %d < pages of max_seq_len (%lld)",
+                p->block_table_stride, (long long)cdiv(p->max_seq_len, p->page_size));
+  if (!std::isfinite(p->softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->num_splits < 0 || p->num_splits > attn::kMaxSplits)
+    return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside 0..%d", p->num_splits, attn::kMaxSplits);
+
+  const bool mla = is_mla_shape(p);
+  if (mla) {
+    if (p->num_kv_heads != 1)
+      return fail(ATTN_ERR_UNSUPPORTED, "the 576/512 latent layout needs num_kv_heads == 1");
+    if (p->kv_dtype != ATTN_BF16 && p->kv_dtype != ATTN_FP8_E4M3)
+      return fail(ATTN_ERR_UNSUPPORTED, "latent KV must be bf16 or fp8 e4m3");
+    if (p->k_cache != p->v_cache || p->k_stride_page != p->v_stride_page || p->k_stride_tok != p->v_stride_tok)
+      return fail(ATTN_ERR_UNSUPPORTED, "the latent layout reads V from the K rows: pass the same cache and strides");
+    if (p->num_q_heads > attn::kMlaRows || attn::kMlaRows % p->num_q_heads)
+      return fail(ATTN_ERR_UNSUPPORTED, "latent decode needs num_q_heads dividing %d", attn::kMlaRows);
+    if (p->kv_dtype == ATTN_FP8_E4M3 &&
+        (!(p->k_scale > 0.f) || !std::isfinite(p->k_scale) || p->k_scale != p->v_scale))
+      return fail(ATTN_ERR_INVALID_ARG, "fp8 latent KV needs one finite positive scale (k_scale == v_scale)");
+  } else {
+    if (p->head_dim_qk != p->head_dim_v ||
+        (p->head_dim_qk != 64 && p->head_dim_qk != 128 && p->head_dim_qk != 256))
+      return fail(ATTN_ERR_UNSUPPORTED, "head dims (%d, %d) unsupported: need equal 64/128/256 or 576/512",
+                  p->head_dim_qk, p->head_dim_v);
+    if (p->kv_dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, "GQA decode supports bf16 KV only");
+    if (p->num_q_heads / p->num_kv_heads > attn::kGqaRowsPerTile)
+      return fail(ATTN_ERR_UNSUPPORTED, "more than %d query heads per KV head", attn::kGqaRowsPerTile);
+  }
+  if (p->kv_dtype == ATTN_BF16 && (p->k_scale != 1.f || p->v_scale != 1.f))
+    return fail(ATTN_ERR_INVALID_ARG, "k_scale and v_scale must be 1.0 for bf16 KV");
+
+  if (p->batch == 0 || !check_pointers) return ok();
+  if (!p->q || !p->k_cache || !p->v_cache || !p->seq_lens || !p->block_table || !p->o)
+    return fail(ATTN_ERR_INVALID_ARG, "a required pointer (q, k_cache, v_cache, seq_lens, block_table, o) is NULL");
+  if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || !aligned16(p->o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
+  const int esz = (p->kv_dtype == ATTN_FP8_E4M3) ? 1 : 2;
+  const int64_t strides[6] = {p->k_stride_page, p->k_stride_tok, p->k_stride_head,
+                              p->v_stride_page, p->v_stride_tok, p->v_stride_head};
+  for (int i = 0; i < 6; ++i) {
+    if (strides[i] < 0 || (strides[i] * esz) % 16)
+      return fail(ATTN_ERR_INVALID_ARG, "cache strides must be non-negative and multiples of 16 bytes");
+  }
+  if (p->k_stride_tok < 1 || p->k_stride_page < 1 || p->v_stride_tok < 1 || p->v_stride_page < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "cache page and token strides must be positive");
+  return ok();
+}
+
+DecodePlan plan_decode(const attn_decode_params *p) {
+  DecodePlan pl{};
+  pl.mla = is_mla_shape(p);
+  pl.group = p->num_q_heads / p->num_kv_heads;
+  const int capacity = pl.mla ? attn::kMlaRows : attn::kGqaRowsPerTile;
+  pl.fold = fold_factor(pl.group, p->q_len, capacity);
+  pl.q_groups = p->q_len / pl.fold;
+  pl.rows = pl.group * pl.fold;
+  const int64_t base_units = (int64_t)p->batch * p->num_kv_heads * pl.q_groups;
+  const int tile = pl.mla ? attn::kMlaTileTokens : attn::kGqaTileTokens;
+  int splits;
+  if (p->num_splits > 0) {
+    splits = p->num_splits;
+  } else if (pl.mla) {
+    // MFMA-bound: about two workgroups per CU, but no split shorter than 1024 keys.
+    const int64_t want = cdiv(2 * attn::kNumCUs, base_units > 0 ? base_units : 1);
+    const int64_t by_len = cdiv(p->max_seq_len, 1024);
+    splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
+  } else {
+    // HBM-bound: many small units so ragged lengths balance across 256 CUs,
+    // but no split shorter than 256 keys.
+    const int64_t want = cdiv(32 * attn::kNumCUs, base_units > 0 ? base_units : 1);
+    const int64_t by_len = cdiv(p->max_seq_len, 256);
+    splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
+  }
+  // Split length: a whole number of tiles; then keep only non-empty splits of
+  // the longest request.
+  int64_t split_tokens = cdiv(std::max(p->max_seq_len, 1), splits);
+  split_tokens = cdiv(split_tokens, tile) * tile;
+  splits = (int)std::max<int64_t>(1, cdiv(p->max_seq_len, split_tokens));
+  pl.splits = splits;
+  pl.split_tokens = (int)split_tokens;
+  pl.units = base_units * splits;
+  const int64_t rows_total = (int64_t)p->batch * p->q_len * p->num_q_heads;
+  pl.workspace = splits > 1 ? (size_t)splits * rows_total * (p->head_dim_v + 1) * sizeof(float) : 0;
+  return pl;
+}
+
+
+constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
+
+attn_status_t validate_prefill(const attn_prefill_params *p) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
+    return fail(ATTN_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->head_dim_qk != p->head_dim_v || (p->head_dim_qk != 64 && p->head_dim_qk != 128 && p->head_dim_qk != 256))
+    return fail(ATTN_ERR_UNSUPPORTED, "prefill head dims (%d, %d) unsupported: need equal 64/128/256",
+                p->head_dim_qk, p->head_dim_v);
+  if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_q/max_seqlen_kv must be >= 0");
+  if (!std::isfinite(p->softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const bool paged = p->block_table != nullptr;
+  if (paged) {
+    if (!pow2(p->page_size) || p->page_size < 16)
+      return fail(ATTN_ERR_UNSUPPORTED, "page_size %d is not a power of two >= 16", p->page_size);
+    if (p->num_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", p->num_pages);
+    if ((int64_t)p->max_seqlen_kv > (int64_t)p->num_pages * p->page_size)
+      return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_kv exceeds num_pages * page_size");
+    if (p->block_table_stride < cdiv(p->max_seqlen_kv, p->page_size))
+      return fail(ATTN_ERR_INVALID_ARG, "block_table_stride %d < pages of max_seqlen_kv", p->block_table_stride);
+  }
+  if (p->batch == 0 || p->max_seqlen_q == 0) return ok();
+  if (!p->q || !p->k || !p->v || !p->cu_seqlens_q || !p->o)
+    return fail(ATTN_ERR_INVALID_ARG, "a required pointer (q, k, v, cu_seqlens_q, o) is NULL");
+  if (paged ? !p->seq_lens_kv : !p->cu_seqlens_kv)
+    return fail(ATTN_ERR_INVALID_ARG, paged ? "paged mode needs seq_lens_kv" : "dense mode needs cu_seqlens_kv");
+  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
+    return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  const int64_t strides[] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok, p->k_stride_head,
+                             p->v_stride_tok, p->v_stride_head, p->o_stride_tok, p->o_stride_head,
+                             paged ? p->k_stride_page : 8, paged ? p->v_stride_page : 8};
+  for (int64_t st : strides)
+    if (st < 0 || (st * 2) % 16) return fail(ATTN_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  if (p->q_stride_tok < 1 || p->k_stride_tok < 1 || p->v_stride_tok < 1 || p->o_stride_tok < 1)
+    return fail(ATTN_ERR_INVALID_ARG, "token strides must be positive");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "ATTN_ERR_WORKSPACE_TOO_SMALL";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+  }
+  return "ATTN_ERR_UNKNOWN";
+}
+
+const char *attn_last_error(void) { return g_last_error; }
+
+attn_status_t attn_decode_plan(const attn_decode_params *p, attn_decode_plan_info *info) {
+  if (!info) return fail(ATTN_ERR_INVALID_ARG, "info is NULL");
+  attn_status_t st = validate_decode(p, false);
+  if (st != ATTN_OK) return st;
+  const DecodePlan pl = plan_decode(p);
+  info->group = pl.group;
+  info->fold = pl.fold;
+  info->q_groups = pl.q_groups;
+  info->rows_per_unit = pl.rows;
+  info->num_splits = pl.splits;
+  info->split_tokens = pl.split_tokens;
+  info->num_units = pl.units;
+  info->workspace_bytes = pl.workspace;
+  return ok();
+}
+
+size_t attn_decode_workspace_size(const attn_decode_params *p) {
+  if (validate_decode(p, false) != ATTN_OK) return 0;
+  return plan_decode(p).workspace;
+}
+
+attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream) {
+  attn_status_t st = validate_decode(p, true);
+  if (st != ATTN_OK) return st;
+  if (p->batch == 0) return ok();
+  const DecodePlan pl = plan_decode(p);
+  if (pl.splits > 1) {
+    if (!p->workspace || p->workspace_bytes < pl.workspace)
+      return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.workspace,
+                  p->workspace ? p->workspace_bytes : (size_t)0);
+    if (!aligned16(p->workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  const int64_t rows_total = (int64_t)p->batch * p->q_len * p->num_q_heads;
+  float *o_parts = static_cast<float *>(p->workspace);
+  float *lse_parts = pl.splits > 1 ? o_parts + (size_t)pl.splits * rows_total * p->head_dim_v : nullptr;
+  const float scale_log2 = p->softmax_scale * attn::kLog2eHost;
+  hipError_t err;
+  if (pl.mla) {
+    attn::DecodeMlaArgs a{};
+    a.q = p->q;
+    a.kv_cache = p->k_cache;
+    a.kv_stride_page = p->k_stride_page;
+    a.kv_stride_tok = p->k_stride_tok;
+    a.kv_fp8 = p->kv_dtype == ATTN_FP8_E4M3;
+    a.kv_scale = p->k_scale;
+    a.seq_lens = p->seq_lens;
+    a.block_table = p->block_table;
+    a.block_table_stride = p->block_table_stride;
+    a.batch = p->batch;
+    a.q_len = p->q_len;
+    a.num_heads = p->num_q_heads;
+    a.page_shift = log2i(p->page_size);
+    a.fold = pl.fold;
+    a.q_groups = pl.q_groups;
+    a.rows = pl.rows;
+    a.num_splits = pl.splits;
+    a.split_tokens = pl.split_tokens;
+    a.scale_log2 = scale_log2;
+    a.causal = p->causal;
+    a.o = p->o;
+    a.lse = p->lse;
+    a.o_parts = o_parts;
+    a.lse_parts = lse_parts;
+    err = attn::launch_decode_mla(a, stream);
+  } else {
+    attn::DecodeGqaArgs a{};
+    a.q = p->q;
+    a.k_cache = p->k_cache;
+    a.v_cache = p->v_cache;
+    a.k_stride_page = p->k_stride_page;
+    a.k_stride_tok = p->k_stride_tok;
+    a.k_stride_head = p->k_stride_head;
+    a.v_stride_page = p->v_stride_page;
+    a.v_stride_tok = p->v_stride_tok;
+    a.v_stride_head = p->v_stride_head;
+    a.seq_lens = p->seq_lens;
+    a.block_table = p->block_table;
+    a.block_table_stride = p->block_table_stride;
+    a.batch = p->batch;
+    a.q_len = p->q_len;
+    a.num_q_heads = p->num_q_heads;
+    a.num_kv_heads = p->num_kv_heads;
+    a.head_dim = p->head_dim_qk;
+    a.page_shift = log2i(p->page_size);
+    a.group = pl.group;
+    a.fold = pl.fold;
+    a.q_groups = pl.q_groups;
+    a.rows = pl.rows;
+    a.num_splits = pl.splits;
+    a.split_tokens = pl.split_tokens;
+    a.scale_log2 = scale_log2;
+    a.causal = p->causal;
+    a.o = p->o;
+    a.lse = p->lse;
+    a.o_parts = o_parts;
+    a.lse_parts = lse_parts;
+    err = attn::launch_decode_gqa(a, stream);
+  }
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "split kernel launch: %s", hipGetErrorString(err));
+  if (pl.splits > 1) {
+    attn::MergeArgs m{};
+    m.o_parts = o_parts;
+    m.lse_parts = lse_parts;
+    m.num_splits = pl.splits;
+    m.num_rows = rows_total;
+    m.head_dim_v = p->head_dim_v;
+    m.o = p->o;
+    m.o_bf16 = 1;
+    m.lse = p->lse;
+    err = attn::launch_merge(m, stream);
+    if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(err));
+  }
+  return ok();
+}
+
+attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
+  attn_status_t st = validate_prefill(p);
+  if (st != ATTN_OK) return st;
+  if (p->batch == 0 || p->max_seqlen_q == 0) return ok();
+  attn::PrefillArgs a{};
+  a.q = p->q;
+  a.q_stride_tok = p->q_stride_tok;
+  a.q_stride_head = p->q_stride_head;
+  a.k = p->k;
+  a.v = p->v;
+  a.k_stride_page = p->k_stride_page;
+  a.k_stride_tok = p->k_stride_tok;
+  a.k_stride_head = p->k_stride_head;
+  a.v_stride_page = p->v_stride_page;
+  a.v_stride_tok = p->v_stride_tok;
+  a.v_stride_head = p->v_stride_head;
+  a.cu_seqlens_q = p->cu_seqlens_q;
+  a.cu_seqlens_kv = p->cu_seqlens_kv;
+  a.seq_lens_kv = p->seq_lens_kv;
+  a.block_table = p->block_table;
+  a.block_table_stride = p->block_table_stride;
+  a.page_shift = p->block_table ? log2i(p->page_size) : 0;
+  a.batch = p->batch;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.head_dim = p->head_dim_qk;
+  a.max_seqlen_q = p->max_seqlen_q;
+  a.max_seqlen_kv = p->max_seqlen_kv;
+  a.q_tiles = (int)cdiv(p->max_seqlen_q, kPrefillRows);
+  a.scale_log2 = p->softmax_scale * attn::kLog2eHost;
+  a.causal = p->causal;
+  a.o = p->o;
+  a.o_stride_tok = p->o_stride_tok;
+  a.o_stride_head = p->o_stride_head;
+  a.lse = p->lse;
+  hipError_t err = attn::launch_prefill(a, stream);
+  if (err == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no prefill kernel for this shape");
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(err));
+  return ok();
+}
+
+attn_status_t attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_splits,
+                             int64_t num_rows, int32_t head_dim_v, void *o, attn_dtype_t o_dtype,
+                             float *lse_out, hipStream_t stream) {
+  if (num_splits < 1 || num_splits > attn::kMaxSplits)
+    return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside 1..%d", num_splits, attn::kMaxSplits);
+  if (num_rows < 0) return fail(ATTN_ERR_INVALID_ARG, "num_rows < 0");
+  if (head_dim_v < 4 || head_dim_v > 1024 || head_dim_v % 4)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim_v %d must be a multiple of 4 in 4..1024", head_dim_v);
+  if (o_dtype != ATTN_BF16 && o_dtype != ATTN_FP32)
+    return fail(ATTN_ERR_UNSUPPORTED, "merge output must be bf16 or fp32");
+  if (num_rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o) return fail(ATTN_ERR_INVALID_ARG, "o_parts, lse_parts and o are required");
+  if (!aligned16(o_parts) || !aligned16(o) || (o_dtype == ATTN_BF16 && head_dim_v % 8 && (reinterpret_cast<uintptr_t>(o) & 7)))
+    return fail(ATTN_ERR_INVALID_ARG, "o_parts and o must be 16-byte aligned");
+  attn::MergeArgs m{};
+  m.o_parts = o_parts;
+  m.lse_parts = lse_parts;
+  m.num_splits = num_splits;
+  m.num_rows = num_rows;
+  m.head_dim_v = head_dim_v;
+  m.o = o;
+  m.o_bf16 = o_dtype == ATTN_BF16;
+  m.lse = lse_out;
+  hipError_t err = attn::launch_merge(m, stream);
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(err));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Internal interface between the C-ABI layer (host validation and planning)
+// and the kernel launchers. Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+
+namespace attn {
+
+// Everything the GQA split-decode kernel needs, already validated.
+struct DecodeGqaArgs {
+  const void *q;                 // bf16 [B, q_len, Hq, D]
+  const void *k_cache, *v_cache;
+  int64_t k_stride_page, k_stride_tok, k_stride_head;
+  int64_t v_stride_page, v_stride_tok, v_stride_head;
+  const int32_t *seq_lens;
+  const int32_t *block_table;
+  int32_t block_table_stride;
+  int32_t batch, q_len, num_q_heads, num_kv_heads, head_dim;
+  int32_t page_shift;            // log2(page_size)
+  int32_t group, fold, q_groups, rows;
+  int32_t num_splits, split_tokens;
+  float scale_log2;              // softmax_scale * log2(e)
+  int32_t causal;
+  // outputs: either final (num_splits == 1) or partials
+  void *o;                       // bf16 [B, q_len, Hq, D]
+  float *lse;                    // optional [B, q_len, Hq]
+  float *o_parts;                // [S, R, D]
+  float *lse_parts;              // [S, R]
+};
+
+// MLA-shaped decode: one latent KV head, K = the 576-wide row, V its first 512.
+struct DecodeMlaArgs {
+  const void *q;                 // bf16 [B, q_len, H, 576]
+  const void *kv_cache;          // bf16 or fp8 codes [pages, ps, 1, 576]
+  int64_t kv_stride_page, kv_stride_tok;
+  int32_t kv_fp8;
+  float kv_scale;
+  const int32_t *seq_lens;
+  const int32_t *block_table;
+  int32_t block_table_stride;
+  int32_t batch, q_len, num_heads;
+  int32_t page_shift;
+  int32_t fold, q_groups, rows;  // rows = num_heads * fold
+  int32_t num_splits, split_tokens;
+  float scale_log2;
+  int32_t causal;
+  void *o;
+  float *lse;
+  float *o_parts;
+  float *lse_parts;
+};
+
+struct MergeArgs {
+  const float *o_parts;          // [S, R, Dv]
+  const float *lse_parts;        // [S, R]
+  int32_t num_splits;
+  int64_t num_rows;
+  int32_t head_dim_v;
+  void *o;                       // [R, Dv]
+  int32_t o_bf16;                // 1: bf16 output, 0: fp32
+  float *lse;                    // optional [R]
+};
+
+struct PrefillArgs {
+  const void *q;
+  int64_t q_stride_tok, q_stride_head;
+  const void *k, *v;
+  int64_t k_stride_page, k_stride_tok, k_stride_head;
+  int64_t v_stride_page, v_stride_tok, v_stride_head;
+  const int32_t *cu_seqlens_q;
+  const int32_t *cu_seqlens_kv;
+  const int32_t *seq_lens_kv;
+  const int32_t *block_table;    // null: dense
+  int32_t block_table_stride;
+  int32_t page_shift;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_seqlen_q, max_seqlen_kv;
+  int32_t q_tiles;               // ceil(max_seqlen_q / rows per workgroup)
+  float scale_log2;
+  int32_t causal;
+  void *o;
+  int64_t o_stride_tok, o_stride_head;
+  float *lse;
+};
+
+// Launchers; each returns hipSuccess or the launch error.
+hipError_t launch_decode_gqa(const DecodeGqaArgs &a, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeMlaArgs &a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// Kernel geometry the planner needs.
+constexpr int kGqaRowsPerTile = 16;   // MFMA N rows of the GQA decode kernel
+constexpr int kGqaTileTokens = 32;    // keys per wave iteration
+constexpr int kGqaWaves = 4;
+constexpr int kMlaRows = 128;         // folded rows of the MLA decode kernel
+constexpr int kMlaTileTokens = 32;
+constexpr int kMaxSplits = 256;
+constexpr int kNumCUs = 256;          // MI355X compute units
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+}  // namespace attn

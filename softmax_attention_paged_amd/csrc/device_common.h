@@ -1,0 +1,75 @@
+// Device-side building blocks for gfx950 (CDNA4): MFMA tiles, LDS transpose
+// reads, exp2 and bf16 packing. Only the kernels of this library include it.
+//
+// Lane layouts (checked on gfx950 with an in-bounds probe before use):
+//   v_mfma_f32_16x16x32_bf16, lane l, g = l / 16:
+//     A (16 x 32): A[l % 16][8g + e], e = 0..7
+//     B (32 x 16): B[8g + e][l % 16]
+//     C (16 x 16): C[4g + i][l % 16], i = 0..3
+//   v_mfma_f32_32x32x16_bf16, lane l, h = l / 32:
+//     A: A[l % 32][8h + e]; B: B[8h + e][l % 32]
+//     C: C[8(i / 4) + 4h + (i % 4)][l % 32], i = 0..15
+//   ds_read_b64_tr_b16: within each 16-lane block, lane i receives element
+//     (i % 4) of the 64-bit row addressed by lane (i / 4 + 4j) as its j-th
+//     16-bit result, j = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
+
+// 16-byte global load of eight bf16 values.
+__device__ __forceinline__ bf16x8 load_bf16x8(const void *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ void store_bf16x8_lds(void *p, bf16x8 v) {
+  *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
+}
+
+// ds_read_b64_tr_b16 on an LDS address held in a generic pointer.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void *p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <class T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace attn

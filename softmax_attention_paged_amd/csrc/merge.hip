@@ -1,0 +1,93 @@
+// Log-sum-exp merge of split-KV partials, for gfx950.
+//
+// Split i of a row holds o_i, the output normalised over the split's keys,
+// and lse_i = log2 of the split's softmax denominator. The row's output over
+// all keys is sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M) with M = max_i
+// lse_i, and its log-sum-exp is M + log2(sum_i 2^(lse_i - M)) ("TokenSpeed-
+// MLA", section "Decode performance": a second kernel reduces the split-KV
+// partial results; section "FP8 split-KV partial storage": combine normalised
+// FP32 partials).
+//
+// One wave per row: the lanes read the split LSEs once, reduce M and the
+// weights with wave shuffles, then stream the non-empty partial rows with
+// 16-byte loads. Splits with lse = -inf are never read.
+
+#include "attn_internal.h"
+#include "device_common.h"
+
+namespace attn {
+namespace {
+
+constexpr int kMergeWaves = 4;
+constexpr int kMaxChunksPerLane = 4;   // float4 chunks: head_dim_v <= 1024
+
+__global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rowi = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (rowi >= a.num_rows) return;
+
+  // split weights: lane holds splits lane, lane + 64, ...
+  float lse_r[kMaxSplits / 64];
+  float mmax = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kMaxSplits / 64; ++j) {
+    const int s = lane + 64 * j;
+    lse_r[j] = (s < a.num_splits) ? a.lse_parts[(int64_t)s * a.num_rows + rowi] : kNegInf;
+    mmax = fmaxf(mmax, lse_r[j]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, wave_shfl_xor(mmax, off));
+  const float muse = (mmax == kNegInf) ? 0.f : mmax;
+  float wsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxSplits / 64; ++j) {
+    lse_r[j] = exp2_fast(lse_r[j] - muse);   // weight; 0 for empty splits
+    wsum += lse_r[j];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += wave_shfl_xor(wsum, off);
+
+  const int nchunks = a.head_dim_v >> 2;
+  f32x4 acc[kMaxChunksPerLane];
+#pragma unroll
+  for (int k = 0; k < kMaxChunksPerLane; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < a.num_splits; ++s) {
+    const float w = __shfl(lse_r[s >> 6], s & 63, 64);
+    if (w == 0.f) continue;   // uniform: empty (or negligible) split, not read
+    const float *src = a.o_parts + ((int64_t)s * a.num_rows + rowi) * a.head_dim_v;
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k) {
+      const int c = lane + 64 * k;
+      if (c < nchunks) acc[k] += w * *reinterpret_cast<const f32x4 *>(src + 4 * c);
+    }
+  }
+
+  const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxChunksPerLane; ++k) {
+    const int c = lane + 64 * k;
+    if (c >= nchunks) continue;
+    const f32x4 r = acc[k] * inv;
+    if (a.o_bf16) {
+      bf16x4 ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[e] = to_bf16(r[e]);
+      *reinterpret_cast<u32x2 *>(static_cast<__bf16 *>(a.o) + rowi * a.head_dim_v + 4 * c) =
+          __builtin_bit_cast(u32x2, ob);
+    } else {
+      *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + rowi * a.head_dim_v + 4 * c) = r;
+    }
+  }
+  if (a.lse && lane == 0) a.lse[rowi] = (wsum > 0.f) ? muse + __log2f(wsum) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
+  const int64_t blocks = (a.num_rows + kMergeWaves - 1) / kMergeWaves;
+  hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,221 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/attn.h declares, validates arguments on the host (no GPU call is
+reached on any error path), and plans decode as the pages' formulas say."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from softmax_attention_paged_amd import _ffi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # a 16-byte aligned non-null address; never dereferenced on the host
+
+
+def _lib():
+    if not os.path.exists(_ffi.LIB_PATH):
+        pytest.fail("library not built: run `python -m softmax_attention_paged_amd.build`")
+    return _ffi.load()
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib()
+    names = _header_functions()
+    assert {"attn_prefill", "attn_decode_paged", "attn_merge_lse"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_ffi.EXPORTS), "binding and header disagree"
+
+
+def test_struct_sizes_match_c_layout():
+    # ctypes mirrors must match the C layout (checked against offsets the C
+    # compiler would use: pointers and int64 are 8-aligned, int32/float 4).
+    assert ctypes.sizeof(_ffi.DecodePlanInfo) == 40
+    assert _ffi.DecodeParams.workspace.offset % 8 == 0
+    assert _ffi.PrefillParams.lse.offset % 8 == 0
+
+
+def test_status_strings():
+    lib = _lib()
+    for code, name in [(0, "ATTN_OK"), (1, "ATTN_ERR_INVALID_ARG"), (2, "ATTN_ERR_UNSUPPORTED"),
+                       (3, "ATTN_ERR_WORKSPACE_TOO_SMALL"), (4, "ATTN_ERR_HIP")]:
+        assert lib.attn_status_string(code).decode() == name
+
+
+def decode_params(**kw):
+    p = _ffi.DecodeParams()
+    d = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE + 4096, k_stride_page=16 * 2 * 128, k_stride_tok=2 * 128,
+             k_stride_head=128, v_stride_page=16 * 2 * 128, v_stride_tok=2 * 128, v_stride_head=128,
+             kv_dtype=_ffi.ATTN_BF16, k_scale=1.0, v_scale=1.0, seq_lens=FAKE, block_table=FAKE,
+             block_table_stride=8, batch=2, q_len=1, num_q_heads=8, num_kv_heads=2, head_dim_qk=128,
+             head_dim_v=128, page_size=16, num_pages=16, max_seq_len=100, softmax_scale=0.125, causal=0,
+             num_splits=0, workspace=None, workspace_bytes=0, o=FAKE, lse=None)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def plan(p):
+    info = _ffi.DecodePlanInfo()
+    st = _lib().attn_decode_plan(ctypes.byref(p), ctypes.byref(info))
+    return st, info
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(o=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_q_heads=7), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(head_dim_qk=96, head_dim_v=96), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim_v=64), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(page_size=24), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(page_size=8), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(q_len=5), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(q_len=0), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(max_seq_len=16 * 16 + 1), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(block_table_stride=6), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(causal=2), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_splits=257), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(k_scale=0.5), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=_ffi.ATTN_FP8_E4M3), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 8), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(k_stride_tok=100), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_q_heads=68, num_kv_heads=2), _ffi.ATTN_ERR_UNSUPPORTED),
+])
+def test_decode_validation_errors(kw, code):
+    lib = _lib()
+    p = decode_params(**kw)
+    st = lib.attn_decode_paged(ctypes.byref(p), None)
+    assert st == code, (st, lib.attn_last_error())
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_workspace_too_small_is_reported_before_launch():
+    lib = _lib()
+    p = decode_params(num_splits=4)
+    need = lib.attn_decode_workspace_size(ctypes.byref(p))
+    assert need == 4 * (2 * 1 * 8) * (128 + 1) * 4
+    p.workspace, p.workspace_bytes = FAKE, need - 4
+    assert lib.attn_decode_paged(ctypes.byref(p), None) == _ffi.ATTN_ERR_WORKSPACE_TOO_SMALL
+    p.workspace = None
+    assert lib.attn_decode_paged(ctypes.byref(p), None) == _ffi.ATTN_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_batch_zero_is_a_no_op():
+    lib = _lib()
+    p = decode_params(batch=0, q=None, o=None)
+    assert lib.attn_decode_paged(ctypes.byref(p), None) == _ffi.ATTN_OK
+
+
+def test_merge_validation():
+    lib = _lib()
+    assert lib.attn_merge_lse(FAKE, FAKE, 0, 10, 128, FAKE, _ffi.ATTN_BF16, None, None) == _ffi.ATTN_ERR_INVALID_ARG
+    assert lib.attn_merge_lse(FAKE, FAKE, 300, 10, 128, FAKE, _ffi.ATTN_BF16, None, None) == _ffi.ATTN_ERR_INVALID_ARG
+    assert lib.attn_merge_lse(FAKE, FAKE, 2, 10, 130, FAKE, _ffi.ATTN_BF16, None, None) == _ffi.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_merge_lse(FAKE, FAKE, 2, 10, 128, FAKE, _ffi.ATTN_FP8_E4M3, None, None) == _ffi.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_merge_lse(None, FAKE, 2, 10, 128, FAKE, _ffi.ATTN_BF16, None, None) == _ffi.ATTN_ERR_INVALID_ARG
+    assert lib.attn_merge_lse(None, None, 2, 0, 128, None, _ffi.ATTN_BF16, None, None) == _ffi.ATTN_OK
+
+
+def prefill_params(**kw):
+    p = _ffi.PrefillParams()
+    d = dict(q=FAKE, q_stride_tok=32 * 128, q_stride_head=128, k=FAKE, v=FAKE, k_stride_page=0,
+             k_stride_tok=32 * 128, k_stride_head=128, v_stride_page=0, v_stride_tok=32 * 128,
+             v_stride_head=128, cu_seqlens_q=FAKE, cu_seqlens_kv=FAKE, seq_lens_kv=None, block_table=None,
+             block_table_stride=0, page_size=0, num_pages=0, batch=1, num_q_heads=32, num_kv_heads=32,
+             head_dim_qk=128, head_dim_v=128, max_seqlen_q=8192, max_seqlen_kv=8192, softmax_scale=0.088,
+             causal=1, o=FAKE, o_stride_tok=32 * 128, o_stride_head=128, lse=None)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(cu_seqlens_kv=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_kv_heads=5), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(head_dim_qk=96, head_dim_v=96), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim_v=64), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(block_table=FAKE, seq_lens_kv=FAKE, page_size=48, num_pages=1000, block_table_stride=1000),
+     _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(block_table=FAKE, seq_lens_kv=None, page_size=64, num_pages=1000, block_table_stride=1000),
+     _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(block_table=FAKE, seq_lens_kv=FAKE, page_size=64, num_pages=10, block_table_stride=1000),
+     _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(q_stride_head=100), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(causal=3), _ffi.ATTN_ERR_INVALID_ARG),
+])
+def test_prefill_validation_errors(kw, code):
+    lib = _lib()
+    p = prefill_params(**kw)
+    assert lib.attn_prefill(ctypes.byref(p), None) == code, lib.attn_last_error()
+
+
+# ------------------------------------------------------------- planner --
+
+def test_fold_matches_tokenspeed_example_for_latent_decode():
+    # H64, q_len 4 -> F = 2, H_eff = 128, q_eff = 2 (the pages' worked example)
+    p = decode_params(num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, q_len=4,
+                      v_cache=FAKE, k_stride_page=64 * 576, k_stride_tok=576, k_stride_head=576,
+                      v_stride_page=64 * 576, v_stride_tok=576, v_stride_head=576, page_size=64,
+                      num_pages=10240, max_seq_len=81920, block_table_stride=1280, batch=8)
+    st, info = plan(p)
+    assert st == 0
+    f = oracle.fold_factor(64, 4)
+    assert (info.fold, info.q_groups, info.rows_per_unit) == (f, 4 // f, 64 * f) == (2, 2, 128)
+
+
+def test_latent_workspace_equals_tokenspeed_formula():
+    # Our partial layout is S x R x (Dv + 1) fp32 with R = B * q_len * H;
+    # for H * q_len a multiple of 128 it equals B * 128 * ceil(H q / 128) * S * 513 * 4.
+    for splits in (1, 2, 5, 16):
+        p = decode_params(num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, q_len=4,
+                          v_cache=FAKE, k_stride_page=64 * 576, k_stride_tok=576, k_stride_head=576,
+                          v_stride_page=64 * 576, v_stride_tok=576, v_stride_head=576, page_size=64,
+                          num_pages=10240, max_seq_len=81920, block_table_stride=1280, batch=8,
+                          num_splits=splits)
+        st, info = plan(p)
+        assert st == 0 and info.num_splits == splits
+        assert info.workspace_bytes == oracle.mla_packed_workspace_bytes(8, 64, 4, splits)
+
+
+def test_gqa_plan_folds_heads_and_tokens_into_16_rows():
+    for q_len, hq, hkv, expect_f in [(1, 40, 8, 1), (4, 8, 2, 4), (4, 20, 4, 2), (3, 8, 8, 3), (4, 16, 1, 1)]:
+        st, info = plan(decode_params(q_len=q_len, num_q_heads=hq, num_kv_heads=hkv, block_table_stride=8))
+        assert st == 0
+        assert info.group == hq // hkv
+        assert info.fold == expect_f == oracle.fold_factor(hq // hkv, q_len, 16)
+        assert info.rows_per_unit == info.group * info.fold <= 16
+        assert info.q_groups * info.fold == q_len
+
+
+def test_split_plan_is_nonempty_and_tile_aligned():
+    for max_len in (1, 31, 100, 1000, 8192, 81920):
+        pages = -(-max_len // 16)
+        st, info = plan(decode_params(max_seq_len=max_len, num_pages=pages, block_table_stride=pages))
+        assert st == 0
+        assert info.split_tokens % 32 == 0
+        assert (info.num_splits - 1) * info.split_tokens < max(max_len, 1) <= info.num_splits * info.split_tokens
+        assert info.num_units == 2 * 2 * info.num_splits
+        assert info.workspace_bytes == (0 if info.num_splits == 1 else info.num_splits * 16 * 129 * 4)
+
+
+def test_qwen3_14b_decode_plan():
+    pages = 2200
+    p = decode_params(batch=64, num_q_heads=40, num_kv_heads=8, page_size=128, num_pages=pages,
+                      max_seq_len=8192, block_table_stride=64, k_stride_page=128 * 8 * 128,
+                      k_stride_tok=8 * 128, v_stride_page=128 * 8 * 128, v_stride_tok=8 * 128)
+    st, info = plan(p)
+    assert st == 0
+    assert (info.group, info.fold, info.rows_per_unit) == (5, 1, 5)
+    assert info.num_units == 64 * 8 * info.num_splits and info.num_splits > 1

@@ -1,0 +1,188 @@
+"""GPU parity of paged decode (split kernel + LSE merge) against the fp64 oracle.
+
+Every case calls the HIP library through the C ABI (via the ctypes binding)
+and compares element by element with the oracle on the same seeded inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import softmax_attention_paged_amd as sap
+from softmax_attention_paged_amd import inputs
+from helpers import TOL_BF16, bits, compare, f64, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(case, num_splits=0, return_lse=True):
+    c = case.to(DEV)
+    out, lse = sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal,
+                                head_dim_v=c.head_dim_v,
+                                kv_dtype=c.kv_dtype if c.kv_dtype != "bf16" else None,
+                                k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits,
+                                return_lse=return_lse)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _check(case, num_splits=0, tol=TOL_BF16):
+    out, lse = _run(case, num_splits)
+    ref, lref = oracle_decode(case)
+    return compare(f64(out), ref, lse.numpy(), lref, tol)
+
+
+def test_tiny_gqa_decode_matches_oracle():
+    case = inputs.gqa_decode_tiny()
+    print("case", case.name, flush=True)
+    res = _check(case)
+    print(res)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7])
+def test_tiny_gqa_decode_forced_splits(splits):
+    _check(inputs.gqa_decode_tiny(), num_splits=splits)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("page_size", [16, 64, 128])
+def test_boundary_lengths(d, page_size):
+    # page and tile boundaries on both sides, a 1-key request and an empty one
+    lens = [1, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 256, 257, 511, 512, 513, 0]
+    case = inputs.decode_case(batch=len(lens), q_len=1, hq=8, hkv=2, d=d, dv=d, page_size=page_size,
+                              seq_lens=lens, seed=11 + d + page_size, layout="noncontiguous")
+    print("boundary", d, page_size, flush=True)
+    for splits in (0, 1, 3):
+        _check(case, num_splits=splits)
+
+
+@pytest.mark.parametrize("q_len,hq,hkv", [(2, 8, 2), (3, 8, 8), (4, 8, 2), (4, 20, 4), (4, 16, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_token_fold(q_len, hq, hkv, causal):
+    lens = [1, 2, 3, 5, 40, 300]
+    case = inputs.decode_case(batch=len(lens), q_len=q_len, hq=hq, hkv=hkv, d=128, dv=128, page_size=16,
+                              seq_lens=lens, seed=q_len * 100 + hq, causal=causal)
+    for splits in (0, 1, 2):
+        _check(case, num_splits=splits)
+
+
+def test_layouts_are_bitwise_identical():
+    outs = []
+    for layout in ("identity", "random", "reverse", "noncontiguous"):
+        case = inputs.decode_case(batch=3, q_len=1, hq=8, hkv=2, d=128, dv=128, page_size=16,
+                                  seq_lens=[200, 77, 513], seed=21, layout=layout)
+        outs.append(_run(case, num_splits=3))
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(l, outs[0][1])
+
+
+def test_shared_prefix_layout_is_bitwise_identical():
+    kw = dict(batch=3, q_len=1, hq=8, hkv=2, d=64, dv=64, page_size=16, seq_lens=[64, 100, 90],
+              seed=22, shared_prefix_pages=2)
+    a = _run(inputs.decode_case(layout="shared_prefix", **kw), num_splits=2)
+    b = _run(inputs.decode_case(layout="identity", **kw), num_splits=2)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    case = inputs.decode_case(batch=8, q_len=1, hq=40, hkv=8, d=128, dv=128, page_size=128,
+                              seq_len_range=(256, 2048), seed=23)
+    a, b = _run(case), _run(case)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)) and torch.equal(a[1], b[1])
+
+
+def test_constant_v_and_single_key():
+    case = inputs.decode_case(batch=3, q_len=1, hq=8, hkv=2, d=128, dv=128, page_size=16,
+                              seq_lens=[1, 50, 333], seed=24, q_mult=4.0)
+    # constant V per (request, kv head): every valid slot holds that request's row
+    vc = case.v_cache.clone()
+    bt = case.block_table
+    const = torch.randn(3, 2, 128).to(torch.bfloat16)
+    for b, n in enumerate([1, 50, 333]):
+        for j in range(n):
+            vc[int(bt[b, j // 16]), j % 16] = const[b]
+    case.v_cache = vc
+    out, lse = _run(case, num_splits=3)
+    for b in range(3):
+        for h in range(8):
+            assert torch.equal(out[b, 0, h].view(torch.int16), const[b, h // 4].view(torch.int16))
+    # single key: O is that key's V row, bitwise; LSE is its scaled score in base 2
+    kc = f64(case.k_cache)
+    qf = f64(case.q)
+    p0 = int(bt[0, 0])
+    for h in range(8):
+        assert torch.equal(out[0, 0, h].view(torch.int16), vc[p0, 0, h // 4].view(torch.int16))
+        s = case.scale * float(qf[0, 0, h] @ kc[p0, 0, h // 4])
+        assert abs(float(lse[0, 0, h]) - s / np.log(2.0)) < 1e-3
+
+
+def test_one_hot_v_rows_sum_to_one():
+    lk = 96
+    case = inputs.decode_case(batch=1, q_len=1, hq=4, hkv=1, d=128, dv=128, page_size=16,
+                              seq_lens=[lk], seed=25)
+    vc = case.v_cache.clone()
+    for j in range(lk):
+        row = torch.zeros(128)
+        row[j] = 1.0
+        vc[int(case.block_table[0, j // 16]), j % 16, 0] = row.to(torch.bfloat16)
+    case.v_cache = vc
+    out, _ = _run(case, num_splits=2)
+    p = f64(out)[0, 0]
+    assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-2
+    ref, _ = oracle_decode(case)
+    compare(p, ref[0, 0])
+
+
+def test_peaky_scores_force_rescale():
+    # Q x 8 makes scores large; a rising ramp in K forces a new max on every tile.
+    case = inputs.decode_case(batch=2, q_len=1, hq=8, hkv=2, d=128, dv=128, page_size=16,
+                              seq_lens=[700, 513], seed=26, q_mult=8.0)
+    kc = case.k_cache.clone()
+    bt = case.block_table
+    for b, n in enumerate([700, 513]):
+        for j in range(n):
+            kc[int(bt[b, j // 16]), j % 16] += (0.004 * j)
+    case.k_cache = kc
+    for splits in (1, 4):
+        _check(case, num_splits=splits)
+
+
+def test_qwen3_14b_decode_sampled_rows_full_size():
+    """The Qwen3-14B-shaped workload at full size, planned as the benchmark
+    plans it, checked on 256 sampled (request, head) rows."""
+    case = inputs.qwen3_14b_decode()
+    print("case", case.name, "tokens", int(case.seq_lens.sum()), flush=True)
+    out, lse = _run(case)
+    rng = np.random.default_rng(0)
+    rows = [(int(rng.integers(64)), 0, int(rng.integers(40))) for _ in range(256)]
+    ref, lref = oracle_decode(case, rows)
+    got = np.stack([f64(out[b, t, h]) for b, t, h in rows])
+    gl = np.array([float(lse[b, t, h]) for b, t, h in rows])
+    print(compare(got, ref, gl, lref))
+
+
+# ------------------------------------------------------------------ merge --
+
+@pytest.mark.parametrize("s,r,dv", [(1, 5, 128), (3, 100, 128), (16, 2560, 128), (7, 33, 512), (64, 10, 64)])
+def test_merge_lse_matches_oracle(s, r, dv):
+    import oracle
+    g = torch.Generator().manual_seed(s * 1000 + r)
+    o_parts = torch.randn(s, r, dv, generator=g)
+    lse_parts = torch.randn(s, r, generator=g) * 8
+    # some empty splits (-inf), and one row with every split empty
+    mask = torch.rand(s, r, generator=g) < 0.2
+    lse_parts[mask] = -float("inf")
+    lse_parts[:, 0] = -float("inf")
+    o_parts[mask] = float("nan")          # never read
+    o_parts[:, 0] = float("nan")
+    o, lse = sap.merge_lse(o_parts.to(DEV), lse_parts.to(DEV), out_dtype=torch.float32)
+    ref, lref = oracle.merge_lse(o_parts.double().numpy(), lse_parts.double().numpy())
+    res = compare(o.cpu().double().numpy(), ref, lse.cpu().double().numpy(), lref,
+                  tol=dict(max_abs=1e-5, mean_abs=1e-6), lse_tol=1e-5)
+    ob, _ = sap.merge_lse(o_parts.to(DEV), lse_parts.to(DEV), out_dtype=torch.bfloat16)
+    compare(f64(ob.cpu()), ref)
+    print(res)
