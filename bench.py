@@ -103,6 +103,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--num-splits", type=int, default=0, help="override the planner's KV split count")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of it",
@@ -124,7 +125,7 @@ def main() -> int:
     flops = tokens * q_len * hq * 2 * (d + case.head_dim_v)
 
     params = sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
-                               max_seq_len=c.max_seq_len, softmax_scale=c.scale)
+                               max_seq_len=c.max_seq_len, softmax_scale=c.scale, num_splits=args.num_splits)
     plan = sap.decode_plan(params)
     ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
     out = torch.empty((b_n, q_len, hq, case.head_dim_v), dtype=torch.bfloat16, device=dev)
@@ -132,7 +133,7 @@ def main() -> int:
 
     def step():
         sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
-                         softmax_scale=c.scale, workspace=ws, out=out)
+                         softmax_scale=c.scale, num_splits=args.num_splits, workspace=ws, out=out)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):

@@ -1,21 +1,19 @@
 // Paged GQA decode, split over the KV sequence, for gfx950.
 //
-// One workgroup = one (request b, KV head, query group, KV split) unit: the
-// G query heads that share the KV head ("Writing Page Attention with PyPTO",
-// section 1.3: one task is one batch row + one KV head + its query heads,
-// so the KV pages are read once for all of them) times the F query tokens
-// folded with them into the MFMA row dimension ("TokenSpeed-MLA", section
-// "Key Optimization ... Group q_seqlen and num_heads into BMM1 M").
+// Work unit: one request b, one KV head with the G query heads that share it
+// ("Writing Page Attention with PyPTO", section 1.3: one task is one batch row
+// + one KV head + its query heads, so the KV pages are read once for all of
+// them), the F query tokens folded with those heads into the MFMA row
+// dimension ("TokenSpeed-MLA", section "Key Optimization ... Group q_seqlen
+// and num_heads into BMM1 M"), and one KV split.
 //
-// Inside the workgroup, 4 waves take 32-key tiles of the split in turn. Each
-// wave keeps its own running max m, sum l and output o per row (the online
-// recurrence of "Flywheel Attention", section 1, and "Writing Page Attention
-// with PyPTO", section 6.3) and the waves are combined by log-sum-exp at the
-// end. Per tile:
+// A wave walks 32-key tiles of its unit and keeps a running max m, sums l
+// and output o per row (the online recurrence of "Flywheel Attention",
+// section 1, and "Writing Page Attention with PyPTO", section 6.3). Per tile:
 //   - K rows are gathered through the block table straight into registers,
 //     already in the MFMA A-operand layout (token = l % 16, 8 channels per
-//     lane); the page of a 16-key tile is one table entry (pages hold a
-//     power of two >= 16 keys), read once per tile.
+//     lane); the page of a 16-key half-tile is one table entry (pages hold a
+//     power of two >= 16 keys), read once.
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16, so each lane ends up holding
 //     8 scores of ONE row (l % 16): the softmax state is lane-local.
 //   - Invalid keys (past the split, past the request, or above the causal
@@ -27,9 +25,16 @@
 //     with ds_read_b64_tr_b16. Two row sums are kept: the rounded P that
 //     multiplied V normalises O (so a constant V comes back exactly), and
 //     the unrounded FP32 P gives the log-sum-exp.
-// With one split the workgroup writes bf16 O and the base-2 LSE; otherwise it
-// writes FP32 partials (O normalised over the split, LSE of the split) that
-// the merge kernel reduces ("TokenSpeed-MLA", section "Decode performance").
+// With one split the output is bf16 O and the base-2 LSE; otherwise FP32
+// partials (O normalised over the split, LSE of the split) that the merge
+// kernel reduces ("TokenSpeed-MLA", section "Decode performance").
+//
+// A workgroup is one unit; its 4 waves take the split's tiles in turn and
+// are combined by log-sum-exp in LDS at the end. Workgroups are numbered
+// with the query group, then the KV head, fastest: the units that read the
+// per-head slices of the same token rows ([page, slot, head, dim] stores a
+// token's heads side by side) are dispatched together, which keeps HBM
+// accesses row-local.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -39,7 +44,6 @@ namespace {
 
 template <int D>
 struct GqaGeom {
-  static constexpr int kWaves = kGqaWaves;
   static constexpr int kTile = kGqaTileTokens;                 // 32 keys per wave step
   static constexpr int kKB = D / 32;                            // QK k-steps
   static constexpr int kNB = D / 16;                            // PV 16-channel blocks
@@ -47,255 +51,292 @@ struct GqaGeom {
   static constexpr int kVTile = kTile * kVStride;               // bf16 elements per wave
   static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per V row
   static constexpr int kVChunks = kTile * kChunksPerRow / 64;   // 16-byte chunks per lane per V tile
-  static constexpr int kLdsV = kWaves * kVTile * 2;
-  static constexpr int kLdsMerge = kWaves * 16 * 4 * 3 + kWaves * 16 * D * 4;
-  static constexpr int kLds = kLdsV > kLdsMerge ? kLdsV : kLdsMerge;
-#ifndef ATTN_DECODE_PREFETCH
-#define ATTN_DECODE_PREFETCH 0
-#endif
-  // Register double-buffering of the next tile (costs ~64 VGPRs at D = 128).
-  static constexpr bool kPrefetch = ATTN_DECODE_PREFETCH && D <= 128;
 };
 
-template <int D>
-struct KvRegs {
-  bf16x8 k[2][GqaGeom<D>::kKB];
-  bf16x8 v[GqaGeom<D>::kVChunks];
+// Gather one 32-key tile of K (MFMA A layout) or V (linear 16-byte chunks).
+// Keys at or past `end` read slots of an already-valid page and are masked
+// later (K) or zeroed (V); table entries at or past `end` are never read.
+struct TilePages {
+  int64_t p0, p1;   // physical pages of keys tok0..tok0+15 and tok0+16..tok0+31
 };
 
+__device__ __forceinline__ TilePages tile_pages(const DecodeGqaArgs &a, const int32_t *bt_row, int tok0, int end) {
+  TilePages tp;
+  tp.p0 = bt_row[tok0 >> a.page_shift];
+  tp.p1 = (tok0 + 16 < end) ? (int64_t)bt_row[(tok0 + 16) >> a.page_shift] : tp.p0;
+  return tp;
+}
+
 template <int D>
-__device__ __forceinline__ void load_tile(const DecodeGqaArgs &a, const int32_t *bt_row,
-                                          const __bf16 *kbase, const __bf16 *vbase, int tok0,
-                                          int end, int lane, KvRegs<D> &r) {
+__device__ __forceinline__ void load_k(const DecodeGqaArgs &a, const __bf16 *kbase, const TilePages &tp,
+                                       int tok0, int lane, bf16x8 (&k)[2][GqaGeom<D>::kKB]) {
   using G = GqaGeom<D>;
   const int pmask = (1 << a.page_shift) - 1;
-  // One table entry per 16-key half-tile; never past the request's pages.
-  const int64_t page0 = bt_row[tok0 >> a.page_shift];
-  const int64_t page1 = (tok0 + 16 < end) ? (int64_t)bt_row[(tok0 + 16) >> a.page_shift] : page0;
   const int kg = lane >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int tok = tok0 + 16 * t + (lane & 15);
-    const int64_t page = t ? page1 : page0;
-    const __bf16 *row = kbase + page * a.k_stride_page + (int64_t)(tok & pmask) * a.k_stride_tok;
+    const __bf16 *row = kbase + (t ? tp.p1 : tp.p0) * a.k_stride_page + (int64_t)(tok & pmask) * a.k_stride_tok;
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) r.k[t][kb] = load_bf16x8(row + kb * 32 + kg * 8);
+    for (int kb = 0; kb < G::kKB; ++kb) k[t][kb] = load_bf16x8(row + kb * 32 + kg * 8);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(const DecodeGqaArgs &a, const __bf16 *vbase, const TilePages &tp,
+                                       int tok0, int end, int lane, bf16x8 (&v)[GqaGeom<D>::kVChunks]) {
+  using G = GqaGeom<D>;
+  const int pmask = (1 << a.page_shift) - 1;
 #pragma unroll
   for (int c = 0; c < G::kVChunks; ++c) {
     const int idx = c * 64 + lane;
     const int trow = idx / G::kChunksPerRow;          // 0..31
     const int col = (idx % G::kChunksPerRow) * 8;
     const int tok = tok0 + trow;
-    const int64_t page = (trow >= 16) ? page1 : page0;
-    const __bf16 *row = vbase + page * a.v_stride_page + (int64_t)(tok & pmask) * a.v_stride_tok;
-    bf16x8 v = load_bf16x8(row + col);
-    r.v[c] = (tok < end) ? v : bf16x8{};
+    const __bf16 *row = vbase + (trow >= 16 ? tp.p1 : tp.p0) * a.v_stride_page + (int64_t)(tok & pmask) * a.v_stride_tok;
+    const bf16x8 x = load_bf16x8(row + col);
+    v[c] = (tok < end) ? x : bf16x8{};
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void decode_gqa_kernel(const DecodeGqaArgs a) {
-  using G = GqaGeom<D>;
-  __shared__ __attribute__((aligned(16))) char smem[G::kLds];
+// Where a unit's rows live and which keys they see.
+struct UnitRows {
+  int b, kvh, qg, split;
+  int row;          // this lane's row (lane % 16)
+  bool row_valid;
+  int64_t ridx;     // this lane's row in [B, q_len, Hq]
+  int c0, c1;       // keys of the split any row of the unit sees
+  int row_end;      // keys < row_end are visible to this lane's row
+};
 
+__device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int kvh, int qg, int split, int lane) {
+  UnitRows u;
+  u.b = b;
+  u.kvh = kvh;
+  u.qg = qg;
+  u.split = split;
+  u.row = lane & 15;
+  u.row_valid = u.row < a.rows;
+  const int lk = a.seq_lens[b];
+  // Row r of the unit is query token qg*F + r/G, head kvh*G + r%G.
+  const int t_row = qg * a.fold + (u.row_valid ? u.row / a.group : 0);
+  const int h_row = kvh * a.group + (u.row_valid ? u.row % a.group : 0);
+  int bound = lk, unit_bound = lk;
+  if (a.causal) {
+    bound = min(lk, max(0, lk - a.q_len + t_row + 1));
+    unit_bound = min(lk, max(0, lk - a.q_len + qg * a.fold + a.fold));  // the last folded token sees most
+  }
+  u.c0 = split * a.split_tokens;
+  u.c1 = min(unit_bound, u.c0 + a.split_tokens);
+  u.row_end = min(bound, u.c1);
+  u.ridx = ((int64_t)b * a.q_len + t_row) * a.num_q_heads + h_row;
+  return u;
+}
+
+template <int D>
+struct WaveState {
+  using G = GqaGeom<D>;
+  bf16x8 qop[G::kKB];  // Q^T as the MFMA B operand: row l%16, channels 32kb + 8kg + e
+  float m;             // running max, log2 units of the scaled score
+  float lsum;          // running sum of bf16-rounded p over this lane's keys
+  float lexact;        // running sum of fp32 p over this lane's keys
+  f32x4 oacc[G::kNB];  // O^T: lane holds O[row][16nb + 4kg + i]
+
+  __device__ __forceinline__ void init(const DecodeGqaArgs &a, const UnitRows &u, int lane) {
+    const int kg = lane >> 4;
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + u.ridx * D;
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb) qop[kb] = u.row_valid ? load_bf16x8(qrow + kb * 32 + kg * 8) : bf16x8{};
+    m = kNegInf;
+    lsum = 0.f;
+    lexact = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Walk tiles first, first + stride, ... below u.c1. The registers rotate:
+  // the next tile's K loads are issued as soon as the QK MFMAs have taken
+  // the current K, and its V loads as soon as the current V is in LDS, so a
+  // wave keeps a whole tile of loads in flight while it does the softmax
+  // and PV of the current one.
+  __device__ __forceinline__ void walk(const DecodeGqaArgs &a, const UnitRows &u, int first, int stride,
+                                       __bf16 *vlds, int lane) {
+    const int kg = lane >> 4;
+    const int row = lane & 15;
+    const int32_t *bt_row = a.block_table + (int64_t)u.b * a.block_table_stride;
+    const __bf16 *kbase = static_cast<const __bf16 *>(a.k_cache) + (int64_t)u.kvh * a.k_stride_head;
+    const __bf16 *vbase = static_cast<const __bf16 *>(a.v_cache) + (int64_t)u.kvh * a.v_stride_head;
+    if (first >= u.c1) return;
+    bf16x8 kr[2][G::kKB];
+    bf16x8 vr[G::kVChunks];
+    TilePages tp = tile_pages(a, bt_row, first, u.c1);
+    load_k<D>(a, kbase, tp, first, lane, kr);
+    load_v<D>(a, vbase, tp, first, u.c1, lane, vr);
+    for (int tok0 = first; tok0 < u.c1; tok0 += stride) {
+      const int nxt = tok0 + stride;
+      const bool more = nxt < u.c1;
+      TilePages tn = tp;
+      if (more) tn = tile_pages(a, bt_row, nxt, u.c1);
+      // S^T tiles: sacc[0] keys tok0 + 4kg + i, sacc[1] keys tok0 + 16 + 4kg + i.
+      f32x4 sacc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < G::kKB; ++kb) sacc[t] = mfma16x16x32(kr[t][kb], qop[kb], sacc[t]);
+      }
+      if (more) load_k<D>(a, kbase, tn, nxt, lane, kr);
+      // V tile -> LDS (token-major), for the transposing read.
+#pragma unroll
+      for (int c = 0; c < G::kVChunks; ++c) {
+        const int idx = c * 64 + lane;
+        store_bf16x8_lds(vlds + (idx / G::kChunksPerRow) * G::kVStride + (idx % G::kChunksPerRow) * 8, vr[c]);
+      }
+      if (more) load_v<D>(a, vbase, tn, nxt, u.c1, lane, vr);
+      tp = tn;
+      float x[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = tok0 + 16 * t + 4 * kg + i;
+          const float v = (j < u.row_end) ? sacc[t][i] * a.scale_log2 : kNegInf;
+          x[4 * t + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
+      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_use);
+      bf16x8 pop;
+      float psum = 0.f, pexact = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = exp2_fast(x[e] - m_use);
+        const __bf16 pb = to_bf16(pe);
+        pop[e] = pb;
+        psum += bf16_to_f32(pb);
+        pexact += pe;
+      }
+      lsum = alpha * lsum + psum;
+      lexact = alpha * lexact + pexact;
+      m = m_new;
+#pragma unroll
+      for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] *= alpha;
+      // LDS writes of this wave must land before its transposing reads.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // O^T[16 channels x 16 rows] += V^T[channels x 32 keys] * P^T[32 keys x rows];
+      // k-slot e of lane group kg is key 4kg + e (e < 4) or 16 + 4kg + e - 4.
+      const int src_row = 4 * kg + (row >> 2);
+      const int src_col = 4 * (row & 3);
+#pragma unroll
+      for (int nb = 0; nb < G::kNB; ++nb) {
+        const bf16x4 lo = lds_read_tr16(vlds + src_row * G::kVStride + nb * 16 + src_col);
+        const bf16x4 hi = lds_read_tr16(vlds + (16 + src_row) * G::kVStride + nb * 16 + src_col);
+        oacc[nb] = mfma16x16x32(concat(lo, hi), pop, oacc[nb]);
+      }
+      // The next iteration overwrites this wave's LDS tile: the transposing
+      // reads above must have completed first (their results feed the MFMAs,
+      // so the compiler waits for them before those issue).
+    }
+  }
+
+  // Sum the per-lane-group partial sums of each row.
+  __device__ __forceinline__ void reduce_sums() {
+    lsum += wave_shfl_xor(lsum, 16);
+    lsum += wave_shfl_xor(lsum, 32);
+    lexact += wave_shfl_xor(lexact, 16);
+    lexact += wave_shfl_xor(lexact, 32);
+  }
+};
+
+// Rows of an empty unit: LSE -inf; with one split also O = 0.
+template <int D>
+__device__ __forceinline__ void write_empty(const DecodeGqaArgs &a, const UnitRows &u, int lane) {
+  if (!u.row_valid) return;
+  const int kg = lane >> 4;
+  const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
+  if (a.num_splits == 1) {
+    __bf16 *dst = static_cast<__bf16 *>(a.o) + u.ridx * D + 4 * kg;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<u32x2 *>(dst + nb * 16) = u32x2{0u, 0u};
+    if (a.lse && kg == 0) a.lse[u.ridx] = kNegInf;
+  } else if (kg == 0) {
+    a.lse_parts[(int64_t)u.split * R + u.ridx] = kNegInf;
+  }
+}
+
+// blockIdx -> (b, split, KV head, q group), q group fastest; 4 waves share the split.
+template <int D>
+struct TokensLds {
+  static constexpr int kWaves = kGqaWaves;
+  static constexpr int kV = kWaves * GqaGeom<D>::kVTile * 2;
+  static constexpr int kMerge = kWaves * 16 * 4 * 3 + kWaves * 16 * D * 4;
+  static constexpr int kBytes = kV > kMerge ? kV : kMerge;
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * kGqaWaves) void decode_gqa_tokens_kernel(const DecodeGqaArgs a) {
+  using G = GqaGeom<D>;
+  constexpr int kWaves = kGqaWaves;
+  __shared__ __attribute__((aligned(16))) char smem[TokensLds<D>::kBytes];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int kg = lane >> 4;          // lane group 0..3
-  const int row = lane & 15;         // the score/output row this lane owns
-
-  // unit -> (b, kv head, q group, split)
+  const int kg = lane >> 4;
+  const int row = lane & 15;
   int unit = blockIdx.x;
-  const int split = unit % a.num_splits;
-  unit /= a.num_splits;
   const int qg = unit % a.q_groups;
   unit /= a.q_groups;
   const int kvh = unit % a.num_kv_heads;
-  const int b = unit / a.num_kv_heads;
-
-  const int lk = a.seq_lens[b];
-  // Row r of the unit is query token qg*F + r/G, head kvh*G + r%G.
-  const bool row_valid = row < a.rows;
-  const int t_row = qg * a.fold + (row_valid ? row / a.group : 0);
-  const int h_row = kvh * a.group + (row_valid ? row % a.group : 0);
-  int bound = lk;
-  if (a.causal) bound = min(lk, max(0, lk - a.q_len + t_row + 1));
-  // keys any row of the unit may see (the last folded token sees the most)
-  int unit_bound = lk;
-  if (a.causal) unit_bound = min(lk, max(0, lk - a.q_len + qg * a.fold + a.fold));
-
-  const int c0 = split * a.split_tokens;
-  const int c1 = min(unit_bound, c0 + a.split_tokens);
-  const int row_end = min(bound, c1);
-  const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
-  const int64_t ridx = ((int64_t)b * a.q_len + t_row) * a.num_q_heads + h_row;
-
-  if (c0 >= c1) {
-    // Nothing to attend to in this split.
-    if (threadIdx.x < 64 && kg == 0 && row_valid) {
-      if (a.num_splits == 1) {
-        if (a.lse) a.lse[ridx] = kNegInf;
-      } else {
-        a.lse_parts[(int64_t)split * R + ridx] = kNegInf;
-      }
-    }
-    if (a.num_splits == 1) {
-      // rows without keys: O = 0
-      for (int ch = threadIdx.x; ch < 16 * G::kChunksPerRow; ch += 256) {
-        const int r = ch / G::kChunksPerRow;
-        if (r >= a.rows) continue;
-        const int t = qg * a.fold + r / a.group;
-        const int h = kvh * a.group + r % a.group;
-        const int64_t ri = ((int64_t)b * a.q_len + t) * a.num_q_heads + h;
-        *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(a.o) + ri * D + (ch % G::kChunksPerRow) * 8) = u32x4{};
-      }
-    }
+  unit /= a.num_kv_heads;
+  const int split = unit % a.num_splits;
+  const int b = unit / a.num_splits;
+  const UnitRows u = unit_rows(a, b, kvh, qg, split, lane);
+  if (u.c0 >= u.c1) {   // uniform over the workgroup
+    if (wave == 0) write_empty<D>(a, u, lane);
     return;
   }
+  WaveState<D> st;
+  st.init(a, u, lane);
+  st.walk(a, u, u.c0 + wave * G::kTile, kWaves * G::kTile,
+          reinterpret_cast<__bf16 *>(smem) + wave * G::kVTile, lane);
+  st.reduce_sums();
 
-  // Q^T as the MFMA B operand: row l%16, channels 32kb + 8kg + e.
-  bf16x8 qop[G::kKB];
-  {
-    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + ridx * D;
-#pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb)
-      qop[kb] = row_valid ? load_bf16x8(qrow + kb * 32 + kg * 8) : bf16x8{};
-  }
-
-  const int32_t *bt_row = a.block_table + (int64_t)b * a.block_table_stride;
-  const __bf16 *kbase = static_cast<const __bf16 *>(a.k_cache) + (int64_t)kvh * a.k_stride_head;
-  const __bf16 *vbase = static_cast<const __bf16 *>(a.v_cache) + (int64_t)kvh * a.v_stride_head;
-  __bf16 *vlds = reinterpret_cast<__bf16 *>(smem) + wave * G::kVTile;
-
-  float m = kNegInf;   // running max, log2 units of the scaled score
-  float lsum = 0.f;    // running sum of bf16-rounded p over this lane's keys
-  float lexact = 0.f;  // running sum of fp32 p over this lane's keys
-  f32x4 oacc[G::kNB];
-#pragma unroll
-  for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int tok0, const KvRegs<D> &r) {
-    // S^T tiles: acc[0] keys tok0 + 4kg + i, acc[1] keys tok0 + 16 + 4kg + i.
-    f32x4 sacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < G::kKB; ++kb) sacc[t] = mfma16x16x32(r.k[t][kb], qop[kb], sacc[t]);
-    }
-    // V tile -> LDS (token-major), for the transposing read.
-#pragma unroll
-    for (int c = 0; c < G::kVChunks; ++c) {
-      const int idx = c * 64 + lane;
-      const int trow = idx / G::kChunksPerRow;
-      const int col = (idx % G::kChunksPerRow) * 8;
-      store_bf16x8_lds(vlds + trow * G::kVStride + col, r.v[c]);
-    }
-    float x[8];
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = tok0 + 16 * t + 4 * kg + i;
-        const float v = (j < row_end) ? sacc[t][i] * a.scale_log2 : kNegInf;
-        x[4 * t + i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-    mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_use);
-    bf16x8 pop;
-    float psum = 0.f, pexact = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = exp2_fast(x[e] - m_use);
-      const __bf16 pb = to_bf16(pe);
-      pop[e] = pb;
-      psum += bf16_to_f32(pb);
-      pexact += pe;
-    }
-    lsum = alpha * lsum + psum;
-    lexact = alpha * lexact + pexact;
-    m = m_new;
-#pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] *= alpha;
-    // LDS writes of this wave must land before its transposing reads.
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // O^T[16 channels x 16 rows] += V^T[channels x 32 keys] * P^T[32 keys x rows]
-    // k-slot e of lane group kg is key 4kg + e (e < 4) or 16 + 4kg + e - 4.
-    const int src_row = 4 * kg + (row >> 2);
-    const int src_col = 4 * (row & 3);
-#pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) {
-      const bf16x4 lo = lds_read_tr16(vlds + src_row * G::kVStride + nb * 16 + src_col);
-      const bf16x4 hi = lds_read_tr16(vlds + (16 + src_row) * G::kVStride + nb * 16 + src_col);
-      oacc[nb] = mfma16x16x32(concat(lo, hi), pop, oacc[nb]);
-    }
-  };
-
-  // Two register buffers: the next tile's loads are in flight while the
-  // current one is computed.
-  const int step = G::kWaves * G::kTile;
-  int tok0 = c0 + wave * G::kTile;
-  if constexpr (G::kPrefetch) {
-    KvRegs<D> ra, rb;
-    if (tok0 < c1) load_tile<D>(a, bt_row, kbase, vbase, tok0, c1, lane, ra);
-    while (tok0 < c1) {
-      if (tok0 + step < c1) load_tile<D>(a, bt_row, kbase, vbase, tok0 + step, c1, lane, rb);
-      compute(tok0, ra);
-      tok0 += step;
-      if (tok0 >= c1) break;
-      if (tok0 + step < c1) load_tile<D>(a, bt_row, kbase, vbase, tok0 + step, c1, lane, ra);
-      compute(tok0, rb);
-      tok0 += step;
-    }
-  } else {
-    for (; tok0 < c1; tok0 += step) {
-      KvRegs<D> cur;
-      load_tile<D>(a, bt_row, kbase, vbase, tok0, c1, lane, cur);
-      compute(tok0, cur);
-    }
-  }
-
-  // ---- combine the 4 waves by log-sum-exp ----
-  lsum += wave_shfl_xor(lsum, 16);
-  lsum += wave_shfl_xor(lsum, 32);
-  lexact += wave_shfl_xor(lexact, 16);
-  lexact += wave_shfl_xor(lexact, 32);
+  // combine the waves by log-sum-exp
   __syncthreads();  // every wave is done with its V tile region
   float *sm_m = reinterpret_cast<float *>(smem);
-  float *sm_l = sm_m + G::kWaves * 16;
-  float *sm_le = sm_l + G::kWaves * 16;
-  float *sm_o = sm_le + G::kWaves * 16;
+  float *sm_l = sm_m + kWaves * 16;
+  float *sm_le = sm_l + kWaves * 16;
+  float *sm_o = sm_le + kWaves * 16;
   if (kg == 0) {
-    sm_m[wave * 16 + row] = m;
-    sm_l[wave * 16 + row] = lsum;
-    sm_le[wave * 16 + row] = lexact;
+    sm_m[wave * 16 + row] = st.m;
+    sm_l[wave * 16 + row] = st.lsum;
+    sm_le[wave * 16 + row] = st.lexact;
   }
 #pragma unroll
   for (int nb = 0; nb < G::kNB; ++nb)
-    *reinterpret_cast<f32x4 *>(sm_o + (wave * 16 + row) * D + nb * 16 + 4 * kg) = oacc[nb];
+    *reinterpret_cast<f32x4 *>(sm_o + (wave * 16 + row) * D + nb * 16 + 4 * kg) = st.oacc[nb];
   __syncthreads();
 
-  for (int ch = threadIdx.x; ch < 16 * G::kChunksPerRow; ch += 256) {
+  const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
+  for (int ch = threadIdx.x; ch < 16 * G::kChunksPerRow; ch += 64 * kWaves) {
     const int r = ch / G::kChunksPerRow;
     if (r >= a.rows) continue;
     const int c8 = (ch % G::kChunksPerRow) * 8;
-    float mw[G::kWaves];
+    float mw[kWaves];
     float mmax = kNegInf;
 #pragma unroll
-    for (int w = 0; w < G::kWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       mw[w] = sm_m[w * 16 + r];
       mmax = fmaxf(mmax, mw[w]);
     }
     const float muse = (mmax == kNegInf) ? 0.f : mmax;
-    float f[G::kWaves];
+    float f[kWaves];
     float L = 0.f, Le = 0.f;
 #pragma unroll
-    for (int w = 0; w < G::kWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       f[w] = exp2_fast(mw[w] - muse);
       L += f[w] * sm_l[w * 16 + r];
       Le += f[w] * sm_le[w * 16 + r];
@@ -305,7 +346,7 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(const DecodeGqaArgs 
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < G::kWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const f32x4 lo = *reinterpret_cast<const f32x4 *>(sm_o + (w * 16 + r) * D + c8);
       const f32x4 hi = *reinterpret_cast<const f32x4 *>(sm_o + (w * 16 + r) * D + c8 + 4);
 #pragma unroll
@@ -333,18 +374,22 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_kernel(const DecodeGqaArgs 
   }
 }
 
+template <int D>
+hipError_t launch_d(const DecodeGqaArgs &a, hipStream_t stream) {
+  const int64_t units = (int64_t)a.batch * a.num_splits * a.num_kv_heads * a.q_groups;
+  hipLaunchKernelGGL(decode_gqa_tokens_kernel<D>, dim3((unsigned)units), dim3(64 * kGqaWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode_gqa(const DecodeGqaArgs &a, hipStream_t stream) {
-  const int64_t units = (int64_t)a.batch * a.num_kv_heads * a.q_groups * a.num_splits;
-  const dim3 grid((unsigned)units), block(256);
   switch (a.head_dim) {
-    case 64: hipLaunchKernelGGL(decode_gqa_kernel<64>, grid, block, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(decode_gqa_kernel<128>, grid, block, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL(decode_gqa_kernel<256>, grid, block, 0, stream, a); break;
+    case 64: return launch_d<64>(a, stream);
+    case 128: return launch_d<128>(a, stream);
+    case 256: return launch_d<256>(a, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace attn

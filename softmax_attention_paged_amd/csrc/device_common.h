@@ -51,6 +51,11 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const void *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
 }
 
+// 16-byte streaming load (non-temporal hint: data read once).
+__device__ __forceinline__ bf16x8 load_bf16x8_stream(const void *p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+}
+
 __device__ __forceinline__ void store_bf16x8_lds(void *p, bf16x8 v) {
   *reinterpret_cast<u32x4 *>(p) = __builtin_bit_cast(u32x4, v);
 }
