@@ -73,7 +73,7 @@ def cpu_baseline(case, budget_s: float = 20.0) -> dict:
     import torch
     from threadpoolctl import threadpool_info
 
-    q = oracle.widen_bf16(case.q.view(torch.int16).numpy().view(np.uint16))
+    q = case.q.view(torch.int16).numpy().view(np.uint16)
     kc = case.k_cache.view(torch.int16).numpy().view(np.uint16)
     vc = case.v_cache.view(torch.int16).numpy().view(np.uint16)
     bt, sl = case.block_table.numpy(), case.seq_lens.numpy()
@@ -84,7 +84,7 @@ def cpu_baseline(case, budget_s: float = 20.0) -> dict:
     for b in range(b_n):
         rows = [(b, t, h) for t in range(q_len) for h in range(hq)]
         oracle.decode_paged_rows(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal,
-                                 case.head_dim_v, rows, "bf16")
+                                 case.head_dim_v, rows, "bf16", 1.0, "bf16")
         done_bytes += int(sl[b]) * row_bytes
         done_req += 1
         if time.perf_counter() - t0 >= budget_s:

@@ -174,14 +174,15 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                       block_table: np.ndarray, seq_lens: np.ndarray, page_size: int,
                       scale: float, causal: bool, head_dim_v: int,
                       rows: list[tuple[int, int, int]], kv_format: str = "f64",
-                      kv_scale: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
+                      kv_scale: float = 1.0, q_format: str = "f64") -> tuple[np.ndarray, np.ndarray]:
     """Decode attention for selected (batch, query token, query head) rows.
 
     q: [B, q_len, Hq, Dqk] float64; k_cache: [P, ps, Hkv, Dqk];
     v_cache: [P, ps, Hkv, >=Dv] (V is its first head_dim_v entries); caches
     hold values (kv_format "f64") or raw storage ("bf16", "e4m3fn" with
-    kv_scale), widened after gathering; block_table: [B, max_pages] ints;
-    seq_lens: [B] ints. Returns o [len(rows), Dv] and lse2 [len(rows)].
+    kv_scale), widened after gathering; q likewise ("f64" or "bf16" bits);
+    block_table: [B, max_pages] ints; seq_lens: [B] ints.
+    Returns o [len(rows), Dv] and lse2 [len(rows)].
     """
     _, q_len, hq, _ = q.shape
     hkv = k_cache.shape[2]
@@ -196,7 +197,7 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         k = widen(gather_paged_rows(k_cache, block_table[b], lk, page_size, g), kv_format, kv_scale)
         v = widen(gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v),
                   kv_format, kv_scale)
-        qr = np.stack([q[rows[n][0], rows[n][1], rows[n][2]] for n in members])
+        qr = widen(np.stack([q[rows[n][0], rows[n][1], rows[n][2]] for n in members]), q_format)
         t = np.array([rows[n][1] for n in members], dtype=np.int64)
         bound = causal_key_bound(t, q_len, lk) if causal else np.full(len(members), lk)
         o_m, l_m = attention_rows(qr, k, v, scale, bound)
@@ -206,13 +207,13 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size, scale,
-                 causal, head_dim_v, kv_format="f64", kv_scale=1.0):
+                 causal, head_dim_v, kv_format="f64", kv_scale=1.0, q_format="f64"):
     """Decode attention for every row: returns o [B, q_len, Hq, Dv] and
     lse2 [B, q_len, Hq]."""
     b_n, q_len, hq, _ = q.shape
     rows = [(b, t, h) for b in range(b_n) for t in range(q_len) for h in range(hq)]
     o, lse2 = decode_paged_rows(q, k_cache, v_cache, block_table, seq_lens, page_size,
-                                scale, causal, head_dim_v, rows, kv_format, kv_scale)
+                                scale, causal, head_dim_v, rows, kv_format, kv_scale, q_format)
     return o.reshape(b_n, q_len, hq, head_dim_v), lse2.reshape(b_n, q_len, hq)
 
 
@@ -245,7 +246,7 @@ def prefill_dense(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, causal):
 
 
 def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
-                       page_size, scale, causal, head_dim_v, rows, kv_format="f64"):
+                       page_size, scale, causal, head_dim_v, rows, kv_format="f64", q_format="f64"):
     """Ragged prefill over a paged cache for selected (query token, head) rows,
     where the query token index is global in the packed Q. Caches hold values
     or raw bf16 bits (kv_format "bf16"), widened after gathering."""
@@ -264,7 +265,7 @@ def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_tab
         lk = int(seq_lens_kv[b])
         k = widen(gather_paged_rows(k_cache, block_table[b], lk, page_size, g), kv_format)
         v = widen(gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v), kv_format)
-        qr = np.stack([q[rows[n][0], rows[n][1]] for n in members])
+        qr = widen(np.stack([q[rows[n][0], rows[n][1]] for n in members]), q_format)
         i = np.array([rows[n][0] - cu[b] for n in members], dtype=np.int64)
         bound = causal_key_bound(i, lq, lk) if causal else np.full(len(members), lk)
         o_m, l_m = attention_rows(qr, k, v, scale, bound)
@@ -274,13 +275,14 @@ def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_tab
 
 
 def prefill_paged(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
-                  page_size, scale, causal, head_dim_v, kv_format="f64"):
+                  page_size, scale, causal, head_dim_v, kv_format="f64", q_format="f64"):
     """Ragged prefill over a paged cache for every row: o [Tq, Hq, Dv],
     lse2 [Tq, Hq]."""
     tq, hq, _ = q.shape
     rows = [(t, h) for t in range(tq) for h in range(hq)]
     o, lse2 = prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv,
-                                 block_table, page_size, scale, causal, head_dim_v, rows, kv_format)
+                                 block_table, page_size, scale, causal, head_dim_v, rows, kv_format,
+                                 q_format)
     return o.reshape(tq, hq, head_dim_v), lse2.reshape(tq, hq)
 
 

@@ -44,7 +44,7 @@ def f64(t: torch.Tensor) -> np.ndarray:
 def oracle_decode(case, rows=None):
     """Oracle output for a DecodeCase: full ([B,q,H,Dv], [B,q,H]) or, with
     rows=[(b,t,h)...], ([n,Dv], [n])."""
-    q = f64(case.q)
+    q = bits(case.q)
     fmt = "bf16" if case.kv_dtype == "bf16" else "e4m3fn"
     kc = bits(case.k_cache)
     vc = kc if case.v_cache is None else bits(case.v_cache)
@@ -52,13 +52,15 @@ def oracle_decode(case, rows=None):
     sl = case.seq_lens.numpy()
     if rows is None:
         return oracle.decode_paged(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal, case.head_dim_v,
-                                   fmt, case.kv_scale)
+                                   fmt, case.kv_scale, "bf16")
     return oracle.decode_paged_rows(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal,
-                                    case.head_dim_v, rows, fmt, case.kv_scale)
+                                    case.head_dim_v, rows, fmt, case.kv_scale, "bf16")
 
 
 def oracle_prefill(case, rows=None):
-    q = f64(case.q)
+    """Oracle output for a PrefillCase: full ([Tq,H,Dv], [Tq,H]) or, with
+    rows=[(token, head)...], ([n,Dv], [n])."""
+    q = bits(case.q)
     if case.paged:
         k, v = bits(case.k), bits(case.v)
         bt = case.block_table.numpy()
@@ -66,30 +68,34 @@ def oracle_prefill(case, rows=None):
         cu = case.cu_seqlens_q.numpy()
         if rows is None:
             return oracle.prefill_paged(q, k, v, cu, sl, bt, case.page_size, case.scale, case.causal,
-                                        v.shape[-1], "bf16")
+                                        v.shape[-1], "bf16", "bf16")
         return oracle.prefill_paged_rows(q, k, v, cu, sl, bt, case.page_size, case.scale, case.causal,
-                                         v.shape[-1], rows, "bf16")
-    k = f64(case.k)
-    v = f64(case.v)
+                                         v.shape[-1], rows, "bf16", "bf16")
     cu_q = case.cu_seqlens_q.numpy()
     cu_k = case.cu_seqlens_kv.numpy()
     if rows is None:
-        return oracle.prefill_dense(q, k, v, cu_q, cu_k, case.scale, case.causal)
-    # rows of a dense case: route through the paged-rows function with a
-    # one-token-per-page identity layout? Simpler: per (token, head) row.
-    hq, hkv = q.shape[1], k.shape[1]
+        return oracle.prefill_dense(oracle.widen_bf16(q), f64(case.k), f64(case.v), cu_q, cu_k, case.scale,
+                                    case.causal)
+    # sampled rows of a dense case: widen only the (request, KV head) slices used
+    kb, vb = bits(case.k), bits(case.v)
+    hq, hkv = q.shape[1], kb.shape[1]
     group = hq // hkv
-    o = np.zeros((len(rows), v.shape[-1]))
+    o = np.zeros((len(rows), vb.shape[-1]))
     lse = np.full(len(rows), -np.inf)
+    by = {}
     for n, (tok, h) in enumerate(rows):
         b = int(np.searchsorted(cu_q, tok, side="right") - 1)
+        by.setdefault((b, h // group), []).append(n)
+    for (b, g), members in by.items():
         lq, lk = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b + 1] - cu_k[b])
-        i = tok - cu_q[b]
-        bound = oracle.attention.causal_key_bound(np.array([i]), lq, lk) if case.causal else np.array([lk])
         k0 = int(cu_k[b])
-        on, ln = oracle.attention_rows(q[tok, h][None], k[k0:k0 + lk, h // group], v[k0:k0 + lk, h // group],
-                                       case.scale, bound)
-        o[n], lse[n] = on[0], ln[0]
+        k = oracle.widen_bf16(kb[k0:k0 + lk, g])
+        v = oracle.widen_bf16(vb[k0:k0 + lk, g])
+        qr = oracle.widen_bf16(np.stack([q[rows[n][0], rows[n][1]] for n in members]))
+        i = np.array([rows[n][0] - cu_q[b] for n in members])
+        bound = oracle.attention.causal_key_bound(i, lq, lk) if case.causal else np.full(len(members), lk)
+        on, ln = oracle.attention_rows(qr, k, v, case.scale, bound)
+        o[members], lse[members] = on, ln
     return o, lse
 
 

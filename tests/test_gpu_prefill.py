@@ -1,0 +1,114 @@
+"""GPU parity of ragged prefill (dense and paged KV) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import softmax_attention_paged_amd as sap
+from softmax_attention_paged_amd import inputs
+from helpers import compare, f64, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(case):
+    c = case.to(DEV)
+    kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale,
+              causal=c.causal, return_lse=True)
+    if c.paged:
+        out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv,
+                               block_table=c.block_table, **kw)
+    else:
+        out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, cu_seqlens_kv=c.cu_seqlens_kv, **kw)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _check(case):
+    out, lse = _run(case)
+    ref, lref = oracle_prefill(case)
+    return compare(f64(out), ref, lse.numpy(), lref)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (6, 2), (4, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_ragged(d, hq, hkv, causal):
+    lens = [1, 37, 128, 200, 129]
+    case = inputs.prefill_case(q_lens=lens, kv_lens=lens, hq=hq, hkv=hkv, d=d, seed=d + hq + 7 * causal,
+                               causal=causal)
+    print("dense", d, hq, hkv, causal, flush=True)
+    print(_check(case))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunked_bottom_right(d):
+    # fewer queries than keys (chunked prefill), and more queries than keys
+    # (the first rows see no key: O = 0, LSE = -inf)
+    case = inputs.prefill_case(q_lens=[5, 64, 130, 40, 1], kv_lens=[300, 64, 1000, 17, 0], hq=8, hkv=2, d=d,
+                               seed=31 + d, causal=True)
+    print(_check(case))
+    case = inputs.prefill_case(q_lens=[5, 64, 130, 40], kv_lens=[300, 64, 1000, 17], hq=8, hkv=2, d=d,
+                               seed=32 + d, causal=False)
+    print(_check(case))
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+@pytest.mark.parametrize("layout", ["random", "noncontiguous", "reverse"])
+def test_paged_matches_oracle_and_dense_bitwise(page_size, layout):
+    q_lens, kv_lens = [3, 100, 64, 257], [500, 100, 77, 1024]
+    kw = dict(q_lens=q_lens, kv_lens=kv_lens, hq=8, hkv=2, d=128, seed=41, causal=True)
+    paged = inputs.prefill_case(paged=True, page_size=page_size, layout=layout, **kw)
+    dense = inputs.prefill_case(**kw)
+    assert torch.equal(paged.q, dense.q)
+    po, pl = _run(paged)
+    do, dl = _run(dense)
+    assert torch.equal(po.view(torch.int16), do.view(torch.int16)) and torch.equal(pl, dl)
+    ref, lref = oracle_prefill(paged)
+    print(compare(f64(po), ref, pl.numpy(), lref))
+
+
+def test_constant_v_and_single_key():
+    case = inputs.prefill_case(q_lens=[70], kv_lens=[70], hq=2, hkv=1, d=128, seed=51, causal=True, q_mult=4.0)
+    const = torch.randn(128).to(torch.bfloat16)
+    case.v = const.expand_as(case.v).contiguous()
+    out, lse = _run(case)
+    assert torch.equal(out.view(torch.int16), const.expand_as(out).contiguous().view(torch.int16))
+    # causal row 0 sees only key 0: its LSE is that score in base 2
+    qf, kf = f64(case.q), f64(case.k)
+    for h in range(2):
+        s = case.scale * float(qf[0, h] @ kf[0, 0])
+        assert abs(float(lse[0, h]) - s / np.log(2.0)) < 1e-3
+
+
+def test_peaky_scores():
+    case = inputs.prefill_case(q_lens=[300, 77], kv_lens=[700, 77], hq=4, hkv=4, d=128, seed=52, causal=True,
+                               q_mult=8.0)
+    print(_check(case))
+
+
+def _sampled(case, n_rows, seed=0):
+    out, lse = _run(case)
+    rng = np.random.default_rng(seed)
+    tq, hq = case.q.shape[0], case.q.shape[1]
+    rows = [(int(rng.integers(tq)), int(rng.integers(hq))) for _ in range(n_rows)]
+    rows += [(0, 0), (tq - 1, hq - 1)]
+    ref, lref = oracle_prefill(case, rows)
+    got = np.stack([f64(out[t, h]) for t, h in rows])
+    gl = np.array([float(lse[t, h]) for t, h in rows])
+    return compare(got, ref, gl, lref)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_dense_causal_prefill_8k_sampled(d):
+    case = inputs.dense_causal_prefill(d=d)
+    print("case", case.name, flush=True)
+    print(_sampled(case, 96))
+
+
+def test_ragged_paged_prefill_80k_sampled():
+    case = inputs.ragged_paged_prefill()
+    print("case", case.name, flush=True)
+    print(_sampled(case, 48))
