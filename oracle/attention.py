@@ -74,15 +74,22 @@ def widen_e4m3fn(codes: np.ndarray, scale: float = 1.0) -> np.ndarray:
     per-tensor dequantisation scale multiplies the decoded value
     ("TokenSpeed-MLA": FP8 e4m3 KV inputs; one scale per tensor).
     """
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return _E4M3FN_VALUES[np.asarray(codes, dtype=np.uint8)] * float(scale)
+
+
+def _e4m3fn_value_table() -> np.ndarray:
+    """The value of each of the 256 E4M3 codes, from the format's definition."""
+    c = np.arange(256, dtype=np.int64)
     sign = np.where((c >> 7) & 1, -1.0, 1.0)
     exp = (c >> 3) & 0xF
     man = (c & 0x7).astype(np.float64)
     normal = (1.0 + man / 8.0) * np.exp2(exp.astype(np.float64) - 7.0)
     subnormal = man * 2.0 ** -9
     val = sign * np.where(exp == 0, subnormal, normal)
-    val = np.where((exp == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
-    return val * float(scale)
+    return np.where((exp == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+
+
+_E4M3FN_VALUES = _e4m3fn_value_table()
 
 
 def widen(x: np.ndarray, kv_format: str = "f64", kv_scale: float = 1.0) -> np.ndarray:

@@ -268,7 +268,9 @@ attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream)
     a.kv_stride_page = p->k_stride_page;
     a.kv_stride_tok = p->k_stride_tok;
     a.kv_fp8 = p->kv_dtype == ATTN_FP8_E4M3;
-    a.kv_scale = p->k_scale;
+    // FP8 codes are used as stored: k_scale folds into the score scale,
+    // v_scale into the output normalisation.
+    a.kv_scale = a.kv_fp8 ? p->v_scale : 1.0f;
     a.seq_lens = p->seq_lens;
     a.block_table = p->block_table;
     a.block_table_stride = p->block_table_stride;
@@ -281,7 +283,7 @@ attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream)
     a.rows = pl.rows;
     a.num_splits = pl.splits;
     a.split_tokens = pl.split_tokens;
-    a.scale_log2 = scale_log2;
+    a.scale_log2 = a.kv_fp8 ? scale_log2 * p->k_scale : scale_log2;
     a.causal = p->causal;
     a.o = p->o;
     a.lse = p->lse;

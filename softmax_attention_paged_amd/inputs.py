@@ -141,10 +141,12 @@ def _scatter_pages(tokens: torch.Tensor, layout: PagedLayout, page_size: int, fi
 
 
 def _fp8_codes(x: np.ndarray) -> tuple[torch.Tensor, float]:
-    amax = float(np.max(np.abs(x))) if x.size else 1.0
-    scale = amax / FP8_MAX if amax > 0 else 1.0
-    t = torch.from_numpy(x / np.float32(scale)).clamp_(-FP8_MAX, FP8_MAX)
-    return t.to(torch.float8_e4m3fn).view(torch.uint8), float(np.float32(scale))
+    """Codes of x / scale with scale = amax / 448 (x is consumed)."""
+    t = torch.from_numpy(x)
+    amax = float(torch.linalg.vector_norm(t, ord=float("inf"))) if x.size else 1.0
+    scale = float(np.float32(amax / FP8_MAX)) if amax > 0 else 1.0
+    t.div_(scale).clamp_(-FP8_MAX, FP8_MAX)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8), scale
 
 
 def _share_prefix(x: np.ndarray, seq_lens: list[int], tokens: int) -> None:

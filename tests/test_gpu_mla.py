@@ -1,0 +1,71 @@
+"""GPU parity of the MLA-shaped latent decode (576-wide K, V = first 512 columns,
+bf16 or fp8 e4m3 KV with a per-tensor scale) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import softmax_attention_paged_amd as sap
+from softmax_attention_paged_amd import inputs
+from helpers import TOL_BF16, TOL_FP8, compare, f64, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(case, num_splits=0):
+    c = case.to(DEV)
+    out, lse = sap.decode_paged(c.q, c.k_cache, None, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
+                                softmax_scale=c.scale, causal=c.causal, head_dim_v=512,
+                                kv_dtype=None if c.kv_dtype == "bf16" else c.kv_dtype,
+                                k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits, return_lse=True)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def _check(case, num_splits=0):
+    out, lse = _run(case, num_splits)
+    ref, lref = oracle_decode(case)
+    return compare(f64(out), ref, lse.numpy(), lref, TOL_BF16 if case.kv_dtype == "bf16" else TOL_FP8)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("hq,q_len", [(64, 4), (16, 4), (128, 1), (8, 3), (32, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_latent_decode_small(kv_dtype, hq, q_len, causal):
+    case = inputs.decode_case(batch=3, q_len=q_len, hq=hq, hkv=1, d=576, dv=512, page_size=16,
+                              seq_lens=[3, 37, 300], seed=hq + q_len, kv_dtype=kv_dtype, latent=True,
+                              scale=0.07216882, causal=causal, layout="noncontiguous")
+    print(kv_dtype, hq, q_len, causal, flush=True)
+    for splits in (0, 1, 3):
+        print(_check(case, splits))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_latent_layouts_bitwise(kv_dtype):
+    outs = []
+    for layout in ("identity", "random", "reverse"):
+        case = inputs.decode_case(batch=2, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
+                                  seq_lens=[1000, 129], seed=61, kv_dtype=kv_dtype, latent=True,
+                                  scale=0.07216882, causal=True, layout=layout)
+        outs.append(_run(case, num_splits=2))
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_mla_decode_80k_sampled(kv_dtype, causal):
+    """The MLA-shaped workload at full size (batch 8, 4 tokens, 64 heads,
+    kv_len 81920), planned as the benchmark plans it, on sampled rows."""
+    case = inputs.mla_decode(kv_dtype=kv_dtype, causal=causal)
+    print("case", case.name, flush=True)
+    out, lse = _run(case)
+    rng = np.random.default_rng(1)
+    rows = [(int(rng.integers(8)), int(rng.integers(4)), int(rng.integers(64))) for _ in range(24)]
+    rows += [(0, 0, 0), (7, 3, 63)]
+    ref, lref = oracle_decode(case, rows)
+    got = np.stack([f64(out[b, t, h]) for b, t, h in rows])
+    gl = np.array([float(lse[b, t, h]) for b, t, h in rows])
+    print(compare(got, ref, gl, lref, TOL_BF16 if kv_dtype == "bf16" else TOL_FP8))

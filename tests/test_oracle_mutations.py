@@ -27,6 +27,7 @@ MUTATIONS = [
     ("o[idx] = (e @ v) / l", "o[idx] = (e @ v)"),                                  # missing normalisation
     ("e = np.exp(s - m)", "e = np.exp(m - s)"),                                    # flipped sign
     ("np.exp2(exp.astype(np.float64) - 7.0)", "np.exp2(exp.astype(np.float64) - 8.0)"),  # FNUZ-style bias
+    ("subnormal = man * 2.0 ** -9", "subnormal = man * 2.0 ** -10"),              # wrong subnormal step
     ("np.exp2(lse_parts - top_safe[None, :])", "np.exp(lse_parts - top_safe[None, :])"),  # merge in wrong base
     ("alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)",
      "alpha = np.where(np.isfinite(m), 1.0, 0.0)"),                                # recurrence without rescale
