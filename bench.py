@@ -96,6 +96,72 @@ def cpu_baseline(case, budget_s: float = 20.0) -> dict:
                       f"fp64 numpy, BLAS pool of {threads} threads"}
 
 
+def causal_pairs(cu_q: list[int], kv_lens: list[int], causal: bool) -> int:
+    """Unmasked (query, key) pairs of a ragged batch (bottom-right causal)."""
+    tot = 0
+    for b, lk in enumerate(kv_lens):
+        lq = cu_q[b + 1] - cu_q[b]
+        if not causal:
+            tot += lq * lk
+            continue
+        for i in range(lq):
+            tot += min(lk, max(0, lk - lq + i + 1))
+    return tot
+
+
+def secondary_prefill(name_fn, steps: int) -> dict:
+    import torch
+    import softmax_attention_paged_amd as sap
+    case = name_fn()
+    c = case.to("cuda:0")
+    hq, d = case.q.shape[1], case.q.shape[2]
+    flops = causal_pairs(case.cu_seqlens_q.tolist(), case.seq_lens_kv.tolist(), case.causal) * hq * 2 * (d + d)
+    out = torch.empty_like(c.q)
+    lse = torch.empty((c.q.shape[0], hq), dtype=torch.float32, device=c.q.device)
+    kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale, causal=c.causal,
+              out=out)
+    if c.paged:
+        fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv,
+                                 block_table=c.block_table, **kw)
+    else:
+        fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, cu_seqlens_kv=c.cu_seqlens_kv, **kw)
+    for _ in range(3):
+        fn()
+    ms = time_events(fn, steps, torch.cuda.current_stream())
+    del lse
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+            "roofline": {"bound": "mfma", "kernel": f"prefill_kernel<{d}>", "achieved": round(tf, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+
+
+def secondary_mla(kv_dtype: str, steps: int) -> dict:
+    import torch
+    import softmax_attention_paged_amd as sap
+    from softmax_attention_paged_amd import inputs
+    case = inputs.mla_decode(kv_dtype=kv_dtype)
+    c = case.to("cuda:0")
+    b_n, q_len, hq, dqk = case.q.shape
+    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal, head_dim_v=512,
+              kv_dtype=None if kv_dtype == "bf16" else kv_dtype, k_scale=c.kv_scale, v_scale=c.kv_scale)
+    plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, None, c.block_table, c.seq_lens, **kw))
+    ws = torch.empty(plan["workspace_bytes"] + 16, dtype=torch.uint8, device=c.q.device)
+    out = torch.empty((b_n, q_len, hq, 512), dtype=torch.bfloat16, device=c.q.device)
+    fn = lambda: sap.decode_paged(c.q, c.k_cache, None, c.block_table, c.seq_lens, workspace=ws, out=out, **kw)
+    for _ in range(3):
+        fn()
+    ms = time_events(fn, steps, torch.cuda.current_stream())
+    lens = case.seq_lens.tolist()
+    pairs = hq * sum(min(lk, max(0, lk - q_len + t + 1)) if case.causal else lk for lk in lens for t in range(q_len))
+    flops = pairs * 2 * (dqk + 512)
+    tf = flops / (ms * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS   # the kernel runs bf16 MFMA for both KV formats
+    return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+            "kv_GB/s": round(case.kv_read_bytes() / (ms * 1e-3) / 1e9, 1), "num_splits": plan["num_splits"],
+            "roofline": {"bound": "mfma", "kernel": "decode_mla_kernel + merge", "achieved": round(tf, 1),
+                         "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +170,19 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--num-splits", type=int, default=0, help="override the planner's KV split count")
+    ap.add_argument("--no-secondary", action="store_true", help="time only the main workload")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 3 device-to-device copies of BYTES (reference for HBM counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration}))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this path runs on one GPU; multi-GPU runs are not part of it",
                           "n_gpus": args.gpus}))
@@ -187,6 +265,21 @@ def main() -> int:
                      "merge_avg_launch_ms": round(merge_ms, 5)},
         "decode_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
     }
+    if not args.no_secondary:
+        del c, ws, out
+        torch.cuda.empty_cache()
+        sec = {}
+        for key, fn in [("dense_causal_prefill_d128", lambda: inputs.dense_causal_prefill(d=128)),
+                        ("dense_causal_prefill_d256", lambda: inputs.dense_causal_prefill(d=256)),
+                        ("ragged_paged_prefill_80k", inputs.ragged_paged_prefill)]:
+            log(f"secondary {key} ...")
+            sec[key] = secondary_prefill(fn, max(3, args.steps // 5))
+            torch.cuda.empty_cache()
+        for kv in ("bf16", "fp8_e4m3"):
+            log(f"secondary mla_decode_{kv} ...")
+            sec[f"mla_decode_80k_{kv}"] = secondary_mla(kv, max(3, args.steps // 5))
+            torch.cuda.empty_cache()
+        line["secondary"] = sec
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         line["cpu_baseline"] = cpu_baseline(case)
