@@ -171,6 +171,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--num-splits", type=int, default=0, help="override the planner's KV split count")
     ap.add_argument("--no-secondary", action="store_true", help="time only the main workload")
+    ap.add_argument("--only", default="", metavar="WORKLOAD",
+                    help="time one secondary workload alone (for profiling): dense_causal_prefill_d128, "
+                         "dense_causal_prefill_d256, ragged_paged_prefill_80k, mla_decode_80k_bf16, "
+                         "mla_decode_80k_fp8_e4m3")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (reference for HBM counters)")
     args = ap.parse_args()
@@ -191,6 +195,17 @@ def main() -> int:
     import torch
     import softmax_attention_paged_amd as sap
     from softmax_attention_paged_amd import inputs
+
+    secondaries = {
+        "dense_causal_prefill_d128": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=128), steps),
+        "dense_causal_prefill_d256": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=256), steps),
+        "ragged_paged_prefill_80k": lambda steps: secondary_prefill(inputs.ragged_paged_prefill, steps),
+        "mla_decode_80k_bf16": lambda steps: secondary_mla("bf16", steps),
+        "mla_decode_80k_fp8_e4m3": lambda steps: secondary_mla("fp8_e4m3", steps),
+    }
+    if args.only:
+        print(json.dumps({args.only: secondaries[args.only](args.steps)}), flush=True)
+        return 0
 
     log("generating inputs ...")
     case = inputs.qwen3_14b_decode(seed=args.seed)
@@ -269,15 +284,9 @@ def main() -> int:
         del c, ws, out
         torch.cuda.empty_cache()
         sec = {}
-        for key, fn in [("dense_causal_prefill_d128", lambda: inputs.dense_causal_prefill(d=128)),
-                        ("dense_causal_prefill_d256", lambda: inputs.dense_causal_prefill(d=256)),
-                        ("ragged_paged_prefill_80k", inputs.ragged_paged_prefill)]:
+        for key, fn in secondaries.items():
             log(f"secondary {key} ...")
-            sec[key] = secondary_prefill(fn, max(3, args.steps // 5))
-            torch.cuda.empty_cache()
-        for kv in ("bf16", "fp8_e4m3"):
-            log(f"secondary mla_decode_{kv} ...")
-            sec[f"mla_decode_80k_{kv}"] = secondary_mla(kv, max(3, args.steps // 5))
+            sec[key] = fn(max(3, args.steps // 5))
             torch.cuda.empty_cache()
         line["secondary"] = sec
     if not args.no_cpu_baseline:

@@ -7,23 +7,32 @@
 // base-2 log-sum-exp ("TokenSpeed-MLA", kernel capability summary: optional
 // FP32 LSE, base-2 semantics).
 //
-// Workgroup = 4 waves = 128 query rows that share one KV head: GH query heads
-// of a GQA group (GH in {1, 2, 4}) times 128 / GH consecutive query tokens.
-// Wave w owns 32 rows: tokens of one head. Per 64-key tile (32 at D = 256):
+// A workgroup owns W waves x RB blocks of 32 query rows that share one KV
+// head: GH query heads of a GQA group (GH in {1, 2, 4}) times consecutive
+// query tokens. Each 32-row block is 32 tokens of one head. Per key tile:
 //   - the tile's K and V rows are gathered (through the block table when
-//     paged, "Writing Page Attention with PyPTO", section 5.2) with 16-byte
-//     loads into registers one tile ahead, then stored to a double-buffered,
-//     padded LDS tile; keys past the request are zeroed, table entries past
-//     its last page are never read (section 9);
-//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q^T held in registers, so
-//     each lane holds 16 scores of one row per 32 keys;
+//     paged, "Writing Page Attention with PyPTO", section 5.2) one tile ahead
+//     with direct HBM -> LDS loads (global_load_lds_dwordx4) into a double
+//     buffer whose 16-byte chunks are XOR-swizzled against bank conflicts;
+//     keys past the request are zeroed, table entries past its last page are
+//     never read (section 9);
+//   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q^T in registers: each lane
+//     holds 16 scores of one row per 32 keys. Every K operand read from LDS
+//     feeds the RB row blocks of the wave;
 //   - masking (tail, and above the bottom-right causal diagonal) only on the
-//     tiles that reach a row bound; masked scores are -inf before the max;
+//     tiles that reach a row bound, decided once per tile for the wave;
+//   - the row max is kept lazily: a row re-bases (and rescales O) only when
+//     its max rises by more than 8 in log2 units, so P <= 2^8 ("TokenSpeed-
+//     MLA", section "SM107 decode": the base is retained for rises up to 4
+//     log2 units, 8 for split chunks; "Flywheel Attention", section 1: FA-4
+//     skips the rescale when the max barely moves). The result is the same
+//     softmax, the final division uses the same base;
 //   - P rounded to bf16 (RNE) is the B operand of O^T += V^T P^T straight
-//     from the score registers; V^T comes from LDS via ds_read_b64_tr_b16.
-// The rounded P sums normalise O, the FP32 P sums give the LSE. Query tiles
-// are aligned to the END of each request, so tile 0 of every request sees
-// the most keys and is launched first.
+//     from the score registers; V^T comes from LDS via ds_read_b64_tr_b16
+//     and each V^T operand feeds all RB row blocks.
+// The FP32 P sums normalise O and give the LSE. Query tiles are aligned to
+// the END of each request, so tile 0 of every request sees the most keys and
+// is launched first.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -31,50 +40,82 @@
 namespace attn {
 namespace {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfRows = 32;                  // rows per wave
-constexpr int kPfBlockRows = kPfWaves * kPfRows;
+// W waves per workgroup, RB 32-row blocks per wave, N keys per tile, WPE
+// waves per SIMD the registers are budgeted for. One row block per wave at
+// two waves per SIMD beats two row blocks per wave at one (measured: the
+// extra accumulators spill into AGPR traffic); D = 256 needs a whole SIMD's
+// registers for its Q operand and O accumulator.
+template <int D> struct PfCfg;
+template <> struct PfCfg<64> { static constexpr int W = 4, RB = 1, N = 64, WPE = 2; };
+template <> struct PfCfg<128> { static constexpr int W = 4, RB = 1, N = 64, WPE = 2; };
+template <> struct PfCfg<256> { static constexpr int W = 4, RB = 1, N = 32, WPE = 1; };
 
 template <int D>
 struct PfGeom {
-  static constexpr int kN = D <= 128 ? 64 : 32;       // keys per tile
+  static constexpr int kW = PfCfg<D>::W;              // waves per workgroup
+  static constexpr int kRB = PfCfg<D>::RB;            // 32-row blocks per wave
+  static constexpr int kBlocks = kW * kRB;            // 32-row blocks per workgroup
+  static constexpr int kN = PfCfg<D>::N;              // keys per tile
   static constexpr int kSub = kN / 32;                // 32-key S^T sub-tiles
+  static constexpr int kKK = kN / 16;                 // 16-key PV steps
   static constexpr int kKB = D / 16;                  // QK k-steps (16 channels)
   static constexpr int kNB = D / 32;                  // PV 32-channel blocks
-  static constexpr int kStride = D + 16;              // LDS row stride (bf16)
-  static constexpr int kTileElems = kN * kStride;
-  static constexpr int kChunksPerRow = D / 8;         // 16-byte chunks per row
-  static constexpr int kChunks = kN * kChunksPerRow / (64 * kPfWaves);  // per thread, per tensor
-  static constexpr int kLds = 2 /*K,V*/ * 2 /*buffers*/ * kTileElems * 2;
+  static constexpr int kTileElems = kN * D;           // unpadded rows, 16-byte chunks swizzled
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kLoads = kN * kChunksPerRow / 64 / kW;   // 1 KB direct loads per wave per tensor
 };
 
+constexpr float kRebase = 8.0f;   // log2 units a row max may rise before the row re-bases
+
+// LDS tiles are unpadded [keys][D] with the 16-byte chunks of row r stored at
+// slot chunk ^ f(r). f spreads the 16 rows a K-operand read touches over all
+// 64 banks, and gives the 4 rows x 4 chunks of a transposing V read (32
+// lanes) distinct banks too.
+template <int D>
+__device__ __forceinline__ int pf_swz(int row) {
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// max / sum over the two 32-lane halves, in every lane (v_permlane32_swap)
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct PfUnit {
-  int b, kvh, h0, gh;          // request, KV head, first query head, heads per workgroup
+  int b, kvh, h0;              // request, KV head, first query head of the workgroup
   int q_begin, q_end;          // query rows of the request covered by this workgroup (relative)
   int lq, lk;                  // request lengths
   int64_t q_off;               // first query token of the request in the packed Q
   int64_t kv_off;              // dense: first key of the request in packed K/V
 };
 
+// Issue the direct HBM -> LDS loads of one K and one V tile (16 bytes per
+// lane, lane i of a wave instruction lands at 16 i bytes past the
+// instruction's LDS base). Keys at or past the request's end get zeros with
+// ordinary LDS stores instead, so no table entry or row past the end is read.
 template <int D>
-struct PfTileRegs {
-  bf16x8 k[PfGeom<D>::kChunks];
-  bf16x8 v[PfGeom<D>::kChunks];
-};
-
-template <int D>
-__device__ __forceinline__ void pf_load_tile(const PrefillArgs &a, const PfUnit &u, int j0, int tid,
-                                             PfTileRegs<D> &r) {
+__device__ __forceinline__ void pf_issue_tile(const PrefillArgs &a, const PfUnit &u, int j0, int wave, int lane,
+                                              __bf16 *klds, __bf16 *vlds) {
   using G = PfGeom<D>;
   const int32_t *bt_row = a.block_table ? a.block_table + (int64_t)u.b * a.block_table_stride : nullptr;
   const int pmask = (1 << a.page_shift) - 1;
 #pragma unroll
-  for (int c = 0; c < G::kChunks; ++c) {
-    const int idx = c * 64 * kPfWaves + tid;
-    const int trow = idx / G::kChunksPerRow;
-    const int col = (idx % G::kChunksPerRow) * 8;
-    const int j = j0 + trow;
-    bf16x8 kv = bf16x8{}, vv = bf16x8{};
+  for (int k = 0; k < G::kLoads; ++k) {
+    const int inst = k * G::kW + wave;                   // 1 KB LDS block of this instruction
+    const int chunk_lin = inst * 64 + lane;              // linear chunk index in the tile
+    const int row = chunk_lin / G::kChunksPerRow;
+    const int gchunk = (chunk_lin % G::kChunksPerRow) ^ pf_swz<D>(row);
+    const int j = j0 + row;
+    typedef __attribute__((address_space(3))) void lds_void;
+    lds_void *kdst = (lds_void *)(reinterpret_cast<uintptr_t>(klds + inst * 512));
+    lds_void *vdst = (lds_void *)(reinterpret_cast<uintptr_t>(vlds + inst * 512));
     if (j < u.lk) {
       const __bf16 *kp, *vp;
       if (bt_row) {
@@ -86,40 +127,64 @@ __device__ __forceinline__ void pf_load_tile(const PrefillArgs &a, const PfUnit 
         kp = static_cast<const __bf16 *>(a.k) + (u.kv_off + j) * a.k_stride_tok;
         vp = static_cast<const __bf16 *>(a.v) + (u.kv_off + j) * a.v_stride_tok;
       }
-      kv = load_bf16x8(kp + (int64_t)u.kvh * a.k_stride_head + col);
-      vv = load_bf16x8(vp + (int64_t)u.kvh * a.v_stride_head + col);
+      __builtin_amdgcn_global_load_lds(kp + (int64_t)u.kvh * a.k_stride_head + gchunk * 8, kdst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + (int64_t)u.kvh * a.v_stride_head + gchunk * 8, vdst, 16, 0, 0);
+    } else {
+      *reinterpret_cast<u32x4 *>(klds + chunk_lin * 8) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(vlds + chunk_lin * 8) = u32x4{0u, 0u, 0u, 0u};
     }
-    r.k[c] = kv;
-    r.v[c] = vv;
   }
 }
 
-template <int D>
-__device__ __forceinline__ void pf_store_tile(__bf16 *klds, __bf16 *vlds, int tid, const PfTileRegs<D> &r) {
+// Per-row-block softmax of one tile: (optional) mask, lazy max, P and sums.
+template <int D, bool MASK>
+__device__ __forceinline__ void pf_softmax(f32x16 (&sacc)[PfGeom<D>::kSub], int j0, int bound, int h, float c,
+                                           float &m, float &lsum, float &alpha, bf16x8 (&pop)[PfGeom<D>::kKK]) {
   using G = PfGeom<D>;
+  float mx = kNegInf;
 #pragma unroll
-  for (int c = 0; c < G::kChunks; ++c) {
-    const int idx = c * 64 * kPfWaves + tid;
-    const int off = (idx / G::kChunksPerRow) * G::kStride + (idx % G::kChunksPerRow) * 8;
-    store_bf16x8_lds(klds + off, r.k[c]);
-    store_bf16x8_lds(vlds + off, r.v[c]);
-  }
+  for (int s = 0; s < G::kSub; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (MASK) {
+        const int j = j0 + 32 * s + 8 * (i >> 2) + 4 * h + (i & 3);
+        sacc[s][i] = (j < bound) ? sacc[s][i] : kNegInf;
+      }
+      mx = fmaxf(mx, sacc[s][i]);
+    }
+  mx = half_max(mx) * c;
+  // keep the base unless the max rose by more than kRebase (or there was none)
+  const float m_new = (mx > m + kRebase) ? mx : m;
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  alpha = exp2_fast(m - m_use);        // 1 when the base is kept; 0 from -inf
+  m = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int s = 0; s < G::kSub; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pe = exp2_fast(__builtin_fmaf(sacc[s][i], c, -m_use));
+      pop[2 * s + (i >> 3)][i & 7] = to_bf16(pe);
+      psum += pe;
+    }
+  lsum = alpha * lsum + psum;
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * PfGeom<D>::kW, PfCfg<D>::WPE) void prefill_kernel(const PrefillArgs a) {
   using G = PfGeom<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[G::kLds / 2];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  constexpr int RB = G::kRB;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * 2 * G::kTileElems];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;           // lane half
-  const int r32 = lane & 31;         // this lane's row within the wave
+  const int r32 = lane & 31;         // this lane's row within each 32-row block
 
   // ---- which rows this workgroup owns ----
   const int group = a.num_q_heads / a.num_kv_heads;
-  const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
-  const int tq = kPfBlockRows / gh;                 // query tokens per workgroup
+  const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);   // heads per workgroup
+  const int blocks_per_head = G::kBlocks / gh;
+  const int tq = 32 * blocks_per_head;                               // query tokens per workgroup
   const int head_groups = a.num_q_heads / gh;
   int L = blockIdx.x;
   const int qt = L / (a.batch * head_groups);       // tile index counted from the request's end
@@ -127,7 +192,6 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PrefillArg
   const int hg = L % head_groups;
   PfUnit u;
   u.b = L / head_groups;
-  u.gh = gh;
   u.h0 = hg * gh;
   u.kvh = u.h0 / group;
   const int q_lo = a.cu_seqlens_q[u.b];
@@ -144,161 +208,183 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(const PrefillArg
   u.q_begin = max(0, u.q_end - tq);
   if (u.q_end <= 0) return;          // uniform: this request has fewer tiles
 
-  // ---- this wave's 32 rows: head h0 + w / (4/gh), tokens of block w % (4/gh) ----
-  const int waves_per_head = kPfWaves / gh;
-  const int head = u.h0 + wave / waves_per_head;
-  const int tok_base = u.q_end - tq + (wave % waves_per_head) * kPfRows;   // may be < 0 at the top
-  const int t = tok_base + r32;                                            // this lane's query row
-  const bool row_valid = t >= u.q_begin && t < u.q_end;
-  // keys row t sees: [0, bound)
-  int bound = u.lk;
-  if (a.causal) bound = min(u.lk, max(0, u.lk - u.lq + t + 1));
-  if (!row_valid) bound = 0;
-  // keys the workgroup must walk, and where this wave's masking starts
-  int kv_end = u.lk;
-  if (a.causal) kv_end = min(u.lk, max(0, u.lk - u.lq + u.q_end));
-  int wave_min = bound, wave_max = bound;
+  // ---- this wave's row blocks ----
+  int head[RB], t[RB], bound[RB];
+  bool row_valid[RB];
+  int wave_max = 0, valid_min = 0x7fffffff;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int blk = wave * RB + rb;
+    head[rb] = u.h0 + blk / blocks_per_head;
+    t[rb] = u.q_end - tq + (blk % blocks_per_head) * 32 + r32;      // may be < 0 at the top
+    row_valid[rb] = t[rb] >= u.q_begin && t[rb] < u.q_end;
+    bound[rb] = u.lk;
+    if (a.causal) bound[rb] = min(u.lk, max(0, u.lk - u.lq + t[rb] + 1));
+    if (!row_valid[rb]) bound[rb] = 0;
+    wave_max = max(wave_max, bound[rb]);
+    if (row_valid[rb]) valid_min = min(valid_min, bound[rb]);
+  }
+  // Keys the wave's rows see, and the first key some valid row must mask;
+  // made scalar so the per-tile tests are branches, not per-lane selects.
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    wave_min = min(wave_min, __shfl_xor(wave_min, off, 64));
     wave_max = max(wave_max, __shfl_xor(wave_max, off, 64));
+    valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
   }
-  // lanes of invalid rows pull wave_min to 0; mask from the smallest valid bound instead
-  int valid_min = row_valid ? bound : 0x7fffffff;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
-  (void)wave_min;
+  wave_max = __builtin_amdgcn_readfirstlane(wave_max);
+  valid_min = __builtin_amdgcn_readfirstlane(valid_min);
+  int kv_end = u.lk;                                    // keys the workgroup walks
+  if (a.causal) kv_end = min(u.lk, max(0, u.lk - u.lq + u.q_end));
 
-  // ---- Q^T operand: lane holds Q[row t][16kb + 8h .. +8] ----
-  bf16x8 qop[G::kKB];
+  // ---- Q^T operands: lane holds Q[row t][16kb + 8h .. +8]; a negative scale
+  //      is carried by negating Q (exact in bf16) so c > 0 ----
+  const float c = fabsf(a.scale_log2);
+  const u32x4 qsign = (a.scale_log2 < 0.f) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u} : u32x4{};
+  bf16x8 qop[RB][G::kKB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (u.q_off + t[rb]) * a.q_stride_tok +
+                         (int64_t)head[rb] * a.q_stride_head;
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+      qop[rb][kb] = row_valid[rb] ? __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + h * 8)) ^ qsign)
+                                  : bf16x8{};
+  }
+
+  // Loop-invariant LDS byte offsets of this lane's operand chunks (the
+  // swizzle of a row depends only on its index modulo 16).
+  int koff[G::kKB];
   {
-    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (u.q_off + t) * a.q_stride_tok + (int64_t)head * a.q_stride_head;
+    const int hf = h ^ pf_swz<D>(r32);
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) qop[kb] = row_valid ? load_bf16x8(qrow + kb * 16 + h * 8) : bf16x8{};
+    for (int kb = 0; kb < G::kKB; ++kb) koff[kb] = r32 * D * 2 + ((2 * kb) ^ hf) * 16;
+  }
+  const int s16 = lane & 15;
+  int voff[2][G::kNB];
+  {
+    const int row0 = 4 * h + (s16 >> 2);
+    const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    const int f0 = pf_swz<D>(row0), f1 = pf_swz<D>(row0 + 8);
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) {
+      voff[0][nb] = row0 * D * 2 + ((4 * nb + cb) ^ f0) * 16 + 8 * (s16 & 1);
+      voff[1][nb] = (row0 + 8) * D * 2 + ((4 * nb + cb) ^ f1) * 16 + 8 * (s16 & 1);
+    }
   }
 
-  float m = kNegInf, lsum = 0.f, lexact = 0.f;
-  f32x16 oacc[G::kNB];
+  float m[RB], lsum[RB];
+  f32x16 oacc[RB][G::kNB];
 #pragma unroll
-  for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x16{};
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    lsum[rb] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) oacc[rb][nb] = f32x16{};
+  }
 
   const int ntiles = (kv_end + G::kN - 1) / G::kN;
-  PfTileRegs<D> regs;
-  if (ntiles > 0) {
-    pf_load_tile<D>(a, u, 0, tid, regs);
-    pf_store_tile<D>(lds, lds + G::kTileElems, tid, regs);
-  }
+  if (ntiles > 0) pf_issue_tile<D>(a, u, 0, wave, lane, lds, lds + G::kTileElems);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = it * G::kN;
-    const __bf16 *klds = lds + (it & 1) * 2 * G::kTileElems;
-    const __bf16 *vlds = klds + G::kTileElems;
-    const bool more = it + 1 < ntiles;
-    if (more) pf_load_tile<D>(a, u, j0 + G::kN, tid, regs);
+    const char *kbytes = reinterpret_cast<const char *>(lds + (it & 1) * 2 * G::kTileElems);
+    const char *vbytes = kbytes + G::kTileElems * 2;
+    // The other buffer was last read in iteration it-1, which every wave
+    // finished before the barrier that ended it: load the next tile into it.
+    if (it + 1 < ntiles) {
+      __bf16 *knext = lds + ((it + 1) & 1) * 2 * G::kTileElems;
+      pf_issue_tile<D>(a, u, j0 + G::kN, wave, lane, knext, knext + G::kTileElems);
+    }
 
     if (j0 < wave_max) {
-      // ---- S^T = K Q^T, kSub sub-tiles of 32 keys ----
-      f32x16 sacc[G::kSub];
+      // ---- S^T = K Q^T: each K operand feeds every row block ----
+      f32x16 sacc[RB][G::kSub];
 #pragma unroll
       for (int s = 0; s < G::kSub; ++s) {
-        sacc[s] = f32x16{};
-        const __bf16 *krow = klds + (32 * s + r32) * G::kStride + h * 8;
+        bf16x8 kop[G::kKB];
 #pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(krow + kb * 16);
-          sacc[s] = mfma32x32x16(kop, qop[kb], sacc[s]);
+        for (int kb = 0; kb < G::kKB; ++kb)
+          kop[kb] = *reinterpret_cast<const bf16x8 *>(kbytes + koff[kb] + s * 32 * D * 2);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          sacc[rb][s] = f32x16{};
+#pragma unroll
+          for (int kb = 0; kb < G::kKB; ++kb) sacc[rb][s] = mfma32x32x16(kop[kb], qop[rb][kb], sacc[rb][s]);
         }
       }
-      // ---- scale, mask, online softmax (row r32 lives in this lane) ----
-      const bool need_mask = j0 + G::kN > valid_min;
-      float mx = kNegInf;
+      // ---- softmax (row r32 of each block lives in this lane) ----
+      bf16x8 pop[RB][G::kKK];
+      float alpha[RB];
+      if (j0 + G::kN > valid_min) {
 #pragma unroll
-      for (int s = 0; s < G::kSub; ++s)
+        for (int rb = 0; rb < RB; ++rb)
+          pf_softmax<D, true>(sacc[rb], j0, bound[rb], h, c, m[rb], lsum[rb], alpha[rb], pop[rb]);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = sacc[s][i] * a.scale_log2;
-          if (need_mask) {
-            const int j = j0 + 32 * s + 8 * (i >> 2) + 4 * h + (i & 3);
-            x = (j < bound) ? x : kNegInf;
-          }
-          sacc[s][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      m = m_new;
-      // P^T operand per 16-key block kk: slots e = keys 16kk + 8(e/4) + 4h + e%4
-      bf16x8 pop[G::kN / 16];
-      float psum = 0.f, pexact = 0.f;
+        for (int rb = 0; rb < RB; ++rb)
+          pf_softmax<D, false>(sacc[rb], j0, bound[rb], h, c, m[rb], lsum[rb], alpha[rb], pop[rb]);
+      }
+      bool rebase = false;
 #pragma unroll
-      for (int s = 0; s < G::kSub; ++s)
+      for (int rb = 0; rb < RB; ++rb) rebase |= alpha[rb] != 1.f;
+      if (__ballot(rebase)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pe = exp2_fast(sacc[s][i] - m_use);
-          const __bf16 pb = to_bf16(pe);
-          pop[2 * s + (i >> 3)][i & 7] = pb;
-          psum += bf16_to_f32(pb);
-          pexact += pe;
-        }
-      lsum = alpha * lsum + psum;
-      lexact = alpha * lexact + pexact;
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] *= alpha;
-      // ---- O^T += V^T P^T ----
-      const int s16 = lane & 15;
-      const int b16 = (lane >> 4) & 1;
+          for (int nb = 0; nb < G::kNB; ++nb) oacc[rb][nb] *= alpha[rb];
+      }
+      // ---- O^T += V^T P^T: each V^T operand feeds every row block ----
 #pragma unroll
-      for (int kk = 0; kk < G::kN / 16; ++kk) {
-        const __bf16 *v0 = vlds + (16 * kk + 4 * h + (s16 >> 2)) * G::kStride + 16 * b16 + 4 * (s16 & 3);
-        const __bf16 *v1 = v0 + 8 * G::kStride;
+      for (int kk = 0; kk < G::kKK; ++kk) {
 #pragma unroll
         for (int nb = 0; nb < G::kNB; ++nb) {
-          const bf16x4 lo = lds_read_tr16(v0 + 32 * nb);
-          const bf16x4 hi = lds_read_tr16(v1 + 32 * nb);
-          oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
+          const bf16x4 lo = lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2);
+          const bf16x4 hi = lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2);
+          const bf16x8 vop = concat(lo, hi);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) oacc[rb][nb] = mfma32x32x16(vop, pop[rb][kk], oacc[rb][nb]);
         }
       }
     }
 
-    if (more) {
-      __bf16 *knext = lds + ((it + 1) & 1) * 2 * G::kTileElems;
-      pf_store_tile<D>(knext, knext + G::kTileElems, tid, regs);
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of the next tile landed
     __syncthreads();
   }
 
-  // ---- epilogue: O / l -> bf16; LSE2 = m + log2(l_exact) ----
-  lsum += __shfl_xor(lsum, 32, 64);
-  lexact += __shfl_xor(lexact, 32, 64);
-  if (!row_valid) return;
-  const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-  __bf16 *orow = static_cast<__bf16 *>(a.o) + (u.q_off + t) * a.o_stride_tok + (int64_t)head * a.o_stride_head;
+  // ---- epilogue: O / l -> bf16; LSE2 = m + log2(l) ----
 #pragma unroll
-  for (int nb = 0; nb < G::kNB; ++nb)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l = half_sum(lsum[rb]);
+    if (!row_valid[rb]) continue;
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    __bf16 *orow = static_cast<__bf16 *>(a.o) + (u.q_off + t[rb]) * a.o_stride_tok + (int64_t)head[rb] * a.o_stride_head;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 ob;
+    for (int nb = 0; nb < G::kNB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[nb][4 * g + i] * inv);
-      *reinterpret_cast<u32x2 *>(orow + 32 * nb + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, ob);
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ob;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[rb][nb][4 * g + i] * inv);
+        *reinterpret_cast<u32x2 *>(orow + 32 * nb + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, ob);
+      }
+    if (a.lse && h == 0) {
+      const float muse = (m[rb] == kNegInf) ? 0.f : m[rb];
+      a.lse[(u.q_off + t[rb]) * a.num_q_heads + head[rb]] = (l > 0.f) ? muse + __log2f(l) : kNegInf;
     }
-  if (a.lse && h == 0) {
-    const float muse = (m == kNegInf) ? 0.f : m;
-    a.lse[(u.q_off + t) * a.num_q_heads + head] = (lexact > 0.f) ? muse + __log2f(lexact) : kNegInf;
   }
 }
 
 template <int D>
 hipError_t launch_pf(const PrefillArgs &a, hipStream_t stream) {
+  using G = PfGeom<D>;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
-  const int tq = kPfBlockRows / gh;
+  const int tq = 32 * G::kBlocks / gh;
   const int64_t q_tiles = (a.max_seqlen_q + tq - 1) / tq;
   const int64_t blocks = q_tiles * a.batch * (a.num_q_heads / gh);
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)blocks), dim3(64 * kPfWaves), 0, stream, a);
+  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)blocks), dim3(64 * G::kW), 0, stream, a);
   return hipGetLastError();
 }
 
