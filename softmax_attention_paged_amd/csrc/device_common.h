@@ -72,6 +72,27 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Direct HBM -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's bytes land at LDS byte address lds_base + 16 i; lds_base must be
+// wave-uniform. Written as inline assembly so that the compiler, which
+// cannot tell which LDS bytes the transfer writes, does not make later
+// unrelated LDS reads wait for it: the caller waits (s_waitcnt vmcnt) and
+// synchronises the workgroup before reading the destination.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
+}
+
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane byte
+// offset (the saddr form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void lds_dma16(const void *base, uint32_t lane_off, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(base), "{m0}"(lds_base) : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 template <class T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);

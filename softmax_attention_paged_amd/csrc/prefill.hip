@@ -11,14 +11,13 @@
 // head: GH query heads of a GQA group (GH in {1, 2, 4}) times consecutive
 // query tokens. Each 32-row block is 32 tokens of one head. Per key tile:
 //   - the tile's K and V rows are gathered (through the block table when
-//     paged, "Writing Page Attention with PyPTO", section 5.2) one tile ahead
-//     with direct HBM -> LDS loads (global_load_lds_dwordx4) into a double
-//     buffer whose 16-byte chunks are XOR-swizzled against bank conflicts;
+//     paged, "Writing Page Attention with PyPTO", section 5.2) ahead of use
+//     with direct HBM -> LDS loads (global_load_lds_dwordx4) into double
+//     buffers whose 16-byte chunks are XOR-swizzled against bank conflicts;
 //     keys past the request are zeroed, table entries past its last page are
 //     never read (section 9);
 //   - S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q^T in registers: each lane
-//     holds 16 scores of one row per 32 keys. Every K operand read from LDS
-//     feeds the RB row blocks of the wave;
+//     holds 16 scores of one row per 32 keys;
 //   - masking (tail, and above the bottom-right causal diagonal) only on the
 //     tiles that reach a row bound, decided once per tile for the wave;
 //   - the row max is kept lazily: a row re-bases (and rescales O) only when
@@ -28,11 +27,16 @@
 //     skips the rescale when the max barely moves). The result is the same
 //     softmax, the final division uses the same base;
 //   - P rounded to bf16 (RNE) is the B operand of O^T += V^T P^T straight
-//     from the score registers; V^T comes from LDS via ds_read_b64_tr_b16
-//     and each V^T operand feeds all RB row blocks.
+//     from the score registers; V^T comes from LDS via ds_read_b64_tr_b16.
 // The FP32 P sums normalise O and give the LSE. Query tiles are aligned to
 // the END of each request, so tile 0 of every request sees the most keys and
 // is launched first.
+//
+// Two kernels: for D in {64, 128} a software-pipelined one (scores of tile
+// j+1 on the matrix cores beside the softmax of tile j, separate K and V
+// double buffers, see prefill_pipe_kernel); for D = 256 a plain one with
+// 32-key tiles at one wave per SIMD (its Q operand and O accumulator fill
+// a SIMD's registers).
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -46,8 +50,6 @@ namespace {
 // extra accumulators spill into AGPR traffic); D = 256 needs a whole SIMD's
 // registers for its Q operand and O accumulator.
 template <int D> struct PfCfg;
-template <> struct PfCfg<64> { static constexpr int W = 4, RB = 1, N = 64, WPE = 2; };
-template <> struct PfCfg<128> { static constexpr int W = 4, RB = 1, N = 64, WPE = 2; };
 template <> struct PfCfg<256> { static constexpr int W = 4, RB = 1, N = 32, WPE = 1; };
 
 template <int D>
@@ -90,11 +92,47 @@ __device__ __forceinline__ float half_sum(float x) {
 
 struct PfUnit {
   int b, kvh, h0;              // request, KV head, first query head of the workgroup
+  int gh, tq;                  // query heads and query tokens per workgroup
   int q_begin, q_end;          // query rows of the request covered by this workgroup (relative)
   int lq, lk;                  // request lengths
   int64_t q_off;               // first query token of the request in the packed Q
   int64_t kv_off;              // dense: first key of the request in packed K/V
 };
+
+// Heads per workgroup for a GQA group: the largest of 4, 2, 1 dividing it.
+__host__ __device__ __forceinline__ int pf_heads_per_wg(int group) {
+  return (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
+// The rows workgroup blockIdx.x owns when it holds `blocks` 32-row blocks:
+// gh heads of one KV group times tq = 32 blocks / gh tokens, tiles counted
+// from the end of the request (index slowest, so the longest rows of every
+// request start first). False when the request has no tile of that index.
+__device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit &u) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  u.gh = pf_heads_per_wg(group);
+  u.tq = 32 * (blocks / u.gh);
+  const int head_groups = a.num_q_heads / u.gh;
+  int L = blockIdx.x;
+  const int qt = L / (a.batch * head_groups);
+  L %= a.batch * head_groups;
+  u.b = L / head_groups;
+  u.h0 = (L % head_groups) * u.gh;
+  u.kvh = u.h0 / group;
+  const int q_lo = a.cu_seqlens_q[u.b];
+  u.lq = a.cu_seqlens_q[u.b + 1] - q_lo;
+  u.q_off = q_lo;
+  if (a.block_table) {
+    u.lk = a.seq_lens_kv[u.b];
+    u.kv_off = 0;
+  } else {
+    u.kv_off = a.cu_seqlens_kv[u.b];
+    u.lk = a.cu_seqlens_kv[u.b + 1] - (int)u.kv_off;
+  }
+  u.q_end = u.lq - qt * u.tq;
+  u.q_begin = max(0, u.q_end - u.tq);
+  return u.q_end > 0;
+}
 
 // Issue the direct HBM -> LDS loads of one K and one V tile (16 bytes per
 // lane, lane i of a wave instruction lands at 16 i bytes past the
@@ -181,32 +219,10 @@ __global__ __launch_bounds__(64 * PfGeom<D>::kW, PfCfg<D>::WPE) void prefill_ker
   const int r32 = lane & 31;         // this lane's row within each 32-row block
 
   // ---- which rows this workgroup owns ----
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);   // heads per workgroup
-  const int blocks_per_head = G::kBlocks / gh;
-  const int tq = 32 * blocks_per_head;                               // query tokens per workgroup
-  const int head_groups = a.num_q_heads / gh;
-  int L = blockIdx.x;
-  const int qt = L / (a.batch * head_groups);       // tile index counted from the request's end
-  L %= a.batch * head_groups;
-  const int hg = L % head_groups;
   PfUnit u;
-  u.b = L / head_groups;
-  u.h0 = hg * gh;
-  u.kvh = u.h0 / group;
-  const int q_lo = a.cu_seqlens_q[u.b];
-  u.lq = a.cu_seqlens_q[u.b + 1] - q_lo;
-  u.q_off = q_lo;
-  if (a.block_table) {
-    u.lk = a.seq_lens_kv[u.b];
-    u.kv_off = 0;
-  } else {
-    u.kv_off = a.cu_seqlens_kv[u.b];
-    u.lk = a.cu_seqlens_kv[u.b + 1] - (int)u.kv_off;
-  }
-  u.q_end = u.lq - qt * tq;
-  u.q_begin = max(0, u.q_end - tq);
-  if (u.q_end <= 0) return;          // uniform: this request has fewer tiles
+  if (!pf_unit(a, G::kBlocks, u)) return;          // uniform: this request has fewer tiles
+  const int blocks_per_head = G::kBlocks / u.gh;
+  const int tq = u.tq;
 
   // ---- this wave's row blocks ----
   int head[RB], t[RB], bound[RB];
@@ -376,11 +392,374 @@ __global__ __launch_bounds__(64 * PfGeom<D>::kW, PfCfg<D>::WPE) void prefill_ker
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined kernel for D in {64, 128}: four waves, one 32-row block
+// per wave, 64-key tiles. Inside a wave the scores of tile j+1 are computed
+// on the matrix cores while the vector units turn the scores of tile j into
+// P, so neither unit waits for the other to drain. K and V have their own
+// double buffers, which lets K(j+1) be resident one iteration before V(j+1):
+//
+//   iteration j:  wait + barrier | load K(j+2), V(j+1) | finish max S(j),
+//                 re-base | S(j+1) = K(j+1) Q^T with P(j) = exp2(..) beside it |
+//                 O^T += V(j)^T P(j)^T with the max over S(j+1) beside it
+//
+// The max over S(j+1) is taken unmasked; a tile that needs a mask masks and
+// takes it again. Paged block-table entries are fetched one tile ahead of
+// the loads that use them, so no load waits on a table read.
+
+template <int D>
+struct PpGeom {
+  static constexpr int kW = 4;                         // waves per workgroup
+  static constexpr int kN = 64;                        // keys per tile
+  static constexpr int kKB = D / 16;                   // QK k-steps
+  static constexpr int kNB = D / 32;                   // PV 32-channel blocks
+  static constexpr int kKK = kN / 16;                  // PV k-steps
+  static constexpr int kTile = kN * D;                 // elements of one K or V tile
+  static constexpr int kCPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int kLoads = kN * kCPR / 64 / kW;   // 1 KB direct loads per wave per tile
+};
+
+// How K/V rows are addressed: dense, paged with pages of at least one tile
+// (a tile then lies inside one page), or paged with smaller pages.
+enum PpKv { kKvDense = 0, kKvWidePages = 1, kKvNarrowPages = 2 };
+
+// Tile row that load k of this lane fills.
+template <int D>
+__device__ __forceinline__ int pp_row(int k, int wave, int lane) {
+  using G = PpGeom<D>;
+  return ((k * G::kW + wave) * 64 + lane) / G::kCPR;
+}
+
+// This lane's byte offset inside the rows one load instruction covers. It
+// is the same for every instruction of a wave: instructions start a
+// multiple of 16 rows apart and the swizzle depends on the row modulo 16.
+template <int D>
+__device__ __forceinline__ uint32_t pp_lane_off(int wave, int lane, int64_t stride_tok) {
+  using G = PpGeom<D>;
+  const int r = lane / G::kCPR;
+  const int gchunk = (lane % G::kCPR) ^ pf_swz<D>(wave * (64 / G::kCPR) + r);
+  return static_cast<uint32_t>((r * stride_tok + gchunk * 8) * 2);
+}
+
+// Loads of a tile that lies wholly inside the request (and, paged, inside
+// one page): `tile` is its first row, wave-uniform.
+template <int D>
+__device__ __forceinline__ void pp_issue_whole(const __bf16 *tile, int64_t stride_tok, uint32_t lane_off, int wave,
+                                               uint32_t lds_dst) {
+  using G = PpGeom<D>;
+  constexpr int kRows = 64 / G::kCPR;    // rows per load instruction
+#pragma unroll
+  for (int k = 0; k < G::kLoads; ++k) {
+    const int inst = k * G::kW + wave;
+    lds_dma16(tile + (int64_t)inst * kRows * stride_tok, lane_off, lds_dst + inst * 1024);
+  }
+}
+
+// Loads of a tile row by row: rows at or past the request's end are
+// zero-filled with LDS stores instead, and each row finds its page itself
+// (`page` for wide pages, `pid[k]` for narrow ones).
+template <int D, int KV>
+__device__ __forceinline__ void pp_issue_rows(const __bf16 *src, int64_t stride_page, int64_t stride_tok, int page,
+                                              const int (&pid)[PpGeom<D>::kLoads], int j0, int lk, int pmask,
+                                              int wave, int lane, __bf16 *dst) {
+  using G = PpGeom<D>;
+#pragma unroll
+  for (int k = 0; k < G::kLoads; ++k) {
+    const int inst = k * G::kW + wave;
+    const int chunk_lin = inst * 64 + lane;
+    const int row = chunk_lin / G::kCPR;
+    const int gchunk = (chunk_lin % G::kCPR) ^ pf_swz<D>(row);
+    const int j = j0 + row;
+    if (j < lk) {
+      const int64_t pg = (KV == kKvWidePages) ? page : (KV == kKvNarrowPages ? pid[k] : 0);
+      const __bf16 *p = (KV == kKvDense) ? src + (int64_t)j * stride_tok
+                                         : src + pg * stride_page + (int64_t)(j & pmask) * stride_tok;
+      lds_dma16(p + gchunk * 8, lds_address(dst + inst * 512));
+    } else {
+      *reinterpret_cast<u32x4 *>(dst + chunk_lin * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// One K or V tile: `src` is the request's first key (dense) or page 0
+// (paged) of the workgroup's KV head.
+template <int D, int KV>
+__device__ __forceinline__ void pp_issue(const __bf16 *src, int64_t stride_page, int64_t stride_tok, uint32_t lane_off,
+                                         int page, const int (&pid)[PpGeom<D>::kLoads], int j0, int lk, int pmask,
+                                         int wave, int lane, __bf16 *dst) {
+  if (KV != kKvNarrowPages && j0 + PpGeom<D>::kN <= lk) {
+    const __bf16 *tile = (KV == kKvDense) ? src + (int64_t)j0 * stride_tok
+                                          : src + (int64_t)page * stride_page + (int64_t)(j0 & pmask) * stride_tok;
+    pp_issue_whole<D>(tile, stride_tok, lane_off, wave, lds_address(dst));
+  } else {
+    pp_issue_rows<D, KV>(src, stride_page, stride_tok, page, pid, j0, lk, pmask, wave, lane, dst);
+  }
+}
+
+// Block-table entries for the tile at key j0 (never past the request's last
+// page): one wave-uniform entry for wide pages, one per loaded row otherwise.
+template <int D, int KV>
+__device__ __forceinline__ void pp_fetch_pages(const int32_t *bt_row, int j0, int lk, int shift, int wave, int lane,
+                                               int &page, int (&pid)[PpGeom<D>::kLoads]) {
+  if constexpr (KV == kKvWidePages) {
+    // a scalar load (the table is read-only here): waiting for it does not
+    // wait for the vector-memory tile loads in flight
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    page = (j0 < lk) ? reinterpret_cast<const_i32 *>(reinterpret_cast<uintptr_t>(bt_row))[j0 >> shift] : 0;
+  } else if constexpr (KV == kKvNarrowPages) {
+#pragma unroll
+    for (int k = 0; k < PpGeom<D>::kLoads; ++k) {
+      const int j = j0 + pp_row<D>(k, wave, lane);
+      pid[k] = (j < lk) ? bt_row[j >> shift] : 0;
+    }
+  }
+}
+
+// S^T for the 64 keys of a resident K tile: two 32-key blocks, 16 scores of
+// this lane's row each.
+template <int D>
+__device__ __forceinline__ void pp_scores(const char *kbytes, const int (&koff)[PpGeom<D>::kKB],
+                                          const bf16x8 (&qop)[PpGeom<D>::kKB], f32x16 (&s)[2]) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    s[sub] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < PpGeom<D>::kKB; ++kb)
+      s[sub] = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(kbytes + koff[kb] + sub * 32 * D * 2), qop[kb], s[sub]);
+  }
+}
+
+__device__ __forceinline__ float pp_max(const f32x16 (&s)[2]) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sub][i]);
+  return mx;
+}
+
+// Keys at or past `bound` (this lane's row) get -inf.
+__device__ __forceinline__ void pp_mask(f32x16 (&s)[2], int j0, int bound, int h) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = j0 + 32 * sub + 8 * (i >> 2) + 4 * h + (i & 3);
+      s[sub][i] = (j < bound) ? s[sub][i] : kNegInf;
+    }
+}
+
+// One tile's P, sum and O update, and the scores (with their unmasked max)
+// of the following tile from the K tile in `knext`.
+template <int D>
+__device__ __forceinline__ void pp_step(f32x16 (&s)[2], float &mx, float m_use, float c, float alpha, float &lsum,
+                                        f32x16 (&oacc)[PpGeom<D>::kNB], const char *knext, const char *vbytes,
+                                        const int (&koff)[PpGeom<D>::kKB], const int (&voff)[2][PpGeom<D>::kNB],
+                                        const bf16x8 (&qop)[PpGeom<D>::kKB]) {
+  using G = PpGeom<D>;
+  f32x16 sn[2];
+  pp_scores<D>(knext, koff, qop, sn);
+  bf16x8 pop[G::kKK];
+  float ps[2] = {0.f, 0.f};
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pe = exp2_fast(__builtin_fmaf(s[sub][i], c, -m_use));
+      pop[2 * sub + (i >> 3)][i & 7] = to_bf16(pe);
+      ps[i & 1] += pe;
+    }
+#pragma unroll
+  for (int kk = 0; kk < G::kKK; ++kk)
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) {
+      const bf16x4 lo = lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2);
+      const bf16x4 hi = lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2);
+      oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
+    }
+  lsum = alpha * lsum + (ps[0] + ps[1]);
+  s[0] = sn[0];
+  s[1] = sn[1];
+  mx = pp_max(s);
+}
+
+template <int D, int KV>
+__global__ __launch_bounds__(64 * PpGeom<D>::kW, 2) void prefill_pipe_kernel(const PrefillArgs a) {
+  using G = PpGeom<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[4 * G::kTile];   // K slot 0, K slot 1, V slot 0, V slot 1
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  PfUnit u;
+  if (!pf_unit(a, G::kW, u)) return;
+  const int blocks_per_head = G::kW / u.gh;
+  const int head = u.h0 + wave / blocks_per_head;
+  const int t = u.q_end - u.tq + (wave % blocks_per_head) * 32 + r32;   // may be < 0 at the top
+  const bool row_valid = t >= u.q_begin && t < u.q_end;
+  int bound = a.causal ? min(u.lk, max(0, u.lk - u.lq + t + 1)) : u.lk;
+  if (!row_valid) bound = 0;
+  int wave_max = bound, valid_min = row_valid ? bound : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    wave_max = max(wave_max, __shfl_xor(wave_max, off, 64));
+    valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
+  }
+  wave_max = __builtin_amdgcn_readfirstlane(wave_max);
+  valid_min = __builtin_amdgcn_readfirstlane(valid_min);
+  const int kv_end = a.causal ? min(u.lk, max(0, u.lk - u.lq + u.q_end)) : u.lk;
+  const int nt = (kv_end + G::kN - 1) / G::kN;        // tiles the workgroup loads
+  const int ntw = (wave_max + G::kN - 1) / G::kN;     // tiles this wave computes (ntw <= nt)
+
+  // Q^T operands (a negative scale negates Q, exact in bf16, so c > 0)
+  const float c = fabsf(a.scale_log2);
+  const u32x4 qsign = (a.scale_log2 < 0.f) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u} : u32x4{};
+  bf16x8 qop[G::kKB];
+  {
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (u.q_off + t) * a.q_stride_tok +
+                         (int64_t)head * a.q_stride_head;
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+      qop[kb] = row_valid ? __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + h * 8)) ^ qsign)
+                          : bf16x8{};
+  }
+  int koff[G::kKB];
+  {
+    const int hf = h ^ pf_swz<D>(r32);
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb) koff[kb] = r32 * D * 2 + ((2 * kb) ^ hf) * 16;
+  }
+  int voff[2][G::kNB];
+  {
+    const int s16 = lane & 15;
+    const int row0 = 4 * h + (s16 >> 2);
+    const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    const int f0 = pf_swz<D>(row0), f1 = pf_swz<D>(row0 + 8);
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) {
+      voff[0][nb] = row0 * D * 2 + ((4 * nb + cb) ^ f0) * 16 + 8 * (s16 & 1);
+      voff[1][nb] = (row0 + 8) * D * 2 + ((4 * nb + cb) ^ f1) * 16 + 8 * (s16 & 1);
+    }
+  }
+
+  // KV sources of the workgroup's head
+  const __bf16 *ksrc = static_cast<const __bf16 *>(a.k) + (int64_t)u.kvh * a.k_stride_head;
+  const __bf16 *vsrc = static_cast<const __bf16 *>(a.v) + (int64_t)u.kvh * a.v_stride_head;
+  if constexpr (KV == kKvDense) {
+    ksrc += u.kv_off * a.k_stride_tok;
+    vsrc += u.kv_off * a.v_stride_tok;
+  }
+  const uint32_t koff_g = pp_lane_off<D>(wave, lane, a.k_stride_tok);
+  const uint32_t voff_g = pp_lane_off<D>(wave, lane, a.v_stride_tok);
+  const int32_t *bt_row = (KV != kKvDense) ? a.block_table + (int64_t)u.b * a.block_table_stride : nullptr;
+  const int pmask = (1 << a.page_shift) - 1;
+  // Table entries of the next K tile (it+2) and V tile (it+1) to load, each
+  // fetched into its own registers one iteration before use.
+  int kpage = 0, vpage = 0;
+  int kpid[G::kLoads] = {}, vpid[G::kLoads] = {};
+  auto issue_k = [&](int j0t, int page, const int (&pid)[G::kLoads], __bf16 *dst) {
+    pp_issue<D, KV>(ksrc, a.k_stride_page, a.k_stride_tok, koff_g, page, pid, j0t, u.lk, pmask, wave, lane, dst);
+  };
+  auto issue_v = [&](int j0t, int page, const int (&pid)[G::kLoads], __bf16 *dst) {
+    pp_issue<D, KV>(vsrc, a.v_stride_page, a.v_stride_tok, voff_g, page, pid, j0t, u.lk, pmask, wave, lane, dst);
+  };
+
+  auto kslot = [&](int par) { return lds + par * G::kTile; };
+  auto vslot = [&](int par) { return lds + (2 + par) * G::kTile; };
+  if (nt > 0) {
+    pp_fetch_pages<D, KV>(bt_row, 0, u.lk, a.page_shift, wave, lane, kpage, kpid);
+    issue_k(0, kpage, kpid, kslot(0));
+    issue_v(0, kpage, kpid, vslot(0));
+    pp_fetch_pages<D, KV>(bt_row, G::kN, u.lk, a.page_shift, wave, lane, vpage, vpid);
+    if (nt > 1) issue_k(G::kN, vpage, vpid, kslot(1));
+    pp_fetch_pages<D, KV>(bt_row, 2 * G::kN, u.lk, a.page_shift, wave, lane, kpage, kpid);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  f32x16 s[2];
+  float mx = kNegInf;
+  if (ntw > 0) {
+    pp_scores<D>(reinterpret_cast<const char *>(kslot(0)), koff, qop, s);
+    mx = pp_max(s);
+  }
+  float m = kNegInf, lsum = 0.f;
+  f32x16 oacc[G::kNB];
+#pragma unroll
+  for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x16{};
+
+  for (int it = 0; it < nt; ++it) {
+    // K(it+1) and V(it) have landed for every wave, and every wave is done
+    // with K(it) and V(it-1), whose slots take K(it+2) and V(it+1).
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int j0 = it * G::kN;
+    const int par = it & 1;
+    if (it + 2 < nt) issue_k(j0 + 2 * G::kN, kpage, kpid, kslot(par));
+    if (it + 1 < nt) issue_v(j0 + G::kN, vpage, vpid, vslot(par ^ 1));
+    if constexpr (KV != kKvDense) {
+      if (it + 2 < nt) pp_fetch_pages<D, KV>(bt_row, j0 + 2 * G::kN, u.lk, a.page_shift, wave, lane, vpage, vpid);
+      if (it + 3 < nt) pp_fetch_pages<D, KV>(bt_row, j0 + 3 * G::kN, u.lk, a.page_shift, wave, lane, kpage, kpid);
+    }
+    if (it < ntw) {
+      if (j0 + G::kN > valid_min) {
+        pp_mask(s, j0, bound, h);
+        mx = pp_max(s);
+      }
+      const float mt = half_max(mx) * c;
+      const float m_new = (mt > m + kRebase) ? mt : m;    // keep the base unless the max rose by > kRebase
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2_fast(m - m_use);          // 1 when kept; 0 from -inf
+      m = m_new;
+      if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] *= alpha;
+      }
+      const char *knext = reinterpret_cast<const char *>(kslot(par ^ 1));
+      const char *vbytes = reinterpret_cast<const char *>(vslot(par));
+      // The scores of tile it+1 are computed even on the wave's last tile
+      // (from whatever that LDS slot holds) and then dropped: one branch-free
+      // body keeps the exp work beside the MFMAs.
+      pp_step<D>(s, mx, m_use, c, alpha, lsum, oacc, knext, vbytes, koff, voff, qop);
+    }
+  }
+
+  // ---- epilogue: O / l -> bf16; LSE2 = m + log2(l) ----
+  const float l = half_sum(lsum);
+  if (!row_valid) return;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  __bf16 *orow = static_cast<__bf16 *>(a.o) + (u.q_off + t) * a.o_stride_tok + (int64_t)head * a.o_stride_head;
+#pragma unroll
+  for (int nb = 0; nb < G::kNB; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[nb][4 * g + i] * inv);
+      *reinterpret_cast<u32x2 *>(orow + 32 * nb + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, ob);
+    }
+  if (a.lse && h == 0) {
+    const float muse = (m == kNegInf) ? 0.f : m;
+    a.lse[(u.q_off + t) * a.num_q_heads + head] = (l > 0.f) ? muse + __log2f(l) : kNegInf;
+  }
+}
+
+template <int D, int KV>
+hipError_t launch_pp(const PrefillArgs &a, hipStream_t stream) {
+  using G = PpGeom<D>;
+  const int gh = pf_heads_per_wg(a.num_q_heads / a.num_kv_heads);
+  const int tq = 32 * G::kW / gh;
+  const int64_t q_tiles = (a.max_seqlen_q + tq - 1) / tq;
+  const int64_t blocks = q_tiles * a.batch * (a.num_q_heads / gh);
+  hipLaunchKernelGGL((prefill_pipe_kernel<D, KV>), dim3((unsigned)blocks), dim3(64 * G::kW), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_pf(const PrefillArgs &a, hipStream_t stream) {
   using G = PfGeom<D>;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
+  const int gh = pf_heads_per_wg(a.num_q_heads / a.num_kv_heads);
   const int tq = 32 * G::kBlocks / gh;
   const int64_t q_tiles = (a.max_seqlen_q + tq - 1) / tq;
   const int64_t blocks = q_tiles * a.batch * (a.num_q_heads / gh);
@@ -388,12 +767,19 @@ hipError_t launch_pf(const PrefillArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_pp_kv(const PrefillArgs &a, hipStream_t stream) {
+  if (!a.block_table) return launch_pp<D, kKvDense>(a, stream);
+  if ((1 << a.page_shift) >= PpGeom<D>::kN) return launch_pp<D, kKvWidePages>(a, stream);
+  return launch_pp<D, kKvNarrowPages>(a, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: return launch_pf<64>(a, stream);
-    case 128: return launch_pf<128>(a, stream);
+    case 64: return launch_pp_kv<64>(a, stream);
+    case 128: return launch_pp_kv<128>(a, stream);
     case 256: return launch_pf<256>(a, stream);
     default: return hipErrorNotSupported;
   }

@@ -70,6 +70,15 @@ def test_paged_matches_oracle_and_dense_bitwise(page_size, layout):
     print(compare(f64(po), ref, pl.numpy(), lref))
 
 
+@pytest.mark.parametrize("page_size", [16, 128])
+def test_paged_d64(page_size):
+    # pages smaller than a 64-key tile (rows find their own pages) and
+    # larger (a tile lies in one page); ragged tails in both
+    case = inputs.prefill_case(q_lens=[7, 190, 64], kv_lens=[450, 190, 1100], hq=8, hkv=4, d=64, seed=43,
+                               causal=True, paged=True, page_size=page_size, layout="random")
+    print(_check(case))
+
+
 def test_constant_v_and_single_key():
     case = inputs.prefill_case(q_lens=[70], kv_lens=[70], hq=2, hkv=1, d=128, seed=51, causal=True, q_mult=4.0)
     const = torch.randn(128).to(torch.bfloat16)
