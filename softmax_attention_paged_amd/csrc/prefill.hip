@@ -32,40 +32,17 @@
 // the END of each request, so tile 0 of every request sees the most keys and
 // is launched first.
 //
-// Two kernels: for D in {64, 128} a software-pipelined one (scores of tile
-// j+1 on the matrix cores beside the softmax of tile j, separate K and V
-// double buffers, see prefill_pipe_kernel); for D = 256 a plain one with
-// 32-key tiles at one wave per SIMD (its Q operand and O accumulator fill
-// a SIMD's registers).
+// The kernel is software-pipelined: the scores of tile j+1 are computed on
+// the matrix cores beside the softmax of tile j, with separate K and V
+// double buffers (see prefill_pipe_kernel). D = 256 runs at one wave per
+// SIMD (its Q operand and O accumulator take most of a SIMD's registers),
+// D <= 128 at two.
 
 #include "attn_internal.h"
 #include "device_common.h"
 
 namespace attn {
 namespace {
-
-// W waves per workgroup, RB 32-row blocks per wave, N keys per tile, WPE
-// waves per SIMD the registers are budgeted for. One row block per wave at
-// two waves per SIMD beats two row blocks per wave at one (measured: the
-// extra accumulators spill into AGPR traffic); D = 256 needs a whole SIMD's
-// registers for its Q operand and O accumulator.
-template <int D> struct PfCfg;
-template <> struct PfCfg<256> { static constexpr int W = 4, RB = 1, N = 32, WPE = 1; };
-
-template <int D>
-struct PfGeom {
-  static constexpr int kW = PfCfg<D>::W;              // waves per workgroup
-  static constexpr int kRB = PfCfg<D>::RB;            // 32-row blocks per wave
-  static constexpr int kBlocks = kW * kRB;            // 32-row blocks per workgroup
-  static constexpr int kN = PfCfg<D>::N;              // keys per tile
-  static constexpr int kSub = kN / 32;                // 32-key S^T sub-tiles
-  static constexpr int kKK = kN / 16;                 // 16-key PV steps
-  static constexpr int kKB = D / 16;                  // QK k-steps (16 channels)
-  static constexpr int kNB = D / 32;                  // PV 32-channel blocks
-  static constexpr int kTileElems = kN * D;           // unpadded rows, 16-byte chunks swizzled
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kLoads = kN * kChunksPerRow / 64 / kW;   // 1 KB direct loads per wave per tensor
-};
 
 constexpr float kRebase = 8.0f;   // log2 units a row max may rise before the row re-bases
 
@@ -134,267 +111,9 @@ __device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit
   return u.q_end > 0;
 }
 
-// Issue the direct HBM -> LDS loads of one K and one V tile (16 bytes per
-// lane, lane i of a wave instruction lands at 16 i bytes past the
-// instruction's LDS base). Keys at or past the request's end get zeros with
-// ordinary LDS stores instead, so no table entry or row past the end is read.
-template <int D>
-__device__ __forceinline__ void pf_issue_tile(const PrefillArgs &a, const PfUnit &u, int j0, int wave, int lane,
-                                              __bf16 *klds, __bf16 *vlds) {
-  using G = PfGeom<D>;
-  const int32_t *bt_row = a.block_table ? a.block_table + (int64_t)u.b * a.block_table_stride : nullptr;
-  const int pmask = (1 << a.page_shift) - 1;
-#pragma unroll
-  for (int k = 0; k < G::kLoads; ++k) {
-    const int inst = k * G::kW + wave;                   // 1 KB LDS block of this instruction
-    const int chunk_lin = inst * 64 + lane;              // linear chunk index in the tile
-    const int row = chunk_lin / G::kChunksPerRow;
-    const int gchunk = (chunk_lin % G::kChunksPerRow) ^ pf_swz<D>(row);
-    const int j = j0 + row;
-    typedef __attribute__((address_space(3))) void lds_void;
-    lds_void *kdst = (lds_void *)(reinterpret_cast<uintptr_t>(klds + inst * 512));
-    lds_void *vdst = (lds_void *)(reinterpret_cast<uintptr_t>(vlds + inst * 512));
-    if (j < u.lk) {
-      const __bf16 *kp, *vp;
-      if (bt_row) {
-        const int64_t page = bt_row[j >> a.page_shift];
-        const int64_t slot = j & pmask;
-        kp = static_cast<const __bf16 *>(a.k) + page * a.k_stride_page + slot * a.k_stride_tok;
-        vp = static_cast<const __bf16 *>(a.v) + page * a.v_stride_page + slot * a.v_stride_tok;
-      } else {
-        kp = static_cast<const __bf16 *>(a.k) + (u.kv_off + j) * a.k_stride_tok;
-        vp = static_cast<const __bf16 *>(a.v) + (u.kv_off + j) * a.v_stride_tok;
-      }
-      __builtin_amdgcn_global_load_lds(kp + (int64_t)u.kvh * a.k_stride_head + gchunk * 8, kdst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + (int64_t)u.kvh * a.v_stride_head + gchunk * 8, vdst, 16, 0, 0);
-    } else {
-      *reinterpret_cast<u32x4 *>(klds + chunk_lin * 8) = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(vlds + chunk_lin * 8) = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-// Per-row-block softmax of one tile: (optional) mask, lazy max, P and sums.
-template <int D, bool MASK>
-__device__ __forceinline__ void pf_softmax(f32x16 (&sacc)[PfGeom<D>::kSub], int j0, int bound, int h, float c,
-                                           float &m, float &lsum, float &alpha, bf16x8 (&pop)[PfGeom<D>::kKK]) {
-  using G = PfGeom<D>;
-  float mx = kNegInf;
-#pragma unroll
-  for (int s = 0; s < G::kSub; ++s)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if constexpr (MASK) {
-        const int j = j0 + 32 * s + 8 * (i >> 2) + 4 * h + (i & 3);
-        sacc[s][i] = (j < bound) ? sacc[s][i] : kNegInf;
-      }
-      mx = fmaxf(mx, sacc[s][i]);
-    }
-  mx = half_max(mx) * c;
-  // keep the base unless the max rose by more than kRebase (or there was none)
-  const float m_new = (mx > m + kRebase) ? mx : m;
-  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-  alpha = exp2_fast(m - m_use);        // 1 when the base is kept; 0 from -inf
-  m = m_new;
-  float psum = 0.f;
-#pragma unroll
-  for (int s = 0; s < G::kSub; ++s)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pe = exp2_fast(__builtin_fmaf(sacc[s][i], c, -m_use));
-      pop[2 * s + (i >> 3)][i & 7] = to_bf16(pe);
-      psum += pe;
-    }
-  lsum = alpha * lsum + psum;
-}
-
-template <int D>
-__global__ __launch_bounds__(64 * PfGeom<D>::kW, PfCfg<D>::WPE) void prefill_kernel(const PrefillArgs a) {
-  using G = PfGeom<D>;
-  constexpr int RB = G::kRB;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * 2 * G::kTileElems];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h = lane >> 5;           // lane half
-  const int r32 = lane & 31;         // this lane's row within each 32-row block
-
-  // ---- which rows this workgroup owns ----
-  PfUnit u;
-  if (!pf_unit(a, G::kBlocks, u)) return;          // uniform: this request has fewer tiles
-  const int blocks_per_head = G::kBlocks / u.gh;
-  const int tq = u.tq;
-
-  // ---- this wave's row blocks ----
-  int head[RB], t[RB], bound[RB];
-  bool row_valid[RB];
-  int wave_max = 0, valid_min = 0x7fffffff;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int blk = wave * RB + rb;
-    head[rb] = u.h0 + blk / blocks_per_head;
-    t[rb] = u.q_end - tq + (blk % blocks_per_head) * 32 + r32;      // may be < 0 at the top
-    row_valid[rb] = t[rb] >= u.q_begin && t[rb] < u.q_end;
-    bound[rb] = u.lk;
-    if (a.causal) bound[rb] = min(u.lk, max(0, u.lk - u.lq + t[rb] + 1));
-    if (!row_valid[rb]) bound[rb] = 0;
-    wave_max = max(wave_max, bound[rb]);
-    if (row_valid[rb]) valid_min = min(valid_min, bound[rb]);
-  }
-  // Keys the wave's rows see, and the first key some valid row must mask;
-  // made scalar so the per-tile tests are branches, not per-lane selects.
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    wave_max = max(wave_max, __shfl_xor(wave_max, off, 64));
-    valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
-  }
-  wave_max = __builtin_amdgcn_readfirstlane(wave_max);
-  valid_min = __builtin_amdgcn_readfirstlane(valid_min);
-  int kv_end = u.lk;                                    // keys the workgroup walks
-  if (a.causal) kv_end = min(u.lk, max(0, u.lk - u.lq + u.q_end));
-
-  // ---- Q^T operands: lane holds Q[row t][16kb + 8h .. +8]; a negative scale
-  //      is carried by negating Q (exact in bf16) so c > 0 ----
-  const float c = fabsf(a.scale_log2);
-  const u32x4 qsign = (a.scale_log2 < 0.f) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u} : u32x4{};
-  bf16x8 qop[RB][G::kKB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (u.q_off + t[rb]) * a.q_stride_tok +
-                         (int64_t)head[rb] * a.q_stride_head;
-#pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb)
-      qop[rb][kb] = row_valid[rb] ? __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + h * 8)) ^ qsign)
-                                  : bf16x8{};
-  }
-
-  // Loop-invariant LDS byte offsets of this lane's operand chunks (the
-  // swizzle of a row depends only on its index modulo 16).
-  int koff[G::kKB];
-  {
-    const int hf = h ^ pf_swz<D>(r32);
-#pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) koff[kb] = r32 * D * 2 + ((2 * kb) ^ hf) * 16;
-  }
-  const int s16 = lane & 15;
-  int voff[2][G::kNB];
-  {
-    const int row0 = 4 * h + (s16 >> 2);
-    const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
-    const int f0 = pf_swz<D>(row0), f1 = pf_swz<D>(row0 + 8);
-#pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) {
-      voff[0][nb] = row0 * D * 2 + ((4 * nb + cb) ^ f0) * 16 + 8 * (s16 & 1);
-      voff[1][nb] = (row0 + 8) * D * 2 + ((4 * nb + cb) ^ f1) * 16 + 8 * (s16 & 1);
-    }
-  }
-
-  float m[RB], lsum[RB];
-  f32x16 oacc[RB][G::kNB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = kNegInf;
-    lsum[rb] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) oacc[rb][nb] = f32x16{};
-  }
-
-  const int ntiles = (kv_end + G::kN - 1) / G::kN;
-  if (ntiles > 0) pf_issue_tile<D>(a, u, 0, wave, lane, lds, lds + G::kTileElems);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = it * G::kN;
-    const char *kbytes = reinterpret_cast<const char *>(lds + (it & 1) * 2 * G::kTileElems);
-    const char *vbytes = kbytes + G::kTileElems * 2;
-    // The other buffer was last read in iteration it-1, which every wave
-    // finished before the barrier that ended it: load the next tile into it.
-    if (it + 1 < ntiles) {
-      __bf16 *knext = lds + ((it + 1) & 1) * 2 * G::kTileElems;
-      pf_issue_tile<D>(a, u, j0 + G::kN, wave, lane, knext, knext + G::kTileElems);
-    }
-
-    if (j0 < wave_max) {
-      // ---- S^T = K Q^T: each K operand feeds every row block ----
-      f32x16 sacc[RB][G::kSub];
-#pragma unroll
-      for (int s = 0; s < G::kSub; ++s) {
-        bf16x8 kop[G::kKB];
-#pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb)
-          kop[kb] = *reinterpret_cast<const bf16x8 *>(kbytes + koff[kb] + s * 32 * D * 2);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          sacc[rb][s] = f32x16{};
-#pragma unroll
-          for (int kb = 0; kb < G::kKB; ++kb) sacc[rb][s] = mfma32x32x16(kop[kb], qop[rb][kb], sacc[rb][s]);
-        }
-      }
-      // ---- softmax (row r32 of each block lives in this lane) ----
-      bf16x8 pop[RB][G::kKK];
-      float alpha[RB];
-      if (j0 + G::kN > valid_min) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          pf_softmax<D, true>(sacc[rb], j0, bound[rb], h, c, m[rb], lsum[rb], alpha[rb], pop[rb]);
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          pf_softmax<D, false>(sacc[rb], j0, bound[rb], h, c, m[rb], lsum[rb], alpha[rb], pop[rb]);
-      }
-      bool rebase = false;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) rebase |= alpha[rb] != 1.f;
-      if (__ballot(rebase)) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int nb = 0; nb < G::kNB; ++nb) oacc[rb][nb] *= alpha[rb];
-      }
-      // ---- O^T += V^T P^T: each V^T operand feeds every row block ----
-#pragma unroll
-      for (int kk = 0; kk < G::kKK; ++kk) {
-#pragma unroll
-        for (int nb = 0; nb < G::kNB; ++nb) {
-          const bf16x4 lo = lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2);
-          const bf16x4 hi = lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2);
-          const bf16x8 vop = concat(lo, hi);
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) oacc[rb][nb] = mfma32x32x16(vop, pop[rb][kk], oacc[rb][nb]);
-        }
-      }
-    }
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of the next tile landed
-    __syncthreads();
-  }
-
-  // ---- epilogue: O / l -> bf16; LSE2 = m + log2(l) ----
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l = half_sum(lsum[rb]);
-    if (!row_valid[rb]) continue;
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
-    __bf16 *orow = static_cast<__bf16 *>(a.o) + (u.q_off + t[rb]) * a.o_stride_tok + (int64_t)head[rb] * a.o_stride_head;
-#pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ob;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[rb][nb][4 * g + i] * inv);
-        *reinterpret_cast<u32x2 *>(orow + 32 * nb + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, ob);
-      }
-    if (a.lse && h == 0) {
-      const float muse = (m[rb] == kNegInf) ? 0.f : m[rb];
-      a.lse[(u.q_off + t[rb]) * a.num_q_heads + head[rb]] = (l > 0.f) ? muse + __log2f(l) : kNegInf;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Software-pipelined kernel for D in {64, 128}: four waves, one 32-row block
-// per wave, 64-key tiles. Inside a wave the scores of tile j+1 are computed
+// Software-pipelined kernel: four waves, one 32-row block per wave, 64-key
+// tiles. Inside a wave the scores of tile j+1 are computed
 // on the matrix cores while the vector units turn the scores of tile j into
 // P, so neither unit waits for the other to drain. K and V have their own
 // double buffers, which lets K(j+1) be resident one iteration before V(j+1):
@@ -405,11 +124,14 @@ __global__ __launch_bounds__(64 * PfGeom<D>::kW, PfCfg<D>::WPE) void prefill_ker
 //
 // The max over S(j+1) is taken unmasked; a tile that needs a mask masks and
 // takes it again. Paged block-table entries are fetched one tile ahead of
-// the loads that use them, so no load waits on a table read.
+// the loads that use them, so no load waits on a table read, and the tile
+// loads are issued as inline assembly so that no LDS read in between waits
+// for them (only the barrier at the top of the next iteration does).
 
 template <int D>
 struct PpGeom {
   static constexpr int kW = 4;                         // waves per workgroup
+  static constexpr int kWPE = D <= 128 ? 2 : 1;        // waves per SIMD the registers allow
   static constexpr int kN = 64;                        // keys per tile
   static constexpr int kKB = D / 16;                   // QK k-steps
   static constexpr int kNB = D / 32;                   // PV 32-channel blocks
@@ -417,6 +139,10 @@ struct PpGeom {
   static constexpr int kTile = kN * D;                 // elements of one K or V tile
   static constexpr int kCPR = D / 8;                   // 16-byte chunks per row
   static constexpr int kLoads = kN * kCPR / 64 / kW;   // 1 KB direct loads per wave per tile
+  static constexpr int kRowsPerInst = 64 / kCPR;       // rows one load instruction covers
+  // distinct per-lane offsets: instruction k starts at row (k kW + wave) kRowsPerInst
+  // and the swizzle repeats every 16 rows
+  static constexpr int kLaneOffs = (kW * kRowsPerInst >= 16) ? 1 : 16 / (kW * kRowsPerInst);
 };
 
 // How K/V rows are addressed: dense, paged with pages of at least one tile
@@ -430,28 +156,33 @@ __device__ __forceinline__ int pp_row(int k, int wave, int lane) {
   return ((k * G::kW + wave) * 64 + lane) / G::kCPR;
 }
 
-// This lane's byte offset inside the rows one load instruction covers. It
-// is the same for every instruction of a wave: instructions start a
-// multiple of 16 rows apart and the swizzle depends on the row modulo 16.
+// This lane's byte offsets inside the rows one load instruction covers.
+// Load instruction k uses entry k % kLaneOffs: the swizzle depends on the
+// row modulo 16, and instructions k and k + kLaneOffs start a multiple of
+// 16 rows apart.
 template <int D>
-__device__ __forceinline__ uint32_t pp_lane_off(int wave, int lane, int64_t stride_tok) {
+__device__ __forceinline__ void pp_lane_off(int wave, int lane, int64_t stride_tok,
+                                            uint32_t (&off)[PpGeom<D>::kLaneOffs]) {
   using G = PpGeom<D>;
   const int r = lane / G::kCPR;
-  const int gchunk = (lane % G::kCPR) ^ pf_swz<D>(wave * (64 / G::kCPR) + r);
-  return static_cast<uint32_t>((r * stride_tok + gchunk * 8) * 2);
+#pragma unroll
+  for (int v = 0; v < G::kLaneOffs; ++v) {
+    const int gchunk = (lane % G::kCPR) ^ pf_swz<D>((v * G::kW + wave) * G::kRowsPerInst + r);
+    off[v] = static_cast<uint32_t>((r * stride_tok + gchunk * 8) * 2);
+  }
 }
 
 // Loads of a tile that lies wholly inside the request (and, paged, inside
 // one page): `tile` is its first row, wave-uniform.
 template <int D>
-__device__ __forceinline__ void pp_issue_whole(const __bf16 *tile, int64_t stride_tok, uint32_t lane_off, int wave,
+__device__ __forceinline__ void pp_issue_whole(const __bf16 *tile, int64_t stride_tok,
+                                               const uint32_t (&lane_off)[PpGeom<D>::kLaneOffs], int wave,
                                                uint32_t lds_dst) {
   using G = PpGeom<D>;
-  constexpr int kRows = 64 / G::kCPR;    // rows per load instruction
 #pragma unroll
   for (int k = 0; k < G::kLoads; ++k) {
     const int inst = k * G::kW + wave;
-    lds_dma16(tile + (int64_t)inst * kRows * stride_tok, lane_off, lds_dst + inst * 1024);
+    lds_dma16(tile + (int64_t)inst * G::kRowsPerInst * stride_tok, lane_off[k % G::kLaneOffs], lds_dst + inst * 1024);
   }
 }
 
@@ -484,8 +215,8 @@ __device__ __forceinline__ void pp_issue_rows(const __bf16 *src, int64_t stride_
 // One K or V tile: `src` is the request's first key (dense) or page 0
 // (paged) of the workgroup's KV head.
 template <int D, int KV>
-__device__ __forceinline__ void pp_issue(const __bf16 *src, int64_t stride_page, int64_t stride_tok, uint32_t lane_off,
-                                         int page, const int (&pid)[PpGeom<D>::kLoads], int j0, int lk, int pmask,
+__device__ __forceinline__ void pp_issue(const __bf16 *src, int64_t stride_page, int64_t stride_tok,
+                                         const uint32_t (&lane_off)[PpGeom<D>::kLaneOffs], int page, const int (&pid)[PpGeom<D>::kLoads], int j0, int lk, int pmask,
                                          int wave, int lane, __bf16 *dst) {
   if (KV != kKvNarrowPages && j0 + PpGeom<D>::kN <= lk) {
     const __bf16 *tile = (KV == kKvDense) ? src + (int64_t)j0 * stride_tok
@@ -584,7 +315,7 @@ __device__ __forceinline__ void pp_step(f32x16 (&s)[2], float &mx, float m_use, 
 }
 
 template <int D, int KV>
-__global__ __launch_bounds__(64 * PpGeom<D>::kW, 2) void prefill_pipe_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_pipe_kernel(const PrefillArgs a) {
   using G = PpGeom<D>;
   __shared__ __attribute__((aligned(16))) __bf16 lds[4 * G::kTile];   // K slot 0, K slot 1, V slot 0, V slot 1
   const int lane = threadIdx.x & 63;
@@ -650,8 +381,9 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, 2) void prefill_pipe_kernel(con
     ksrc += u.kv_off * a.k_stride_tok;
     vsrc += u.kv_off * a.v_stride_tok;
   }
-  const uint32_t koff_g = pp_lane_off<D>(wave, lane, a.k_stride_tok);
-  const uint32_t voff_g = pp_lane_off<D>(wave, lane, a.v_stride_tok);
+  uint32_t koff_g[G::kLaneOffs], voff_g[G::kLaneOffs];
+  pp_lane_off<D>(wave, lane, a.k_stride_tok, koff_g);
+  pp_lane_off<D>(wave, lane, a.v_stride_tok, voff_g);
   const int32_t *bt_row = (KV != kKvDense) ? a.block_table + (int64_t)u.b * a.block_table_stride : nullptr;
   const int pmask = (1 << a.page_shift) - 1;
   // Table entries of the next K tile (it+2) and V tile (it+1) to load, each
@@ -757,17 +489,6 @@ hipError_t launch_pp(const PrefillArgs &a, hipStream_t stream) {
 }
 
 template <int D>
-hipError_t launch_pf(const PrefillArgs &a, hipStream_t stream) {
-  using G = PfGeom<D>;
-  const int gh = pf_heads_per_wg(a.num_q_heads / a.num_kv_heads);
-  const int tq = 32 * G::kBlocks / gh;
-  const int64_t q_tiles = (a.max_seqlen_q + tq - 1) / tq;
-  const int64_t blocks = q_tiles * a.batch * (a.num_q_heads / gh);
-  hipLaunchKernelGGL(prefill_kernel<D>, dim3((unsigned)blocks), dim3(64 * G::kW), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <int D>
 hipError_t launch_pp_kv(const PrefillArgs &a, hipStream_t stream) {
   if (!a.block_table) return launch_pp<D, kKvDense>(a, stream);
   if ((1 << a.page_shift) >= PpGeom<D>::kN) return launch_pp<D, kKvWidePages>(a, stream);
@@ -780,7 +501,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
     case 64: return launch_pp_kv<64>(a, stream);
     case 128: return launch_pp_kv<128>(a, stream);
-    case 256: return launch_pf<256>(a, stream);
+    case 256: return launch_pp_kv<256>(a, stream);
     default: return hipErrorNotSupported;
   }
 }
