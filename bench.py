@@ -131,7 +131,8 @@ def secondary_prefill(name_fn, steps: int) -> dict:
     del lse
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
-            "roofline": {"bound": "mfma", "kernel": f"prefill_kernel<{d}>", "achieved": round(tf, 1),
+            "roofline": {"bound": "mfma", "kernel": f"prefill_pipe_kernel<{d}, {1 if c.paged else 0}>",
+                         "achieved": round(tf, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
 
 
@@ -273,7 +274,7 @@ def main() -> int:
                    "num_splits": plan["num_splits"], "split_tokens": plan["split_tokens"],
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_gqa_kernel<128>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_gqa_tokens_kernel<128>", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_ms, 5),
