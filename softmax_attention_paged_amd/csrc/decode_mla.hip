@@ -11,17 +11,32 @@
 // split) and writes split partials merged by log-sum-exp in a second kernel
 // ("TokenSpeed-MLA", section "Decode performance").
 //
-// Workgroup: 8 waves x 16 rows. Per 32-key tile:
-//   - the latent tile is gathered through the block table and stored ONCE
-//     in LDS (double-buffered, loaded one tile ahead through registers): the
-//     same bytes serve as K and as V;
-//   - FP8 e4m3 codes are widened to bf16 exactly while staging (every e4m3
-//     value is a bf16 value) and the per-tensor scale is applied to the
-//     scores and to the final output instead ("TokenSpeed-MLA": FP8 KV with
-//     FP32 softmax exponentials and sums, bf16 output);
-//   - S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the
-//     row state lane-local as in the GQA decode kernel; V^T is read from LDS
-//     with ds_read_b64_tr_b16.
+// Workgroup: 4 waves x 32 rows at one wave per SIMD, so that the 32 x 512
+// FP32 output block of a wave (256 registers per lane) fills the accumulation
+// registers; the query operand of the first 288 columns stays in vector
+// registers, the other 288 columns wait in LDS (rows padded to 592 bytes,
+// bank-conflict-free). Per 32-key tile:
+//   - the latent tile is gathered through the block table ONCE into LDS
+//     (double-buffered, one tile ahead): bf16 rows by direct HBM -> LDS
+//     loads, fp8 e4m3 rows through registers, widened to bf16 exactly on the
+//     way (every e4m3 value is a bf16 value), the per-tensor scale applied to
+//     the scores and the final output instead ("TokenSpeed-MLA": FP8 KV with
+//     FP32 softmax exponentials and sums, bf16 output). The same LDS bytes
+//     serve as K and, for the first 512 columns, as V;
+//   - S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16: each K or V
+//     operand read from LDS feeds 32 rows; the row state is lane-local and P
+//     is the B operand straight from the score registers; V^T is read with
+//     ds_read_b64_tr_b16;
+//   - static-anchor softmax ("Flywheel Attention", section "Static-anchor
+//     softmax" and Appendix A): each row fixes its anchor at the max of its
+//     first tile and never moves it, so O is never rescaled (it stays in the
+//     accumulation registers, untouched by vector ALU work); after each tile
+//     the running sum is checked against 2^kAnchorLog2, which bounds every
+//     exponential taken so far. A failed check (a score far above the anchor,
+//     or an overflow) makes the whole workgroup start its split again with
+//     the failing rows' anchors raised to that tile's max; the pages replay
+//     one block from saved state instead, which would need a second copy of
+//     O. One FP32 sum of the exponentials normalises O and gives the LSE.
 // Workgroups are renumbered so that consecutive units run on the same XCD:
 // the query groups of one split then share that XCD's L2 for the latent.
 
@@ -33,22 +48,34 @@ namespace {
 
 constexpr int kDk = 576;
 constexpr int kDv = 512;
-constexpr int kMlaWaves = 8;
-constexpr int kTileN = kMlaTileTokens;            // 32 keys per tile
-constexpr int kStride = kDk + 16;                 // LDS row stride (bf16)
-constexpr int kTileElems = kTileN * kStride;
-constexpr int kKB = kDk / 32;                     // 18 QK k-steps
-constexpr int kNB = kDv / 16;                     // 32 PV channel blocks
-constexpr int kThreads = 64 * kMlaWaves;
+constexpr int kW = 4;                              // waves, 32 rows each
+constexpr int kThreads = 64 * kW;
+constexpr int kTileN = kMlaTileTokens;             // 32 keys per tile
+constexpr int kRowB = kDk * 2;                     // bytes of a latent row in LDS
+constexpr int kChunks = kDk / 8;                   // 16-byte chunks per row
+constexpr int kTileB = kTileN * kRowB;             // bytes of one LDS tile
+constexpr int kKB = kDk / 16;                      // 36 QK k-steps
+constexpr int kKBReg = 18;                         // k-steps whose Q operand stays in registers
+constexpr int kQRowB = (kDk - 16 * kKBReg) * 2 + 16;   // LDS bytes per row of the other Q columns (padded)
+constexpr int kNB = kDv / 32;                      // 16 PV channel blocks
+constexpr int kDma = kTileN * kChunks / 64 / kW;   // 9 direct loads per wave per bf16 tile
+constexpr int kF8Chunks = kTileN * (kDk / 16);     // 16-byte fp8 chunks per tile
+constexpr int kF8PerThread = (kF8Chunks + kThreads - 1) / kThreads;
 constexpr int kXcds = 8;
+// A row's running sum may reach 2^kAnchorLog2 before its split restarts: then
+// every exponential is at most 2^40, a split's sum at most 2^60 (splits hold
+// under 2^20 keys), and O at most |V|max 2^60 (finite for fp8 codes, |c| <=
+// 448, and for bf16 latents below 2^67).
+constexpr float kAnchorLog2 = 40.0f;
+constexpr int kMaxRestarts = 8;                    // each restart raises an anchor by > 20 log2 units
+static_assert(kTileN * kChunks % (64 * kW) == 0, "whole direct loads per tile");
+static_assert(kW * 32 == kMlaRows, "rows per workgroup");
 
-// Chunks a thread stages per tile: bf16 rows are 72 16-byte chunks, fp8 rows 36.
-template <bool FP8>
-struct Stage {
-  static constexpr int kRowChunks = FP8 ? kDk / 16 : kDk / 8;
-  static constexpr int kChunks = kTileN * kRowChunks;
-  static constexpr int kPerThread = (kChunks + kThreads - 1) / kThreads;
-};
+// LDS rows are unpadded; 16-byte chunk c of row r sits at slot c ^ swz(r).
+// With the 1152-byte row stride (rows alternate bank halves) this keeps the
+// 16 rows of a K-operand read and the 4 rows x 4 chunks of a transposing V
+// read on distinct banks. swz < 8, so a chunk stays in its aligned group of 8.
+__device__ __forceinline__ int mla_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // Bijective renumbering: hardware dispatches workgroup i to XCD i % 8; unit
 // numbers handed to one XCD become consecutive.
@@ -78,56 +105,104 @@ __device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, bf16x8 &lo, bf16x8 &hi) 
   }
 }
 
+// Where this thread's tile loads go. bf16: load k of the wave fills LDS slot
+// (k kW + wave) 64 + lane; fp8: chunk c of the thread is fp8 chunk
+// c kThreads + tid of the tile (row, 16 codes).
+struct MlaLoadMap {
+  uint32_t off[kDma > kF8PerThread ? kDma : kF8PerThread];   // byte offset from the tile's first row
+};
+
 template <bool FP8>
-__device__ __forceinline__ void stage_load(const DecodeMlaArgs &a, const int32_t *bt_row, int j0, int end, int tid,
-                                           u32x4 (&r)[Stage<FP8>::kPerThread]) {
-  using S = Stage<FP8>;
-  const int pmask = (1 << a.page_shift) - 1;
-#pragma unroll
-  for (int c = 0; c < S::kPerThread; ++c) {
+__device__ __forceinline__ void mla_row_chunk(int c, int wave, int lane, int tid, int &row, int &chunk) {
+  if constexpr (FP8) {
     const int idx = c * kThreads + tid;
-    const int trow = idx / S::kRowChunks;
-    const int j = j0 + trow;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (idx < S::kChunks && j < end) {
-      const int64_t page = bt_row[j >> a.page_shift];
-      const int64_t elem = page * a.kv_stride_page + (int64_t)(j & pmask) * a.kv_stride_tok +
-                           (idx % S::kRowChunks) * (FP8 ? 16 : 8);
-      const char *base = static_cast<const char *>(a.kv_cache) + elem * (FP8 ? 1 : 2);
-      v = *reinterpret_cast<const u32x4 *>(base);
-    }
-    r[c] = v;
+    row = idx / (kDk / 16);
+    chunk = idx % (kDk / 16);
+  } else {
+    const int slot = (c * kW + wave) * 64 + lane;
+    row = slot / kChunks;
+    chunk = (slot % kChunks) ^ mla_swz(row);   // global chunk stored at this slot
   }
 }
 
+struct MlaCtx {
+  const char *kv;          // cache bytes
+  int64_t page_b, tok_b;   // page / token strides in bytes
+  const int32_t *bt_row;
+  int page_shift, pmask;
+  bool wide;               // every tile lies inside one page
+};
+
+// Issue the loads of the tile at key j0 (keys >= end are zero). bf16: direct
+// HBM -> LDS into `dst`; fp8: into the thread's stage registers.
 template <bool FP8>
-__device__ __forceinline__ void stage_store(__bf16 *tile, int tid, const u32x4 (&r)[Stage<FP8>::kPerThread]) {
-  using S = Stage<FP8>;
-#pragma unroll
-  for (int c = 0; c < S::kPerThread; ++c) {
-    const int idx = c * kThreads + tid;
-    if (idx >= S::kChunks) continue;
-    const int trow = idx / S::kRowChunks;
+__device__ __forceinline__ void mla_issue(const MlaCtx &x, const MlaLoadMap &map, int j0, int end, int wave, int lane,
+                                          int tid, char *dst, u32x4 (&stage)[kF8PerThread]) {
+  if (x.wide && j0 + kTileN <= end) {
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const int64_t page = reinterpret_cast<const_i32 *>(reinterpret_cast<uintptr_t>(x.bt_row))[j0 >> x.page_shift];
+    const char *tile = x.kv + page * x.page_b + (int64_t)(j0 & x.pmask) * x.tok_b;
     if constexpr (FP8) {
-      bf16x8 lo, hi;
-      fp8x16_to_bf16(r[c], lo, hi);
-      __bf16 *dst = tile + trow * kStride + (idx % S::kRowChunks) * 16;
-      store_bf16x8_lds(dst, lo);
-      store_bf16x8_lds(dst + 8, hi);
+#pragma unroll
+      for (int c = 0; c < kF8PerThread; ++c)
+        stage[c] = (c * kThreads + tid < kF8Chunks) ? *reinterpret_cast<const u32x4 *>(tile + map.off[c])
+                                                    : u32x4{0u, 0u, 0u, 0u};
     } else {
-      store_bf16x8_lds(tile + trow * kStride + (idx % S::kRowChunks) * 8, __builtin_bit_cast(bf16x8, r[c]));
+      const uint32_t lds = lds_address(dst);
+#pragma unroll
+      for (int k = 0; k < kDma; ++k) lds_dma16(tile, map.off[k], lds + (k * kW + wave) * 1024);
+    }
+    return;
+  }
+  // row by row: the tail tile, or pages smaller than a tile
+  constexpr int kN = FP8 ? kF8PerThread : kDma;
+#pragma unroll
+  for (int c = 0; c < kN; ++c) {
+    int row, chunk;
+    mla_row_chunk<FP8>(c, wave, lane, tid, row, chunk);
+    const int j = j0 + row;
+    const bool in = (!FP8 || c * kThreads + tid < kF8Chunks) && j < end;
+    const char *src = nullptr;
+    if (in) {
+      const int64_t page = x.bt_row[j >> x.page_shift];
+      src = x.kv + page * x.page_b + (int64_t)(j & x.pmask) * x.tok_b + chunk * 16;
+    }
+    if constexpr (FP8) {
+      stage[c] = in ? *reinterpret_cast<const u32x4 *>(src) : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const int slot = (c * kW + wave) * 64 + lane;
+      if (in)
+        lds_dma16(src, lds_address(dst + slot * 16));
+      else
+        *reinterpret_cast<u32x4 *>(dst + slot * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
 
+// fp8: widen the staged codes and store them as bf16 rows.
+__device__ __forceinline__ void mla_store_fp8(char *dst, int tid, const u32x4 (&stage)[kF8PerThread]) {
+#pragma unroll
+  for (int c = 0; c < kF8PerThread; ++c) {
+    const int idx = c * kThreads + tid;
+    if (idx >= kF8Chunks) continue;
+    const int row = idx / (kDk / 16), c8 = idx % (kDk / 16);
+    bf16x8 lo, hi;
+    fp8x16_to_bf16(stage[c], lo, hi);
+    char *r = dst + row * kRowB;
+    store_bf16x8_lds(r + ((2 * c8) ^ mla_swz(row)) * 16, lo);
+    store_bf16x8_lds(r + ((2 * c8 + 1) ^ mla_swz(row)) * 16, hi);
+  }
+}
+
 template <bool FP8>
-__global__ __launch_bounds__(kThreads) void decode_mla_kernel(const DecodeMlaArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 tiles[2 * kTileElems];
+__global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMlaArgs a) {
+  __shared__ __attribute__((aligned(16))) char tiles[2 * kTileB];
+  __shared__ __attribute__((aligned(16))) char qlds[kMlaRows * kQRowB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int kg = lane >> 4;
-  const int row16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int r32 = lane & 31;
 
   const int n_units = a.batch * a.num_splits * a.q_groups;
   int unit = xcd_unit(blockIdx.x, n_units);
@@ -142,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(const DecodeMlaArg
   const int c0 = split * a.split_tokens;
   const int c1 = min(unit_bound, c0 + a.split_tokens);
 
-  // this lane's row: r = 16 * wave + lane % 16 -> query token qg*F + r/H, head r%H
-  const int r = 16 * wave + row16;
+  // this lane's row: r = 32 * wave + lane % 32 -> query token qg*F + r/H, head r%H
+  const int r = 32 * wave + r32;
   const bool row_valid = r < a.rows;
   const int t_row = qg * a.fold + (row_valid ? r / a.num_heads : 0);
   const int h_row = row_valid ? r % a.num_heads : 0;
@@ -152,128 +227,211 @@ __global__ __launch_bounds__(kThreads) void decode_mla_kernel(const DecodeMlaArg
   int bound = lk;
   if (a.causal) bound = min(lk, max(0, lk - a.q_len + t_row + 1));
   const int row_end = min(bound, c1);
-  const bool wave_active = 16 * wave < a.rows;
 
   if (c0 >= c1) {   // uniform: no key of this split is visible
     if (row_valid) {
       if (a.num_splits == 1) {
-        __bf16 *dst = static_cast<__bf16 *>(a.o) + ridx * kDv + 4 * kg;
+        __bf16 *dst = static_cast<__bf16 *>(a.o) + ridx * kDv + 4 * half;
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb) *reinterpret_cast<u32x2 *>(dst + nb * 16) = u32x2{0u, 0u};
-        if (a.lse && kg == 0) a.lse[ridx] = kNegInf;
-      } else if (kg == 0) {
+        for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2 *>(dst + 32 * nb + 8 * g) = u32x2{0u, 0u};
+        if (a.lse && half == 0) a.lse[ridx] = kNegInf;
+      } else if (half == 0) {
         a.lse_parts[(int64_t)split * R + ridx] = kNegInf;
       }
     }
     return;
   }
 
-  // Q^T operand: lane holds Q[row r][32kb + 8kg .. +8]
-  bf16x8 qop[kKB];
+  // first key of the split some valid row of this wave must mask (scalar)
+  int valid_min = row_valid ? row_end : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
+  valid_min = __builtin_amdgcn_readfirstlane(valid_min);
+  const bool wave_active = 32 * wave < a.rows;
+
+  // Q^T operand: lane holds Q[row r][16 kb + 8 half .. +8]; a negative scale
+  // negates Q (exact in bf16) so that c > 0
+  const float c = fabsf(a.scale_log2);
+  const u32x4 qsign = (a.scale_log2 < 0.f) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u} : u32x4{};
+  bf16x8 qop[kKBReg];
   {
     const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + ridx * kDk;
 #pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) qop[kb] = row_valid ? load_bf16x8(qrow + kb * 32 + kg * 8) : bf16x8{};
+    for (int kb = 0; kb < kKBReg; ++kb)
+      qop[kb] = row_valid ? __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + half * 8)) ^ qsign)
+                          : bf16x8{};
+    // the other columns: chunk 2 (kb - kKBReg) + half of the row's LDS copy
+    char *qdst = qlds + r * kQRowB;
+#pragma unroll
+    for (int kb = kKBReg; kb < kKB; ++kb) {
+      const u32x4 v = row_valid ? __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + half * 8)) ^ qsign : u32x4{};
+      *reinterpret_cast<u32x4 *>(qdst + (2 * (kb - kKBReg) + half) * 16) = v;
+    }
   }
-  float m = kNegInf, lsum = 0.f, lexact = 0.f;
-  f32x4 oacc[kNB];
+  const char *qsrc = qlds + r * kQRowB + half * 16;
+
+  // LDS operand offsets: chunk 2 kb + half of key row r32 is at
+  // koff[kb % 4] + 128 (kb / 4); the V^T reads (see the prefill kernel for the
+  // lane mapping) at voff[lo/hi][nb % 2] + 128 (nb / 2) + 16 kk rows
+  int koff[4];
+  {
+    const int f = mla_swz(r32);
 #pragma unroll
-  for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) koff[t] = r32 * kRowB + ((2 * t + half) ^ f) * 16;
+  }
+  int voff[2][2];
+  {
+    const int s16 = lane & 15;
+    const int row0 = 4 * half + (s16 >> 2);
+    const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    const int f0 = mla_swz(row0), f1 = mla_swz(row0 + 8);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      voff[0][q] = row0 * kRowB + ((4 * q + cb) ^ f0) * 16 + 8 * (s16 & 1);
+      voff[1][q] = (row0 + 8) * kRowB + ((4 * q + cb) ^ f1) * 16 + 8 * (s16 & 1);
+    }
+  }
 
-  const int32_t *bt_row = a.block_table + (int64_t)b * a.block_table_stride;
-  u32x4 stage[Stage<FP8>::kPerThread];
-  stage_load<FP8>(a, bt_row, c0, c1, tid, stage);
-  stage_store<FP8>(tiles, tid, stage);
-  __syncthreads();
+  MlaCtx x;
+  x.kv = static_cast<const char *>(a.kv_cache);
+  x.page_b = a.kv_stride_page * (FP8 ? 1 : 2);
+  x.tok_b = a.kv_stride_tok * (FP8 ? 1 : 2);
+  x.bt_row = a.block_table + (int64_t)b * a.block_table_stride;
+  x.page_shift = a.page_shift;
+  x.pmask = (1 << a.page_shift) - 1;
+  x.wide = (1 << a.page_shift) >= kTileN;   // tiles start at multiples of 32 keys
+  MlaLoadMap map;
+#pragma unroll
+  for (int k = 0; k < (FP8 ? kF8PerThread : kDma); ++k) {
+    int row, chunk;
+    mla_row_chunk<FP8>(k, wave, lane, tid, row, chunk);
+    map.off[k] = static_cast<uint32_t>(row * x.tok_b + chunk * 16);
+  }
 
+  __shared__ int restart;                     // set by a wave whose rows failed the anchor check
+  if (tid == 0) restart = 0;
+  float anchor = kNegInf;                     // this row's static anchor (log2 units); -inf: no key yet
+  float lsum = 0.f;
+  f32x16 oacc[kNB];
   const int ntiles = (c1 - c0 + kTileN - 1) / kTileN;
-  const int src_row = 4 * kg + (row16 >> 2);
-  const int src_col = 4 * (row16 & 3);
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = c0 + it * kTileN;
-    const __bf16 *tile = tiles + (it & 1) * kTileElems;
-    const bool more = it + 1 < ntiles;
-    if (more) stage_load<FP8>(a, bt_row, j0 + kTileN, c1, tid, stage);
+  u32x4 stage[kF8PerThread];
+  const float sum_limit = exp2f(kAnchorLog2);
 
-    if (wave_active) {
-      // S^T: sacc[t] holds keys j0 + 16t + 4kg + i of row r
-      f32x4 sacc[2];
+  for (int attempt = 0;; ++attempt) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const __bf16 *krow = tile + (16 * t + row16) * kStride + 8 * kg;
+    for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x16{};
+    lsum = 0.f;
+    mla_issue<FP8>(x, map, c0, c1, wave, lane, tid, tiles, stage);
+    if constexpr (FP8) mla_store_fp8(tiles, tid, stage);
+    for (int it = 0; it < ntiles; ++it) {
+      const int j0 = c0 + it * kTileN;
+      const int p = it & 1;
+      // tile it has landed for every wave; every wave is done with tile it-1,
+      // whose buffer takes tile it+1
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (restart) break;                     // uniform: read after the barrier
+      if (it + 1 < ntiles) mla_issue<FP8>(x, map, j0 + kTileN, c1, wave, lane, tid, tiles + (p ^ 1) * kTileB, stage);
+
+      if (wave_active) {
+        const char *tile = tiles + p * kTileB;
+        // S^T: lane holds keys j0 + 8(i/4) + 4 half + i%4 of row r32
+        f32x16 s = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < kKB; ++kb)
-          sacc[t] = mfma16x16x32(*reinterpret_cast<const bf16x8 *>(krow + 32 * kb), qop[kb], sacc[t]);
-      }
-      float x[8];
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j0 + 16 * t + 4 * kg + i;
-          const float v = (j < row_end) ? sacc[t][i] * a.scale_log2 : kNegInf;
-          x[4 * t + i] = v;
-          mx = fmaxf(mx, v);
+        for (int kb = 0; kb < kKB; ++kb) {
+          const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(tile + koff[kb & 3] + (kb >> 2) * 128);
+          const bf16x8 qv = (kb < kKBReg) ? qop[kb < kKBReg ? kb : 0]
+                                          : *reinterpret_cast<const bf16x8 *>(qsrc + (kb - kKBReg) * 32);
+          s = mfma32x32x16(kop, qv, s);
         }
-      mx = fmaxf(mx, wave_shfl_xor(mx, 16));
-      mx = fmaxf(mx, wave_shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m - m_use);
-      m = m_new;
-      bf16x8 pop;
-      float psum = 0.f, pexact = 0.f;
+        if (j0 + kTileN > valid_min) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = exp2_fast(x[e] - m_use);
-        const __bf16 pb = to_bf16(pe);
-        pop[e] = pb;
-        psum += bf16_to_f32(pb);
-        pexact += pe;
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            s[i] = (j < row_end) ? s[i] : kNegInf;
+          }
+        }
+        if (it == 0 && attempt == 0) {        // the anchor: the max of the row's first tile
+          float mx = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          anchor = half_max(mx) * c;
+        }
+        const float a_use = (anchor == kNegInf) ? 0.f : anchor;
+        bf16x8 pop[2];
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pe = exp2_fast(__builtin_fmaf(s[i], c, -a_use));
+          pop[i >> 3][i & 7] = to_bf16(pe);
+          if (i & 1) ps1 += pe; else ps0 += pe;
+        }
+        lsum += half_sum(ps0 + ps1);
+        if (__ballot(!(lsum <= sum_limit) && lsum == lsum)) {
+          // some row's sum left the budget (NaN sums, from NaN inputs, pass
+          // through): raise those rows' anchors to this tile's max and start over
+          float mx = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          const float mt = half_max(mx) * c;
+          if (!(lsum <= sum_limit)) anchor = fmaxf(anchor, mt);
+          restart = 1;
+        }
+        // O^T += V^T P^T; V is the first 512 columns of the latent tile
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int nb = 0; nb < kNB; ++nb) {
+            const char *vb = tile + kk * 16 * kRowB + (nb >> 1) * 128;
+            const bf16x4 lo = lds_read_tr16(vb + voff[0][nb & 1]);
+            const bf16x4 hi = lds_read_tr16(vb + voff[1][nb & 1]);
+            oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
+          }
       }
-      lsum = alpha * lsum + psum;
-      lexact = alpha * lexact + pexact;
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) oacc[nb] *= alpha;
-      // O^T += V^T P^T; V is the first 512 columns of the latent tile
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) {
-        const bf16x4 lo = lds_read_tr16(tile + src_row * kStride + nb * 16 + src_col);
-        const bf16x4 hi = lds_read_tr16(tile + (16 + src_row) * kStride + nb * 16 + src_col);
-        oacc[nb] = mfma16x16x32(concat(lo, hi), pop, oacc[nb]);
+      if constexpr (FP8) {
+        if (it + 1 < ntiles) mla_store_fp8(tiles + (p ^ 1) * kTileB, tid, stage);
       }
     }
-
-    if (more) stage_store<FP8>(tiles + ((it + 1) & 1) * kTileElems, tid, stage);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    const int again = restart;
+    __syncthreads();                          // every wave has read the flag before it is cleared
+    if (!again || attempt == kMaxRestarts) break;
+    if (tid == 0) restart = 0;
   }
 
   // ---- epilogue: each wave writes its own rows ----
-  lsum += wave_shfl_xor(lsum, 16);
-  lsum += wave_shfl_xor(lsum, 32);
-  lexact += wave_shfl_xor(lexact, 16);
-  lexact += wave_shfl_xor(lexact, 32);
+  const float l = lsum;                        // already summed over the two halves
   if (!row_valid) return;
-  const float inv = (lsum > 0.f) ? a.kv_scale / lsum : 0.f;     // V dequantisation folded in
-  const float muse = (m == kNegInf) ? 0.f : m;
-  const float lse2 = (lexact > 0.f) ? muse + __log2f(lexact) : kNegInf;
+  const float inv = (l > 0.f) ? a.kv_scale / l : 0.f;     // V dequantisation folded in
+  const float muse = (anchor == kNegInf) ? 0.f : anchor;
+  const float lse2 = (l > 0.f) ? muse + __log2f(l) : kNegInf;
   if (a.num_splits == 1) {
-    __bf16 *dst = static_cast<__bf16 *>(a.o) + ridx * kDv + 4 * kg;
+    __bf16 *dst = static_cast<__bf16 *>(a.o) + ridx * kDv + 4 * half;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      bf16x4 ob;
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[nb][i] * inv);
-      *reinterpret_cast<u32x2 *>(dst + nb * 16) = __builtin_bit_cast(u32x2, ob);
-    }
-    if (a.lse && kg == 0) a.lse[ridx] = lse2;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ob;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[nb][4 * g + i] * inv);
+        *reinterpret_cast<u32x2 *>(dst + 32 * nb + 8 * g) = __builtin_bit_cast(u32x2, ob);
+      }
+    if (a.lse && half == 0) a.lse[ridx] = lse2;
   } else {
-    float *dst = a.o_parts + ((int64_t)split * R + ridx) * kDv + 4 * kg;
+    float *dst = a.o_parts + ((int64_t)split * R + ridx) * kDv + 4 * half;
 #pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) *reinterpret_cast<f32x4 *>(dst + nb * 16) = oacc[nb] * inv;
-    if (kg == 0) a.lse_parts[(int64_t)split * R + ridx] = lse2;
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = oacc[nb][4 * g + i] * inv;
+        *reinterpret_cast<f32x4 *>(dst + 32 * nb + 8 * g) = ov;
+      }
+    if (half == 0) a.lse_parts[(int64_t)split * R + ridx] = lse2;
   }
 }
 

@@ -93,6 +93,18 @@ __device__ __forceinline__ uint32_t lds_address(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
+// Max / sum of a value over the two 32-lane halves of a wave, in every lane
+// (v_permlane32_swap exchanges the halves).
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <class T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);

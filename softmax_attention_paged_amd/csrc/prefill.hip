@@ -56,17 +56,6 @@ __device__ __forceinline__ int pf_swz(int row) {
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-// max / sum over the two 32-lane halves, in every lane (v_permlane32_swap)
-__device__ __forceinline__ float half_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float half_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 struct PfUnit {
   int b, kvh, h0;              // request, KV head, first query head of the workgroup
   int gh, tq;                  // query heads and query tokens per workgroup
