@@ -56,6 +56,7 @@ constexpr int kChunks = kDk / 8;                   // 16-byte chunks per row
 constexpr int kTileB = kTileN * kRowB;             // bytes of one LDS tile
 constexpr int kKB = kDk / 16;                      // 36 QK k-steps
 constexpr int kKBReg = 18;                         // k-steps whose Q operand stays in registers
+constexpr int kRing = 4;                           // LDS operand reads in flight ahead of the MFMAs
 constexpr int kQRowB = (kDk - 16 * kKBReg) * 2 + 16;   // LDS bytes per row of the other Q columns (padded)
 constexpr int kNB = kDv / 32;                      // 16 PV channel blocks
 constexpr int kDma = kTileN * kChunks / 64 / kW;   // 9 direct loads per wave per bf16 tile
@@ -338,13 +339,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
       if (wave_active) {
         const char *tile = tiles + p * kTileB;
         // S^T: lane holds keys j0 + 8(i/4) + 4 half + i%4 of row r32
+        // Operands come from LDS kRing MFMAs ahead of use (one wave per SIMD:
+        // no other wave hides the LDS latency); the fences keep that order.
         f32x16 s = f32x16{};
+        {
+          auto kread = [&](int kb) { return *reinterpret_cast<const bf16x8 *>(tile + koff[kb & 3] + (kb >> 2) * 128); };
+          auto qread = [&](int kb) {
+            return (kb < kKBReg) ? qop[kb < kKBReg ? kb : 0]
+                                 : *reinterpret_cast<const bf16x8 *>(qsrc + (kb - kKBReg) * 32);
+          };
+          bf16x8 kr[kRing], qr[kRing];
 #pragma unroll
-        for (int kb = 0; kb < kKB; ++kb) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8 *>(tile + koff[kb & 3] + (kb >> 2) * 128);
-          const bf16x8 qv = (kb < kKBReg) ? qop[kb < kKBReg ? kb : 0]
-                                          : *reinterpret_cast<const bf16x8 *>(qsrc + (kb - kKBReg) * 32);
-          s = mfma32x32x16(kop, qv, s);
+          for (int i = 0; i < kRing; ++i) {
+            kr[i] = kread(i);
+            qr[i] = qread(i);
+          }
+#pragma unroll
+          for (int kb = 0; kb < kKB; ++kb) {
+            __builtin_amdgcn_sched_barrier(0);
+            s = mfma32x32x16(kr[kb % kRing], qr[kb % kRing], s);
+            if (kb + kRing < kKB) {
+              kr[kb % kRing] = kread(kb + kRing);
+              qr[kb % kRing] = qread(kb + kRing);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (j0 + kTileN > valid_min) {
 #pragma unroll
@@ -380,15 +399,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
           restart = 1;
         }
         // O^T += V^T P^T; V is the first 512 columns of the latent tile
+        {
+          // step t: k-step t / kNB (16 keys), channel block t % kNB
+          auto vread = [&](int t) {
+            const char *vb = tile + (t / kNB) * 16 * kRowB + ((t % kNB) >> 1) * 128;
+            return concat(lds_read_tr16(vb + voff[0][t & 1]), lds_read_tr16(vb + voff[1][t & 1]));
+          };
+          bf16x8 vr[kRing];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+          for (int i = 0; i < kRing; ++i) vr[i] = vread(i);
 #pragma unroll
-          for (int nb = 0; nb < kNB; ++nb) {
-            const char *vb = tile + kk * 16 * kRowB + (nb >> 1) * 128;
-            const bf16x4 lo = lds_read_tr16(vb + voff[0][nb & 1]);
-            const bf16x4 hi = lds_read_tr16(vb + voff[1][nb & 1]);
-            oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
+          for (int t = 0; t < 2 * kNB; ++t) {
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[t % kNB] = mfma32x32x16(vr[t % kRing], pop[t / kNB], oacc[t % kNB]);
+            if (t + kRing < 2 * kNB) vr[t % kRing] = vread(t + kRing);
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       if constexpr (FP8) {
         if (it + 1 < ntiles) mla_store_fp8(tiles + (p ^ 1) * kTileB, tid, stage);
