@@ -96,7 +96,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // Kernel geometry the planner needs.
 constexpr int kGqaRowsPerTile = 16;   // MFMA N rows of the GQA decode kernel
 constexpr int kGqaTileTokens = 32;    // keys per wave iteration
-constexpr int kGqaWaves = 4;           // waves per workgroup
+
 constexpr int kMlaRows = 128;         // folded rows of the MLA decode kernel
 constexpr int kMlaTileTokens = 32;
 constexpr int kMaxSplits = 256;

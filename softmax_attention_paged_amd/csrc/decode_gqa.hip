@@ -29,12 +29,12 @@
 // partials (O normalised over the split, LSE of the split) that the merge
 // kernel reduces ("TokenSpeed-MLA", section "Decode performance").
 //
-// A workgroup is one unit; its 4 waves take the split's tiles in turn and
-// are combined by log-sum-exp in LDS at the end. Workgroups are numbered
-// with the query group, then the KV head, fastest: the units that read the
-// per-head slices of the same token rows ([page, slot, head, dim] stores a
-// token's heads side by side) are dispatched together, which keeps HBM
-// accesses row-local.
+// A workgroup is one wave and one unit: it walks its split's tiles in order
+// and writes its rows itself (no cross-wave merge; a finished wave frees
+// its slot at once). Workgroups are numbered with the query group, then the
+// KV head, fastest: the units that read the per-head slices of the same
+// token rows ([page, slot, head, dim] stores a token's heads side by side)
+// are dispatched together, which keeps HBM accesses row-local.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -51,6 +51,9 @@ struct GqaGeom {
   static constexpr int kVTile = kTile * kVStride;               // bf16 elements per wave
   static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per V row
   static constexpr int kVChunks = kTile * kChunksPerRow / 64;   // 16-byte chunks per lane per V tile
+  // waves per SIMD the registers are budgeted for: more waves keep more
+  // K/V loads in flight per CU (D = 128 fits 3 in 167 VGPRs without spills)
+  static constexpr int kWPE = D <= 64 ? 4 : (D <= 128 ? 3 : 1);
 };
 
 // Gather one 32-key tile of K (MFMA A layout) or V (linear 16-byte chunks).
@@ -60,10 +63,15 @@ struct TilePages {
   int64_t p0, p1;   // physical pages of keys tok0..tok0+15 and tok0+16..tok0+31
 };
 
+// Table entries of the tile at tok0 (tok0 < end), read with scalar loads:
+// the table is read-only here, and waiting for a scalar load does not wait
+// for the vector-memory K/V loads in flight.
 __device__ __forceinline__ TilePages tile_pages(const DecodeGqaArgs &a, const int32_t *bt_row, int tok0, int end) {
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const const_i32 *bt = reinterpret_cast<const const_i32 *>(reinterpret_cast<uintptr_t>(bt_row));
   TilePages tp;
-  tp.p0 = bt_row[tok0 >> a.page_shift];
-  tp.p1 = (tok0 + 16 < end) ? (int64_t)bt_row[(tok0 + 16) >> a.page_shift] : tp.p0;
+  tp.p0 = bt[tok0 >> a.page_shift];
+  tp.p1 = (tok0 + 16 < end) ? (int64_t)bt[(tok0 + 16) >> a.page_shift] : tp.p0;
   return tp;
 }
 
@@ -172,11 +180,12 @@ struct WaveState {
     TilePages tp = tile_pages(a, bt_row, first, u.c1);
     load_k<D>(a, kbase, tp, first, lane, kr);
     load_v<D>(a, vbase, tp, first, u.c1, lane, vr);
+    // table entries of the next tile, fetched one iteration before its loads
+    TilePages tn = tp;
+    if (first + stride < u.c1) tn = tile_pages(a, bt_row, first + stride, u.c1);
     for (int tok0 = first; tok0 < u.c1; tok0 += stride) {
       const int nxt = tok0 + stride;
       const bool more = nxt < u.c1;
-      TilePages tn = tp;
-      if (more) tn = tile_pages(a, bt_row, nxt, u.c1);
       // S^T tiles: sacc[0] keys tok0 + 4kg + i, sacc[1] keys tok0 + 16 + 4kg + i.
       f32x4 sacc[2];
 #pragma unroll
@@ -193,7 +202,7 @@ struct WaveState {
         store_bf16x8_lds(vlds + (idx / G::kChunksPerRow) * G::kVStride + (idx % G::kChunksPerRow) * 8, vr[c]);
       }
       if (more) load_v<D>(a, vbase, tn, nxt, u.c1, lane, vr);
-      tp = tn;
+      if (nxt + stride < u.c1) tn = tile_pages(a, bt_row, nxt + stride, u.c1);
       float x[8];
       float mx = kNegInf;
 #pragma unroll
@@ -268,24 +277,17 @@ __device__ __forceinline__ void write_empty(const DecodeGqaArgs &a, const UnitRo
   }
 }
 
-// blockIdx -> (b, split, KV head, q group), q group fastest; 4 waves share the split.
+// One wave per workgroup and per unit: blockIdx -> (b, split, KV head, q
+// group), q group fastest, so the units that read the per-head slices of
+// the same token rows are dispatched together. The wave walks its split's
+// tiles in order and writes its rows itself: no cross-wave merge, and a
+// finished wave frees its slot at once.
 template <int D>
-struct TokensLds {
-  static constexpr int kWaves = kGqaWaves;
-  static constexpr int kV = kWaves * GqaGeom<D>::kVTile * 2;
-  static constexpr int kMerge = kWaves * 16 * 4 * 3 + kWaves * 16 * D * 4;
-  static constexpr int kBytes = kV > kMerge ? kV : kMerge;
-};
-
-template <int D>
-__global__ __launch_bounds__(64 * kGqaWaves) void decode_gqa_tokens_kernel(const DecodeGqaArgs a) {
+__global__ __launch_bounds__(64, GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(const DecodeGqaArgs a) {
   using G = GqaGeom<D>;
-  constexpr int kWaves = kGqaWaves;
-  __shared__ __attribute__((aligned(16))) char smem[TokensLds<D>::kBytes];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) __bf16 vlds[G::kVTile];
+  const int lane = threadIdx.x;
   const int kg = lane >> 4;
-  const int row = lane & 15;
   int unit = blockIdx.x;
   const int qg = unit % a.q_groups;
   unit /= a.q_groups;
@@ -294,90 +296,44 @@ __global__ __launch_bounds__(64 * kGqaWaves) void decode_gqa_tokens_kernel(const
   const int split = unit % a.num_splits;
   const int b = unit / a.num_splits;
   const UnitRows u = unit_rows(a, b, kvh, qg, split, lane);
-  if (u.c0 >= u.c1) {   // uniform over the workgroup
-    if (wave == 0) write_empty<D>(a, u, lane);
+  if (u.c0 >= u.c1) {
+    write_empty<D>(a, u, lane);
     return;
   }
   WaveState<D> st;
   st.init(a, u, lane);
-  st.walk(a, u, u.c0 + wave * G::kTile, kWaves * G::kTile,
-          reinterpret_cast<__bf16 *>(smem) + wave * G::kVTile, lane);
+  st.walk(a, u, u.c0, G::kTile, vlds, lane);
   st.reduce_sums();
+  if (!u.row_valid) return;
 
-  // combine the waves by log-sum-exp
-  __syncthreads();  // every wave is done with its V tile region
-  float *sm_m = reinterpret_cast<float *>(smem);
-  float *sm_l = sm_m + kWaves * 16;
-  float *sm_le = sm_l + kWaves * 16;
-  float *sm_o = sm_le + kWaves * 16;
-  if (kg == 0) {
-    sm_m[wave * 16 + row] = st.m;
-    sm_l[wave * 16 + row] = st.lsum;
-    sm_le[wave * 16 + row] = st.lexact;
-  }
+  // lane holds O[row][16 nb + 4 kg + i]; the rounded-P sum normalises O,
+  // the exact sum gives the LSE
+  const float inv = (st.lsum > 0.f) ? 1.f / st.lsum : 0.f;
+  const float muse = (st.m == kNegInf) ? 0.f : st.m;
+  const float lse2 = (st.lexact > 0.f) ? muse + __log2f(st.lexact) : kNegInf;
+  if (a.num_splits == 1) {
+    __bf16 *dst = static_cast<__bf16 *>(a.o) + u.ridx * D + 4 * kg;
 #pragma unroll
-  for (int nb = 0; nb < G::kNB; ++nb)
-    *reinterpret_cast<f32x4 *>(sm_o + (wave * 16 + row) * D + nb * 16 + 4 * kg) = st.oacc[nb];
-  __syncthreads();
-
-  const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
-  for (int ch = threadIdx.x; ch < 16 * G::kChunksPerRow; ch += 64 * kWaves) {
-    const int r = ch / G::kChunksPerRow;
-    if (r >= a.rows) continue;
-    const int c8 = (ch % G::kChunksPerRow) * 8;
-    float mw[kWaves];
-    float mmax = kNegInf;
+    for (int nb = 0; nb < G::kNB; ++nb) {
+      bf16x4 ob;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      mw[w] = sm_m[w * 16 + r];
-      mmax = fmaxf(mmax, mw[w]);
+      for (int i = 0; i < 4; ++i) ob[i] = to_bf16(st.oacc[nb][i] * inv);
+      *reinterpret_cast<u32x2 *>(dst + nb * 16) = __builtin_bit_cast(u32x2, ob);
     }
-    const float muse = (mmax == kNegInf) ? 0.f : mmax;
-    float f[kWaves];
-    float L = 0.f, Le = 0.f;
+    if (a.lse && kg == 0) a.lse[u.ridx] = lse2;
+  } else {
+    const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
+    float *dst = a.o_parts + ((int64_t)split * R + u.ridx) * D + 4 * kg;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      f[w] = exp2_fast(mw[w] - muse);
-      L += f[w] * sm_l[w * 16 + r];
-      Le += f[w] * sm_le[w * 16 + r];
-    }
-    const float inv = (L > 0.f) ? 1.f / L : 0.f;
-    float out[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const f32x4 lo = *reinterpret_cast<const f32x4 *>(sm_o + (w * 16 + r) * D + c8);
-      const f32x4 hi = *reinterpret_cast<const f32x4 *>(sm_o + (w * 16 + r) * D + c8 + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        out[e] += f[w] * lo[e];
-        out[4 + e] += f[w] * hi[e];
-      }
-    }
-    const int t = qg * a.fold + r / a.group;
-    const int h = kvh * a.group + r % a.group;
-    const int64_t ri = ((int64_t)b * a.q_len + t) * a.num_q_heads + h;
-    const float lse2 = (Le > 0.f) ? muse + __log2f(Le) : kNegInf;
-    if (a.num_splits == 1) {
-      bf16x8 ob;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ob[e] = to_bf16(out[e] * inv);
-      *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(a.o) + ri * D + c8) = __builtin_bit_cast(u32x4, ob);
-      if (a.lse && c8 == 0) a.lse[ri] = lse2;
-    } else {
-      float *dst = a.o_parts + ((int64_t)split * R + ri) * D + c8;
-      *reinterpret_cast<f32x4 *>(dst) = f32x4{out[0] * inv, out[1] * inv, out[2] * inv, out[3] * inv};
-      *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{out[4] * inv, out[5] * inv, out[6] * inv, out[7] * inv};
-      if (c8 == 0) a.lse_parts[(int64_t)split * R + ri] = lse2;
-    }
+    for (int nb = 0; nb < G::kNB; ++nb) *reinterpret_cast<f32x4 *>(dst + nb * 16) = st.oacc[nb] * inv;
+    if (kg == 0) a.lse_parts[(int64_t)split * R + u.ridx] = lse2;
   }
 }
 
 template <int D>
 hipError_t launch_d(const DecodeGqaArgs &a, hipStream_t stream) {
   const int64_t units = (int64_t)a.batch * a.num_splits * a.num_kv_heads * a.q_groups;
-  hipLaunchKernelGGL(decode_gqa_tokens_kernel<D>, dim3((unsigned)units), dim3(64 * kGqaWaves), 0, stream, a);
+  hipLaunchKernelGGL(decode_gqa_wave_kernel<D>, dim3((unsigned)units), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -8,9 +8,12 @@
 // partial results; section "FP8 split-KV partial storage": combine normalised
 // FP32 partials).
 //
-// One wave per row: the lanes read the split LSEs once, reduce M and the
-// weights with wave shuffles, then stream the non-empty partial rows with
-// 16-byte loads. Splits with lse = -inf are never read.
+// One wave per row: the lanes read the split LSEs once and reduce M and the
+// weights with wave shuffles. The row's float4 chunks are spread over the
+// lanes; when they do not fill the wave, lane groups take every G-th split
+// and are summed with shuffles at the end. Within a group, partial rows are
+// read four splits at a time so their loads are in flight together. Splits
+// with weight 0 (lse = -inf, an empty split) are never read.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -20,6 +23,7 @@ namespace {
 
 constexpr int kMergeWaves = 4;
 constexpr int kMaxChunksPerLane = 4;   // float4 chunks: head_dim_v <= 1024
+constexpr int kBatch = 4;              // partial rows read together
 
 __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
   const int lane = threadIdx.x & 63;
@@ -47,36 +51,65 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += wave_shfl_xor(wsum, off);
 
+  // lane layout: G groups of 64 / G lanes; group g sums splits g, g + G, ...
   const int nchunks = a.head_dim_v >> 2;
+  const int G = nchunks >= 64 ? 1 : (nchunks >= 32 ? 2 : 4);
+  const int glanes = 64 / G;
+  const int g = lane / glanes, gl = lane % glanes;
   f32x4 acc[kMaxChunksPerLane];
 #pragma unroll
   for (int k = 0; k < kMaxChunksPerLane; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s = 0; s < a.num_splits; ++s) {
-    const float w = __shfl(lse_r[s >> 6], s & 63, 64);
-    if (w == 0.f) continue;   // uniform: empty (or negligible) split, not read
-    const float *src = a.o_parts + ((int64_t)s * a.num_rows + rowi) * a.head_dim_v;
+  for (int s0 = 0; s0 < a.num_splits; s0 += kBatch * G) {
+    float w[kBatch];
+    f32x4 v[kBatch][kMaxChunksPerLane];
 #pragma unroll
-    for (int k = 0; k < kMaxChunksPerLane; ++k) {
-      const int c = lane + 64 * k;
-      if (c < nchunks) acc[k] += w * *reinterpret_cast<const f32x4 *>(src + 4 * c);
+    for (int u = 0; u < kBatch; ++u) {
+      const int sg = s0 + u * G;            // this batch slot's split for group 0; group g adds g
+      float wu = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {         // the weight of split sg + g, from its lane
+        const int sq = sg + q;
+        const float wq = (sq < a.num_splits) ? __shfl(lse_r[(sq >> 6) & (kMaxSplits / 64 - 1)], sq & 63, 64) : 0.f;
+        if (q == g) wu = wq;
+      }
+      w[u] = wu;
+      const int s = sg + g;
+      const float *src = a.o_parts + ((int64_t)s * a.num_rows + rowi) * a.head_dim_v;
+#pragma unroll
+      for (int k = 0; k < kMaxChunksPerLane; ++k) {
+        const int c = gl + glanes * k;
+        v[u][k] = (wu != 0.f && c < nchunks) ? *reinterpret_cast<const f32x4 *>(src + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int k = 0; k < kMaxChunksPerLane; ++k) acc[k] += w[u] * v[u][k];
   }
+  // sum the lane groups (lanes gl, gl + glanes, ... hold the same chunks)
+  for (int off = glanes; off < 64; off <<= 1)
+#pragma unroll
+    for (int k = 0; k < kMaxChunksPerLane; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[k][e] += wave_shfl_xor(acc[k][e], off);
 
   const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
+  if (g == 0) {
 #pragma unroll
-  for (int k = 0; k < kMaxChunksPerLane; ++k) {
-    const int c = lane + 64 * k;
-    if (c >= nchunks) continue;
-    const f32x4 r = acc[k] * inv;
-    if (a.o_bf16) {
-      bf16x4 ob;
+    for (int k = 0; k < kMaxChunksPerLane; ++k) {
+      const int c = gl + glanes * k;
+      if (c >= nchunks) continue;
+      const f32x4 r = acc[k] * inv;
+      if (a.o_bf16) {
+        bf16x4 ob;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ob[e] = to_bf16(r[e]);
-      *reinterpret_cast<u32x2 *>(static_cast<__bf16 *>(a.o) + rowi * a.head_dim_v + 4 * c) =
-          __builtin_bit_cast(u32x2, ob);
-    } else {
-      *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + rowi * a.head_dim_v + 4 * c) = r;
+        for (int e = 0; e < 4; ++e) ob[e] = to_bf16(r[e]);
+        *reinterpret_cast<u32x2 *>(static_cast<__bf16 *>(a.o) + rowi * a.head_dim_v + 4 * c) =
+            __builtin_bit_cast(u32x2, ob);
+      } else {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.o) + rowi * a.head_dim_v + 4 * c) = r;
+      }
     }
   }
   if (a.lse && lane == 0) a.lse[rowi] = (wsum > 0.f) ? muse + __log2f(wsum) : kNegInf;
