@@ -10,10 +10,12 @@
 // A wave walks 32-key tiles of its unit and keeps a running max m, sums l
 // and output o per row (the online recurrence of "Flywheel Attention",
 // section 1, and "Writing Page Attention with PyPTO", section 6.3). Per tile:
-//   - K rows are gathered through the block table straight into registers,
-//     already in the MFMA A-operand layout (token = l % 16, 8 channels per
-//     lane); the page of a 16-key half-tile is one table entry (pages hold a
-//     power of two >= 16 keys), read once.
+//   - K and V rows are gathered through the block table into registers with
+//     full-row loads (16 lanes per 256-byte row slice), one tile ahead; the
+//     page of a 16-key half-tile is one table entry (pages hold a power of
+//     two >= 16 keys), read once. K goes through the wave's LDS tile to the
+//     MFMA A-operand layout (token = l % 16, 8 channels per lane), then V
+//     takes the same tile.
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16, so each lane ends up holding
 //     8 scores of ONE row (l % 16): the softmax state is lane-local.
 //   - Invalid keys (past the split, past the request, or above the causal
@@ -75,18 +77,23 @@ __device__ __forceinline__ TilePages tile_pages(const DecodeGqaArgs &a, const in
   return tp;
 }
 
+// K rows in the same coalesced pattern as V (16 lanes cover a 256-byte row
+// slice): loading straight into the MFMA operand layout would make every
+// load instruction touch 16 rows x 64 bytes (half lines), which costs a
+// third of the read bandwidth; the operand layout is read back from LDS.
 template <int D>
 __device__ __forceinline__ void load_k(const DecodeGqaArgs &a, const __bf16 *kbase, const TilePages &tp,
-                                       int tok0, int lane, bf16x8 (&k)[2][GqaGeom<D>::kKB]) {
+                                       int tok0, int lane, bf16x8 (&k)[GqaGeom<D>::kVChunks]) {
   using G = GqaGeom<D>;
   const int pmask = (1 << a.page_shift) - 1;
-  const int kg = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tok = tok0 + 16 * t + (lane & 15);
-    const __bf16 *row = kbase + (t ? tp.p1 : tp.p0) * a.k_stride_page + (int64_t)(tok & pmask) * a.k_stride_tok;
-#pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) k[t][kb] = load_bf16x8(row + kb * 32 + kg * 8);
+  for (int c = 0; c < G::kVChunks; ++c) {
+    const int idx = c * 64 + lane;
+    const int trow = idx / G::kChunksPerRow;
+    const int col = (idx % G::kChunksPerRow) * 8;
+    const int tok = tok0 + trow;
+    const __bf16 *row = kbase + (trow >= 16 ? tp.p1 : tp.p0) * a.k_stride_page + (int64_t)(tok & pmask) * a.k_stride_tok;
+    k[c] = load_bf16x8(row + col);   // keys past the end are masked before use
   }
 }
 
@@ -175,7 +182,7 @@ struct WaveState {
     const __bf16 *kbase = static_cast<const __bf16 *>(a.k_cache) + (int64_t)u.kvh * a.k_stride_head;
     const __bf16 *vbase = static_cast<const __bf16 *>(a.v_cache) + (int64_t)u.kvh * a.v_stride_head;
     if (first >= u.c1) return;
-    bf16x8 kr[2][G::kKB];
+    bf16x8 kr[G::kVChunks];
     bf16x8 vr[G::kVChunks];
     TilePages tp = tile_pages(a, bt_row, first, u.c1);
     load_k<D>(a, kbase, tp, first, lane, kr);
@@ -186,16 +193,28 @@ struct WaveState {
     for (int tok0 = first; tok0 < u.c1; tok0 += stride) {
       const int nxt = tok0 + stride;
       const bool more = nxt < u.c1;
+      // K tile -> the wave's LDS tile (token-major, padded rows), read back
+      // in the MFMA A layout (token = l % 16, 8 channels per lane). LDS
+      // operations of one wave execute in order, so the V rows written
+      // into the same tile below land after these reads.
+#pragma unroll
+      for (int c = 0; c < G::kVChunks; ++c) {
+        const int idx = c * 64 + lane;
+        store_bf16x8_lds(vlds + (idx / G::kChunksPerRow) * G::kVStride + (idx % G::kChunksPerRow) * 8, kr[c]);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (more) load_k<D>(a, kbase, tn, nxt, lane, kr);
       // S^T tiles: sacc[0] keys tok0 + 4kg + i, sacc[1] keys tok0 + 16 + 4kg + i.
       f32x4 sacc[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const __bf16 *krow = vlds + (16 * t + row) * G::kVStride + kg * 8;
 #pragma unroll
-        for (int kb = 0; kb < G::kKB; ++kb) sacc[t] = mfma16x16x32(kr[t][kb], qop[kb], sacc[t]);
+        for (int kb = 0; kb < G::kKB; ++kb)
+          sacc[t] = mfma16x16x32(*reinterpret_cast<const bf16x8 *>(krow + kb * 32), qop[kb], sacc[t]);
       }
-      if (more) load_k<D>(a, kbase, tn, nxt, lane, kr);
-      // V tile -> LDS (token-major), for the transposing read.
+      // V tile -> the same LDS tile, for the transposing read.
 #pragma unroll
       for (int c = 0; c < G::kVChunks; ++c) {
         const int idx = c * 64 + lane;
