@@ -69,3 +69,28 @@ def test_mla_decode_80k_sampled(kv_dtype, causal):
     got = np.stack([f64(out[b, t, h]) for b, t, h in rows])
     gl = np.array([float(lse[b, t, h]) for b, t, h in rows])
     print(compare(got, ref, gl, lref, TOL_BF16 if kv_dtype == "bf16" else TOL_FP8))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_static_anchor_restart(kv_dtype, splits):
+    """One latent row gives the row (token 0, head 0) a score of about 150-175
+    log2 units, about 145 above its first tile's max: without a restart its
+    exponential would overflow FP32. The running-sum check fails, the split
+    restarts with a raised anchor, and the result matches the oracle. bf16:
+    the large values sit in the 64 rope columns (K only, so V and the output
+    keep their usual size); fp8: the whole row is 3 x the query, clamped to
+    the e4m3 range."""
+    case = inputs.decode_case(batch=2, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
+                              seq_lens=[700, 300], seed=71, kv_dtype=kv_dtype, latent=True,
+                              scale=0.07216882, causal=True, layout="random")
+    j = 500                                            # logical key of request 0
+    page = int(case.block_table[0, j // 64])
+    q00 = case.q[0, 0, 0].float()
+    if kv_dtype == "bf16":
+        case.k_cache[page, j % 64, 0, 512:] = (28.0 * q00[512:]).to(torch.bfloat16)
+    else:
+        codes = (3.0 * q00 / case.kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        case.k_cache[page, j % 64, 0] = codes
+    res = _check(case, splits)
+    print(res)
