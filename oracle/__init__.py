@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     widen_e4m3fn,
     widen,
     attention_rows,
+    window_key_start,
     gather_paged_rows,
     decode_paged,
     decode_paged_rows,

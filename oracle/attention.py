@@ -27,6 +27,12 @@ Readings of the pages used here (each one is listed in the design notes):
     kernel capability summary).
   * A row that sees no key returns o = 0 and lse2 = -inf ("TokenSpeed-MLA",
     section "SM107 decode": rows with no visible keys).
+  * A sliding window (window_left >= 0) also bounds each row from below:
+    query row i of a block of Lq rows over Lk keys sees keys
+    j >= max(0, Lk - Lq - window_left + i), i.e. the whole block plus
+    window_left keys of context ("TokenSpeed-MLA", kernel capability
+    summary, window_left); -1 means the full history. The same bound is
+    applied to prefill rows, with Lq the request's query count.
   * Query head h reads KV head h // G with G = Hq / Hkv, i.e. consecutive
     query heads share a KV head ("Writing Page Attention with PyPTO",
     sections 1.2 and 1.3).
@@ -114,13 +120,24 @@ def causal_key_bound(i: np.ndarray | int, lq: int, lk: int) -> np.ndarray:
     return np.clip(np.asarray(i, dtype=np.int64) + (lk - lq) + 1, 0, lk)
 
 
+def window_key_start(i: np.ndarray | int, lq: int, lk: int, window_left: int) -> np.ndarray:
+    """First key query row i may see under a sliding window of window_left
+    keys of context: max(0, lk - lq - window_left + i); 0 when window_left
+    is -1 (full history)."""
+    i = np.asarray(i, dtype=np.int64)
+    if window_left < 0:
+        return np.zeros_like(i)
+    return np.maximum(0, i + (lk - lq - window_left))
+
+
 def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   key_bound: np.ndarray | None = None,
+                   key_bound: np.ndarray | None = None, key_start: np.ndarray | None = None,
                    row_group: int = 1024) -> tuple[np.ndarray, np.ndarray]:
     """Attention of R query rows over one key/value sequence.
 
     q: [R, Dqk], k: [Lk, Dqk], v: [Lk, Dv], all float64.
-    key_bound: [R] ints; row r sees keys 0 .. key_bound[r]-1 (default: all).
+    key_bound: [R] ints; row r sees keys key_start[r] .. key_bound[r]-1
+    (defaults: 0 and Lk).
     Returns o [R, Dv] and lse2 [R].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -130,6 +147,9 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     if key_bound is None:
         key_bound = np.full(r_total, lk, dtype=np.int64)
     key_bound = np.asarray(key_bound, dtype=np.int64)
+    if key_start is None:
+        key_start = np.zeros(r_total, dtype=np.int64)
+    key_start = np.asarray(key_start, dtype=np.int64)
     o = np.zeros((r_total, dv), dtype=np.float64)
     lse2 = np.full(r_total, NEG_INF, dtype=np.float64)
     if lk == 0 or r_total == 0:
@@ -138,8 +158,9 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     for r0 in range(0, r_total, row_group):
         r1 = min(r_total, r0 + row_group)
         s = scale * (q[r0:r1] @ k.T)                       # [rows, Lk]
-        s = np.where(cols[None, :] < key_bound[r0:r1, None], s, NEG_INF)
-        seen = key_bound[r0:r1] > 0
+        visible = (cols[None, :] < key_bound[r0:r1, None]) & (cols[None, :] >= key_start[r0:r1, None])
+        s = np.where(visible, s, NEG_INF)
+        seen = visible.any(axis=1)
         if not seen.any():
             continue
         s = s[seen]
@@ -181,7 +202,8 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                       block_table: np.ndarray, seq_lens: np.ndarray, page_size: int,
                       scale: float, causal: bool, head_dim_v: int,
                       rows: list[tuple[int, int, int]], kv_format: str = "f64",
-                      kv_scale: float = 1.0, q_format: str = "f64") -> tuple[np.ndarray, np.ndarray]:
+                      kv_scale: float = 1.0, q_format: str = "f64",
+                      window_left: int = -1) -> tuple[np.ndarray, np.ndarray]:
     """Decode attention for selected (batch, query token, query head) rows.
 
     q: [B, q_len, Hq, Dqk] float64; k_cache: [P, ps, Hkv, Dqk];
@@ -207,20 +229,22 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         qr = widen(np.stack([q[rows[n][0], rows[n][1], rows[n][2]] for n in members]), q_format)
         t = np.array([rows[n][1] for n in members], dtype=np.int64)
         bound = causal_key_bound(t, q_len, lk) if causal else np.full(len(members), lk)
-        o_m, l_m = attention_rows(qr, k, v, scale, bound)
+        start = window_key_start(t, q_len, lk, window_left)
+        o_m, l_m = attention_rows(qr, k, v, scale, bound, start)
         o[members] = o_m
         lse2[members] = l_m
     return o, lse2
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size, scale,
-                 causal, head_dim_v, kv_format="f64", kv_scale=1.0, q_format="f64"):
+                 causal, head_dim_v, kv_format="f64", kv_scale=1.0, q_format="f64", window_left=-1):
     """Decode attention for every row: returns o [B, q_len, Hq, Dv] and
     lse2 [B, q_len, Hq]."""
     b_n, q_len, hq, _ = q.shape
     rows = [(b, t, h) for b in range(b_n) for t in range(q_len) for h in range(hq)]
     o, lse2 = decode_paged_rows(q, k_cache, v_cache, block_table, seq_lens, page_size,
-                                scale, causal, head_dim_v, rows, kv_format, kv_scale, q_format)
+                                scale, causal, head_dim_v, rows, kv_format, kv_scale, q_format,
+                                window_left)
     return o.reshape(b_n, q_len, hq, head_dim_v), lse2.reshape(b_n, q_len, hq)
 
 
@@ -228,7 +252,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size, scale,
 # Prefill over ragged dense or paged KV.
 # ---------------------------------------------------------------------------
 
-def prefill_dense(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, causal):
+def prefill_dense(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, causal, window_left=-1):
     """Ragged prefill over packed dense K/V ("TokenSpeed-MLA", kernel capability
     summary: Q [sum q_lens, h_q, d_qk], K [sum kv_lens, h_k, d_qk],
     V [sum kv_lens, h_k, d_v]; the two packings may differ).
@@ -245,15 +269,17 @@ def prefill_dense(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, causal):
         k0, k1 = int(cu_seqlens_kv[b]), int(cu_seqlens_kv[b + 1])
         lq, lk = q1 - q0, k1 - k0
         bound = causal_key_bound(np.arange(lq), lq, lk) if causal else np.full(lq, lk)
+        start = window_key_start(np.arange(lq), lq, lk, window_left)
         for h in range(hq):
             g = h // group
             o[q0:q1, h], lse2[q0:q1, h] = attention_rows(
-                q[q0:q1, h], k[k0:k1, g], v[k0:k1, g], scale, bound)
+                q[q0:q1, h], k[k0:k1, g], v[k0:k1, g], scale, bound, start)
     return o, lse2
 
 
 def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
-                       page_size, scale, causal, head_dim_v, rows, kv_format="f64", q_format="f64"):
+                       page_size, scale, causal, head_dim_v, rows, kv_format="f64", q_format="f64",
+                       window_left=-1):
     """Ragged prefill over a paged cache for selected (query token, head) rows,
     where the query token index is global in the packed Q. Caches hold values
     or raw bf16 bits (kv_format "bf16"), widened after gathering."""
@@ -275,21 +301,22 @@ def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_tab
         qr = widen(np.stack([q[rows[n][0], rows[n][1]] for n in members]), q_format)
         i = np.array([rows[n][0] - cu[b] for n in members], dtype=np.int64)
         bound = causal_key_bound(i, lq, lk) if causal else np.full(len(members), lk)
-        o_m, l_m = attention_rows(qr, k, v, scale, bound)
+        start = window_key_start(i, lq, lk, window_left)
+        o_m, l_m = attention_rows(qr, k, v, scale, bound, start)
         o[members] = o_m
         lse2[members] = l_m
     return o, lse2
 
 
 def prefill_paged(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
-                  page_size, scale, causal, head_dim_v, kv_format="f64", q_format="f64"):
+                  page_size, scale, causal, head_dim_v, kv_format="f64", q_format="f64", window_left=-1):
     """Ragged prefill over a paged cache for every row: o [Tq, Hq, Dv],
     lse2 [Tq, Hq]."""
     tq, hq, _ = q.shape
     rows = [(t, h) for t in range(tq) for h in range(hq)]
     o, lse2 = prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv,
                                  block_table, page_size, scale, causal, head_dim_v, rows, kv_format,
-                                 q_format)
+                                 q_format, window_left)
     return o.reshape(tq, hq, head_dim_v), lse2.reshape(tq, hq)
 
 

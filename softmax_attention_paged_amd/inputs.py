@@ -178,6 +178,8 @@ class DecodeCase:
     kv_scale: float                 # dequantisation scale (1.0 for bf16)
     max_seq_len: int
     seed: int
+    window_left: int = -1           # sliding window of context keys; -1: full history
+    packed_q: bool = False          # continuous (token * H + head) row packing
 
     @property
     def latent(self) -> bool:
@@ -202,7 +204,8 @@ def decode_case(*, batch: int, q_len: int, hq: int, hkv: int, d: int, dv: int, p
                 seq_lens=None, seq_len_range=None, seed: int, layout: str = "random",
                 pool_pages: int | None = None, max_pages: int | None = None, kv_dtype: str = "bf16",
                 latent: bool = False, scale: float | None = None, causal: bool = False,
-                q_mult: float = 1.0, shared_prefix_pages: int = 0, name: str = "") -> DecodeCase:
+                q_mult: float = 1.0, shared_prefix_pages: int = 0, name: str = "",
+                window_left: int = -1, packed_q: bool = False) -> DecodeCase:
     s_layout, s_q, s_k, s_v = _streams(seed)
     rng = np.random.Generator(np.random.PCG64(s_layout))
     if seq_lens is None:
@@ -238,7 +241,8 @@ def decode_case(*, batch: int, q_len: int, hq: int, hkv: int, d: int, dv: int, p
     return DecodeCase(name=name, q=q, k_cache=kc, v_cache=vc, block_table=lay.block_table,
                       seq_lens=torch.tensor(seq_lens, dtype=torch.int32), page_size=page_size,
                       head_dim_v=dv, scale=float(scale), causal=causal, kv_dtype=kv_dtype,
-                      kv_scale=kv_scale, max_seq_len=max(seq_lens, default=0), seed=seed)
+                      kv_scale=kv_scale, max_seq_len=max(seq_lens, default=0), seed=seed,
+                      window_left=window_left, packed_q=packed_q)
 
 
 # --------------------------------------------------------------------------
@@ -261,6 +265,7 @@ class PrefillCase:
     max_seqlen_q: int
     max_seqlen_kv: int
     seed: int
+    window_left: int = -1            # sliding window of context keys; -1: full history
 
     @property
     def paged(self) -> bool:
@@ -276,7 +281,7 @@ class PrefillCase:
 def prefill_case(*, q_lens: list[int], kv_lens: list[int], hq: int, hkv: int, d: int, seed: int,
                  causal: bool = True, paged: bool = False, page_size: int = 64, layout: str = "random",
                  pool_pages: int | None = None, scale: float | None = None, q_mult: float = 1.0,
-                 name: str = "") -> PrefillCase:
+                 name: str = "", window_left: int = -1) -> PrefillCase:
     s_layout, s_q, s_k, s_v = _streams(seed)
     rng = np.random.Generator(np.random.PCG64(s_layout))
     lay = make_layout(rng, kv_lens, page_size, layout, pool_pages) if paged else None
@@ -295,7 +300,7 @@ def prefill_case(*, q_lens: list[int], kv_lens: list[int], hq: int, hkv: int, d:
                        seq_lens_kv=torch.tensor(kv_lens, dtype=torch.int32), block_table=bt,
                        page_size=page_size, scale=float(scale if scale is not None else 1.0 / math.sqrt(d)),
                        causal=causal, max_seqlen_q=max(q_lens, default=0), max_seqlen_kv=max(kv_lens, default=0),
-                       seed=seed)
+                       seed=seed, window_left=window_left)
 
 
 # --------------------------------------------------------------------------

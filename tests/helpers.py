@@ -50,17 +50,19 @@ def oracle_decode(case, rows=None):
     vc = kc if case.v_cache is None else bits(case.v_cache)
     bt = case.block_table.numpy()
     sl = case.seq_lens.numpy()
+    w = getattr(case, "window_left", -1)
     if rows is None:
         return oracle.decode_paged(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal, case.head_dim_v,
-                                   fmt, case.kv_scale, "bf16")
+                                   fmt, case.kv_scale, "bf16", w)
     return oracle.decode_paged_rows(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal,
-                                    case.head_dim_v, rows, fmt, case.kv_scale, "bf16")
+                                    case.head_dim_v, rows, fmt, case.kv_scale, "bf16", w)
 
 
 def oracle_prefill(case, rows=None):
     """Oracle output for a PrefillCase: full ([Tq,H,Dv], [Tq,H]) or, with
     rows=[(token, head)...], ([n,Dv], [n])."""
     q = bits(case.q)
+    w = getattr(case, "window_left", -1)
     if case.paged:
         k, v = bits(case.k), bits(case.v)
         bt = case.block_table.numpy()
@@ -68,14 +70,14 @@ def oracle_prefill(case, rows=None):
         cu = case.cu_seqlens_q.numpy()
         if rows is None:
             return oracle.prefill_paged(q, k, v, cu, sl, bt, case.page_size, case.scale, case.causal,
-                                        v.shape[-1], "bf16", "bf16")
+                                        v.shape[-1], "bf16", "bf16", w)
         return oracle.prefill_paged_rows(q, k, v, cu, sl, bt, case.page_size, case.scale, case.causal,
-                                         v.shape[-1], rows, "bf16", "bf16")
+                                         v.shape[-1], rows, "bf16", "bf16", w)
     cu_q = case.cu_seqlens_q.numpy()
     cu_k = case.cu_seqlens_kv.numpy()
     if rows is None:
         return oracle.prefill_dense(oracle.widen_bf16(q), f64(case.k), f64(case.v), cu_q, cu_k, case.scale,
-                                    case.causal)
+                                    case.causal, w)
     # sampled rows of a dense case: widen only the (request, KV head) slices used
     kb, vb = bits(case.k), bits(case.v)
     hq, hkv = q.shape[1], kb.shape[1]
@@ -94,7 +96,8 @@ def oracle_prefill(case, rows=None):
         qr = oracle.widen_bf16(np.stack([q[rows[n][0], rows[n][1]] for n in members]))
         i = np.array([rows[n][0] - cu_q[b] for n in members])
         bound = oracle.attention.causal_key_bound(i, lq, lk) if case.causal else np.full(len(members), lk)
-        on, ln = oracle.attention_rows(qr, k, v, case.scale, bound)
+        start = oracle.window_key_start(i, lq, lk, w)
+        on, ln = oracle.attention_rows(qr, k, v, case.scale, bound, start)
         o[members], lse[members] = on, ln
     return o, lse
 

@@ -162,6 +162,84 @@ def test_rows_without_keys_are_zero_and_neg_inf():
     assert np.all(o0 == 0) and np.all(np.isneginf(l0))
 
 
+# ------------------------------------------------------------ sliding window --
+# "TokenSpeed-MLA", kernel capability summary, window_left: row i of a block
+# of q_len rows over K keys sees keys from max(0, K - q_len - window_left + i)
+# up to its causal bound -- the whole block plus window_left keys of context.
+
+def test_window_zero_leaves_the_diagonal_key_only():
+    # causal with no context: each row sees exactly its own key j = K - q_len + i,
+    # so o = v_j and lse2 = scale * <q, k_j> / ln 2
+    r = _rng(31)
+    lq, lk, scale = 4, 19, 0.37
+    q, k, v = r.standard_normal((lq, 6)), r.standard_normal((lk, 6)), r.standard_normal((lk, 5))
+    i = np.arange(lq)
+    bound = oracle.attention.causal_key_bound(i, lq, lk)
+    start = oracle.window_key_start(i, lq, lk, 0)
+    o, lse2 = oracle.attention_rows(q, k, v, scale, bound, start)
+    for row in range(lq):
+        j = lk - lq + row
+        assert np.max(np.abs(o[row] - v[j])) < 1e-14
+        assert abs(lse2[row] - scale * float(q[row] @ k[j]) / math.log(2.0)) < 1e-13
+
+
+def test_window_visible_keys_are_block_plus_context():
+    # one-hot V turns o into the softmax weights: the nonzero columns are the
+    # keys each row sees. With causal and window W: W + 1 keys per row, and
+    # the block's rows together see its q_len keys plus W keys of context.
+    r = _rng(32)
+    lq, lk, w = 4, 40, 9
+    q, k = r.standard_normal((lq, 8)) * 0.1, r.standard_normal((lk, 8))
+    i = np.arange(lq)
+    o, _ = oracle.attention_rows(q, k, np.eye(lk), 0.5, oracle.attention.causal_key_bound(i, lq, lk),
+                                 oracle.window_key_start(i, lq, lk, w))
+    seen = [set(np.nonzero(o[row] > 0)[0].tolist()) for row in range(lq)]
+    assert all(len(sv) == w + 1 for sv in seen)
+    assert set().union(*seen) == set(range(lk - lq - w, lk))
+    assert all(max(sv) == lk - lq + row for row, sv in enumerate(seen))
+
+
+def test_window_wider_than_history_is_full_history():
+    r = _rng(33)
+    lq, lk = 3, 12
+    q, k, v = r.standard_normal((lq, 4)), r.standard_normal((lk, 4)), r.standard_normal((lk, 4))
+    i = np.arange(lq)
+    bound = oracle.attention.causal_key_bound(i, lq, lk)
+    o_w, l_w = oracle.attention_rows(q, k, v, 0.8, bound, oracle.window_key_start(i, lq, lk, lk + 5))
+    o_f, l_f = oracle.attention_rows(q, k, v, 0.8, bound)
+    assert np.max(np.abs(o_w - o_f)) < 1e-14 and np.max(np.abs(l_w - l_f)) < 1e-14
+    assert np.all(oracle.window_key_start(i, lq, lk, -1) == 0)
+
+
+def test_window_row_equals_attention_over_its_key_slice():
+    # a windowed row is unwindowed attention over the keys it may see
+    r = _rng(34)
+    lq, lk, w = 5, 30, 7
+    q, k, v = r.standard_normal((lq, 6)), r.standard_normal((lk, 6)), r.standard_normal((lk, 3))
+    i = np.arange(lq)
+    o, lse2 = oracle.attention_rows(q, k, v, 0.4, oracle.attention.causal_key_bound(i, lq, lk),
+                                    oracle.window_key_start(i, lq, lk, w))
+    for row in range(lq):
+        a, b = lk - lq - w + row, lk - lq + row + 1
+        o1, l1 = oracle.attention_rows(q[row:row + 1], k[a:b], v[a:b], 0.4)
+        assert np.max(np.abs(o[row] - o1[0])) < 1e-13 and abs(lse2[row] - l1[0]) < 1e-13
+
+
+def test_decode_window_matches_prefill_window_on_the_same_rows():
+    # the decode and the dense-prefill entry points apply the same window
+    # bound to a q_len block appended after the cache (dense cache, one page each)
+    r = _rng(35)
+    q_len, lk, d, w = 3, 20, 8, 4
+    qd = r.standard_normal((1, q_len, 2, d))
+    kc = r.standard_normal((1, 32, 1, d))
+    vc = r.standard_normal((1, 32, 1, d))
+    od, ld = oracle.decode_paged(qd, kc, vc, np.array([[0]]), np.array([lk]), 32, 0.3, True, d,
+                                 window_left=w)
+    op, lp = oracle.prefill_dense(qd[0], kc[0, :lk], vc[0, :lk], np.array([0, q_len]), np.array([0, lk]),
+                                  0.3, True, window_left=w)
+    assert np.max(np.abs(od[0] - op)) < 1e-13 and np.max(np.abs(ld[0] - lp)) < 1e-13
+
+
 # ------------------------------------------------------------ causal mask --
 
 def test_bottom_right_last_row_sees_everything():

@@ -31,6 +31,10 @@ MUTATIONS = [
     ("np.exp2(lse_parts - top_safe[None, :])", "np.exp(lse_parts - top_safe[None, :])"),  # merge in wrong base
     ("alpha = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)",
      "alpha = np.where(np.isfinite(m), 1.0, 0.0)"),                                # recurrence without rescale
+    ("return np.maximum(0, i + (lk - lq - window_left))",
+     "return np.maximum(0, i + (lk - lq - window_left) + 1)"),                   # window one key short
+    ("visible = (cols[None, :] < key_bound[r0:r1, None]) & (cols[None, :] >= key_start[r0:r1, None])",
+     "visible = (cols[None, :] < key_bound[r0:r1, None]) & (cols[None, :] > key_start[r0:r1, None])"),  # start excluded
     ("rows.append(cache[physical, :take, head, :width])",
      "rows.append(cache[physical, :page_size, head, :width][:take])"),             # harmless: must survive
 ]
