@@ -274,7 +274,7 @@ def main() -> int:
                    "num_splits": plan["num_splits"], "split_tokens": plan["split_tokens"],
                    "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "decode_gqa_wave_kernel<128>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_gqa_wave_kernel<128, false>", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic["bytes_per_launch"],
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_ms": round(split_ms, 5),

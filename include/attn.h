@@ -84,6 +84,12 @@ typedef enum {
  *   causal         0 or 1 (bottom-right aligned).
  *   o      bf16 [total_q, Hq, Dv], strides o_stride_tok / o_stride_head.
  *   lse    optional float32 [total_q, Hq] contiguous, base 2; NULL to skip.
+ *   window_enabled, window_left   sliding window ("TokenSpeed-MLA", kernel
+ *          capability summary, window_left): with window_enabled = 1, query
+ *          row i of a request with Lq queries and Lk keys also skips keys
+ *          j < Lk - Lq - window_left + i (window_left >= 0 keys of context
+ *          before the query block); window_enabled = 0 (a zeroed struct)
+ *          is the full history.
  * Supported: Dqk == Dv in {64, 128, 256}; Hq % Hkv == 0; page_size a power of
  * two >= 16 (paged mode).
  * ---------------------------------------------------------------------- */
@@ -107,6 +113,8 @@ typedef struct {
   void *o;
   int64_t o_stride_tok, o_stride_head;
   float *lse;
+  int32_t window_enabled;            /* 0: full history */
+  int32_t window_left;               /* keys of context when window_enabled */
 } attn_prefill_params;
 
 /* Enqueue ragged prefill. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,
@@ -138,6 +146,17 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  *              bytes (may be NULL when that is 0); contents undefined after.
  *   o          bf16 [batch, q_len, Hq, Dv] contiguous.
  *   lse        optional float32 [batch, q_len, Hq], base 2; NULL to skip.
+ *   window_enabled, window_left   sliding window: with window_enabled = 1,
+ *              row (t, h) also skips keys j < seq_len - q_len - window_left
+ *              + t ("TokenSpeed-MLA", kernel capability summary,
+ *              window_left); the walk starts at the window, so its cost
+ *              tracks the window. 0 (a zeroed struct): full history.
+ *   packed_q   0: the G query heads and F folded query tokens form the MFMA
+ *              rows of a unit; 1: rows are packed continuously as
+ *              t * G + g over the q_len tokens ("TokenSpeed-MLA", packed-
+ *              query paragraph), so H96 with q_len 4 needs 3 tiles of 128
+ *              rows instead of 4; the last tile may be partial. Output and
+ *              LSE layouts are unchanged.
  * Supported: (Dqk, Dv) in {(64,64), (128,128), (256,256)} with bf16 KV and
  * (576, 512) with Hkv == 1 and bf16 or FP8 KV; Hq % Hkv == 0; page_size a
  * power of two >= 16.
@@ -161,14 +180,21 @@ typedef struct {
   size_t workspace_bytes;
   void *o;
   float *lse;
+  int32_t window_enabled;   /* 0: full history */
+  int32_t window_left;      /* keys of context when window_enabled */
+  int32_t packed_q;         /* 0: folded rows; 1: continuous token * G + head rows */
 } attn_decode_params;
 
 /* How attn_decode_paged will decompose a call (host-only; no device access). */
 typedef struct {
   int32_t group;          /* G = Hq / Hkv: query heads per KV head                     */
-  int32_t fold;           /* F: query tokens folded with the G heads into MFMA rows     */
-  int32_t q_groups;       /* q_len / F: row blocks per (request, KV head)               */
-  int32_t rows_per_unit;  /* G * F rows computed together                               */
+  int32_t fold;           /* F: query tokens folded with the G heads into MFMA rows
+                             (1 with packed_q)                                          */
+  int32_t q_groups;       /* row blocks per (request, KV head): q_len / F, or
+                             ceil(G * q_len / rows_per_unit) with packed_q              */
+  int32_t rows_per_unit;  /* rows computed together: G * F, or the MFMA tile rows (128
+                             for the latent shape, 16 otherwise) capped at G * q_len
+                             with packed_q                                             */
   int32_t num_splits;     /* S: KV splits per (request, KV head, q-group)               */
   int32_t split_tokens;   /* keys per split (the last one of a request may be shorter)  */
   int64_t num_units;      /* workgroups of the split kernel                             */

@@ -41,7 +41,7 @@ class PrefillParams(ctypes.Structure):
         ("max_seqlen_q", _i32), ("max_seqlen_kv", _i32),
         ("softmax_scale", ctypes.c_float), ("causal", _i32),
         ("o", _p), ("o_stride_tok", _i64), ("o_stride_head", _i64),
-        ("lse", _p),
+        ("lse", _p), ("window_enabled", _i32), ("window_left", _i32),
     ]
 
 
@@ -58,6 +58,7 @@ class DecodeParams(ctypes.Structure):
         ("softmax_scale", ctypes.c_float), ("causal", _i32), ("num_splits", _i32),
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
         ("o", _p), ("lse", _p),
+        ("window_enabled", _i32), ("window_left", _i32), ("packed_q", _i32),
     ]
 
 

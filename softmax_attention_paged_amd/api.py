@@ -52,7 +52,8 @@ def _as_4d_cache(cache: torch.Tensor) -> torch.Tensor:
 
 def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                   causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
-                  num_splits=0, workspace=None, out=None, lse=None) -> _ffi.DecodeParams:
+                  num_splits=0, workspace=None, out=None, lse=None, window_left=-1,
+                  packed_q=False) -> _ffi.DecodeParams:
     """Fill the C parameter struct from tensors (no device access)."""
     k4 = _as_4d_cache(k_cache)
     v4 = _as_4d_cache(v_cache if v_cache is not None else k_cache)
@@ -74,6 +75,8 @@ def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, so
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     p.o, p.lse = _ptr(out), _ptr(lse)
+    p.window_enabled, p.window_left = int(window_left >= 0), max(int(window_left), 0)
+    p.packed_q = int(bool(packed_q))
     return p
 
 
@@ -85,12 +88,15 @@ def decode_plan(params: _ffi.DecodeParams) -> dict:
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                  causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
-                 num_splits=0, workspace=None, out=None, return_lse=False):
+                 num_splits=0, workspace=None, out=None, return_lse=False, window_left=-1,
+                 packed_q=False):
     """Paged decode (split-KV + LSE merge). Returns out, or (out, lse).
 
     q [B, q_len, Hq, Dqk] bf16; caches [pages, page_size, Hkv, D] (or a 3-D
     latent cache, pass v_cache=None and head_dim_v=512); block_table
-    [B, max_pages] int32; seq_lens [B] int32.
+    [B, max_pages] int32; seq_lens [B] int32. window_left >= 0 limits each
+    row to the q_len block plus window_left keys of context (-1: full
+    history); packed_q packs rows as token * G + head.
     """
     _need(q.is_cuda and q.dtype == _BF16 and q.is_contiguous(), "q must be a contiguous bf16 CUDA tensor")
     _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
@@ -105,7 +111,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, max_seq_len=max_seq_len,
                       softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
                       k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=workspace,
-                      out=out, lse=lse)
+                      out=out, lse=lse, window_left=window_left, packed_q=packed_q)
     lib = _ffi.load()
     if workspace is None:
         need = lib.attn_decode_workspace_size(ctypes.byref(p))
@@ -122,10 +128,13 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
 # --------------------------------------------------------------------------
 
 def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale, causal=False,
-            cu_seqlens_kv=None, seq_lens_kv=None, block_table=None, out=None, return_lse=False):
+            cu_seqlens_kv=None, seq_lens_kv=None, block_table=None, out=None, return_lse=False,
+            window_left=-1):
     """Ragged prefill over dense (cu_seqlens_kv) or paged (block_table +
     seq_lens_kv) KV. q [Tq, Hq, D] bf16; dense k/v [Tk, Hkv, D]; paged k/v
-    [pages, page_size, Hkv, D]. Returns out [Tq, Hq, Dv], or (out, lse)."""
+    [pages, page_size, Hkv, D]. window_left >= 0: row i of a request sees no
+    key before Lk - Lq - window_left + i (-1: full history). Returns
+    out [Tq, Hq, Dv], or (out, lse)."""
     _need(q.is_cuda and q.dtype == _BF16 and q.stride(2) == 1, "q must be bf16 CUDA with contiguous channels")
     _need(k.dtype == _BF16 and v.dtype == _BF16, "k and v must be bf16")
     _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous(), "cu_seqlens_q must be contiguous int32")
@@ -158,6 +167,7 @@ def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale
     p.softmax_scale, p.causal = float(softmax_scale), int(bool(causal))
     p.o, p.o_stride_tok, p.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
     p.lse = _ptr(lse)
+    p.window_enabled, p.window_left = int(window_left >= 0), max(int(window_left), 0)
     _ffi.check(_ffi.load().attn_prefill(ctypes.byref(p), _stream(q.device)), "attn_prefill")
     return (out, lse) if return_lse else out
 

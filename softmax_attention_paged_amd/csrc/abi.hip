@@ -54,6 +54,14 @@ int fold_factor(int heads, int q_len, int capacity) {
   return best;
 }
 
+// Keys a unit may have to walk: the whole history, or with a window the
+// q_len block plus window_left keys of context, plus up to 31 keys of tile
+// alignment before the window's start.
+int window_span(const attn_decode_params *p) {
+  if (!p->window_enabled) return p->max_seq_len;
+  return (int)std::min<int64_t>(p->max_seq_len, (int64_t)p->window_left + p->q_len + 31);
+}
+
 struct DecodePlan {
   bool mla;
   int group, fold, q_groups, rows, splits, split_tokens;
@@ -82,6 +90,11 @@ attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) 
   if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (p->num_splits < 0 || p->num_splits > attn::kMaxSplits)
     return fail(ATTN_ERR_INVALID_ARG, "num_splits %d outside 0..%d", p->num_splits, attn::kMaxSplits);
+  if (p->window_enabled != 0 && p->window_enabled != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "window_enabled must be 0 or 1");
+  if (p->window_enabled && p->window_left < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "window_left %d < 0", p->window_left);
+  if (p->packed_q != 0 && p->packed_q != 1) return fail(ATTN_ERR_INVALID_ARG, "packed_q must be 0 or 1");
 
   const bool mla = is_mla_shape(p);
   if (mla) {
@@ -91,8 +104,8 @@ attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) 
       return fail(ATTN_ERR_UNSUPPORTED, "latent KV must be bf16 or fp8 e4m3");
     if (p->k_cache != p->v_cache || p->k_stride_page != p->v_stride_page || p->k_stride_tok != p->v_stride_tok)
       return fail(ATTN_ERR_UNSUPPORTED, "the latent layout reads V from the K rows: pass the same cache and strides");
-    if (p->num_q_heads > attn::kMlaRows || attn::kMlaRows % p->num_q_heads)
-      return fail(ATTN_ERR_UNSUPPORTED, "latent decode needs num_q_heads dividing %d", attn::kMlaRows);
+    if (p->num_q_heads > attn::kMlaRows)
+      return fail(ATTN_ERR_UNSUPPORTED, "latent decode supports at most %d query heads", attn::kMlaRows);
     if (p->kv_dtype == ATTN_FP8_E4M3 &&
         (!(p->k_scale > 0.f) || !std::isfinite(p->k_scale) || p->k_scale != p->v_scale))
       return fail(ATTN_ERR_INVALID_ARG, "fp8 latent KV needs one finite positive scale (k_scale == v_scale)");
@@ -131,9 +144,18 @@ DecodePlan plan_decode(const attn_decode_params *p) {
   pl.mla = is_mla_shape(p);
   pl.group = p->num_q_heads / p->num_kv_heads;
   const int capacity = pl.mla ? attn::kMlaRows : attn::kGqaRowsPerTile;
-  pl.fold = fold_factor(pl.group, p->q_len, capacity);
-  pl.q_groups = p->q_len / pl.fold;
-  pl.rows = pl.group * pl.fold;
+  if (p->packed_q) {
+    // continuous t * G + g rows in tiles of `capacity`, only the last one partial
+    // ("TokenSpeed-MLA", packed-query paragraph)
+    const int total = pl.group * p->q_len;
+    pl.fold = 1;
+    pl.rows = std::min(capacity, total);
+    pl.q_groups = (int)cdiv(total, pl.rows);
+  } else {
+    pl.fold = fold_factor(pl.group, p->q_len, capacity);
+    pl.q_groups = p->q_len / pl.fold;
+    pl.rows = pl.group * pl.fold;
+  }
   const int64_t base_units = (int64_t)p->batch * p->num_kv_heads * pl.q_groups;
   const int tile = pl.mla ? attn::kMlaTileTokens : attn::kGqaTileTokens;
   int splits;
@@ -142,20 +164,23 @@ DecodePlan plan_decode(const attn_decode_params *p) {
   } else if (pl.mla) {
     // MFMA-bound: about two workgroups per CU, but no split shorter than 1024 keys.
     const int64_t want = cdiv(2 * attn::kNumCUs, base_units > 0 ? base_units : 1);
-    const int64_t by_len = cdiv(p->max_seq_len, 1024);
+    const int64_t by_len = cdiv(window_span(p), 1024);
     splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
   } else {
     // HBM-bound: many small units so ragged lengths balance across 256 CUs,
     // but no split shorter than 256 keys.
     const int64_t want = cdiv(32 * attn::kNumCUs, base_units > 0 ? base_units : 1);
-    const int64_t by_len = cdiv(p->max_seq_len, 256);
+    const int64_t by_len = cdiv(window_span(p), 256);
     splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
   }
   // Split length: a whole number of tiles; then keep only non-empty splits of
-  // the longest request.
-  int64_t split_tokens = cdiv(std::max(p->max_seq_len, 1), splits);
+  // the longest request. With a window, splits cover each request's window
+  // (from its tile-aligned start), so the walk and the split count track the
+  // window rather than the cache.
+  const int span = window_span(p);
+  int64_t split_tokens = cdiv(std::max(span, 1), splits);
   split_tokens = cdiv(split_tokens, tile) * tile;
-  splits = (int)std::max<int64_t>(1, cdiv(p->max_seq_len, split_tokens));
+  splits = (int)std::max<int64_t>(1, cdiv(span, split_tokens));
   pl.splits = splits;
   pl.split_tokens = (int)split_tokens;
   pl.units = base_units * splits;
@@ -180,6 +205,10 @@ attn_status_t validate_prefill(const attn_prefill_params *p) {
     return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_q/max_seqlen_kv must be >= 0");
   if (!std::isfinite(p->softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (p->window_enabled != 0 && p->window_enabled != 1)
+    return fail(ATTN_ERR_INVALID_ARG, "window_enabled must be 0 or 1");
+  if (p->window_enabled && p->window_left < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "window_left %d < 0", p->window_left);
   const bool paged = p->block_table != nullptr;
   if (paged) {
     if (!pow2(p->page_size) || p->page_size < 16)
@@ -281,10 +310,12 @@ attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream)
     a.fold = pl.fold;
     a.q_groups = pl.q_groups;
     a.rows = pl.rows;
+    a.packed = p->packed_q;
     a.num_splits = pl.splits;
     a.split_tokens = pl.split_tokens;
     a.scale_log2 = a.kv_fp8 ? scale_log2 * p->k_scale : scale_log2;
     a.causal = p->causal;
+    a.window_left = p->window_enabled ? p->window_left : -1;
     a.o = p->o;
     a.lse = p->lse;
     a.o_parts = o_parts;
@@ -314,10 +345,12 @@ attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream)
     a.fold = pl.fold;
     a.q_groups = pl.q_groups;
     a.rows = pl.rows;
+    a.packed = p->packed_q;
     a.num_splits = pl.splits;
     a.split_tokens = pl.split_tokens;
     a.scale_log2 = scale_log2;
     a.causal = p->causal;
+    a.window_left = p->window_enabled ? p->window_left : -1;
     a.o = p->o;
     a.lse = p->lse;
     a.o_parts = o_parts;
@@ -372,6 +405,7 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
   a.q_tiles = (int)cdiv(p->max_seqlen_q, kPrefillRows);
   a.scale_log2 = p->softmax_scale * attn::kLog2eHost;
   a.causal = p->causal;
+  a.window_left = p->window_enabled ? p->window_left : -1;
   a.o = p->o;
   a.o_stride_tok = p->o_stride_tok;
   a.o_stride_head = p->o_stride_head;

@@ -22,9 +22,11 @@ struct DecodeGqaArgs {
   int32_t batch, q_len, num_q_heads, num_kv_heads, head_dim;
   int32_t page_shift;            // log2(page_size)
   int32_t group, fold, q_groups, rows;
+  int32_t packed;                // rows numbered t * group + g across the q_len tokens
   int32_t num_splits, split_tokens;
   float scale_log2;              // softmax_scale * log2(e)
   int32_t causal;
+  int32_t window_left;           // keys of context before the query block; -1: full history
   // outputs: either final (num_splits == 1) or partials
   void *o;                       // bf16 [B, q_len, Hq, D]
   float *lse;                    // optional [B, q_len, Hq]
@@ -44,10 +46,12 @@ struct DecodeMlaArgs {
   int32_t block_table_stride;
   int32_t batch, q_len, num_heads;
   int32_t page_shift;
-  int32_t fold, q_groups, rows;  // rows = num_heads * fold
+  int32_t fold, q_groups, rows;  // rows per unit: num_heads * fold, or up to 128 packed rows
+  int32_t packed;                // rows numbered t * num_heads + h across the q_len tokens
   int32_t num_splits, split_tokens;
   float scale_log2;
   int32_t causal;
+  int32_t window_left;           // keys of context before the query block; -1: full history
   void *o;
   float *lse;
   float *o_parts;
@@ -82,6 +86,7 @@ struct PrefillArgs {
   int32_t q_tiles;               // ceil(max_seqlen_q / rows per workgroup)
   float scale_log2;
   int32_t causal;
+  int32_t window_left;           // keys of context before the query block; -1: full history
   void *o;
   int64_t o_stride_tok, o_stride_head;
   float *lse;

@@ -56,6 +56,7 @@ struct GqaGeom {
   // waves per SIMD the registers are budgeted for: more waves keep more
   // K/V loads in flight per CU (D = 128 fits 3 in 167 VGPRs without spills)
   static constexpr int kWPE = D <= 64 ? 4 : (D <= 128 ? 3 : 1);
+  static constexpr int kWPEExt = D <= 64 ? 4 : (D <= 128 ? 2 : 1);   // window / packed rows
 };
 
 // Gather one 32-key tile of K (MFMA A layout) or V (linear 16-byte chunks).
@@ -121,9 +122,13 @@ struct UnitRows {
   bool row_valid;
   int64_t ridx;     // this lane's row in [B, q_len, Hq]
   int c0, c1;       // keys of the split any row of the unit sees
-  int row_end;      // keys < row_end are visible to this lane's row
+  int first;        // first tile of the split the unit walks (tile-aligned, >= c0)
+  int begin_max;    // the largest row_begin of the unit's valid rows (wave-uniform)
+  int row_begin;    // keys >= row_begin ...
+  int row_end;      // ... and < row_end are visible to this lane's row
 };
 
+template <bool kExt>
 __device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int kvh, int qg, int split, int lane) {
   UnitRows u;
   u.b = b;
@@ -131,19 +136,53 @@ __device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int
   u.qg = qg;
   u.split = split;
   u.row = lane & 15;
-  u.row_valid = u.row < a.rows;
   const int lk = a.seq_lens[b];
-  // Row r of the unit is query token qg*F + r/G, head kvh*G + r%G.
-  const int t_row = qg * a.fold + (u.row_valid ? u.row / a.group : 0);
-  const int h_row = kvh * a.group + (u.row_valid ? u.row % a.group : 0);
+  int t_row, g_row, t_first, t_last;
+  if (kExt && a.packed) {
+    // rows t * G + g packed continuously over the q_len tokens ("TokenSpeed-
+    // MLA", packed-query paragraph): row r of unit qg is packed row qg*rows + r
+    const int total = a.group * a.q_len;
+    const int pr = qg * a.rows + u.row;
+    u.row_valid = u.row < a.rows && pr < total;
+    t_row = u.row_valid ? pr / a.group : 0;
+    g_row = u.row_valid ? pr % a.group : 0;
+    t_first = (qg * a.rows) / a.group;
+    t_last = (min(qg * a.rows + a.rows, total) - 1) / a.group;
+  } else {
+    // row r of unit qg is query token qg*F + r/G, head kvh*G + r%G
+    u.row_valid = u.row < a.rows;
+    t_row = qg * a.fold + (u.row_valid ? u.row / a.group : 0);
+    g_row = u.row_valid ? u.row % a.group : 0;
+    t_first = qg * a.fold;
+    t_last = qg * a.fold + a.fold - 1;
+  }
+  const int h_row = kvh * a.group + g_row;
   int bound = lk, unit_bound = lk;
   if (a.causal) {
     bound = min(lk, max(0, lk - a.q_len + t_row + 1));
-    unit_bound = min(lk, max(0, lk - a.q_len + qg * a.fold + a.fold));  // the last folded token sees most
+    unit_bound = min(lk, max(0, lk - a.q_len + t_last + 1));   // the unit's last token sees most
   }
-  u.c0 = split * a.split_tokens;
+  // Sliding window ("TokenSpeed-MLA", kernel capability summary, window_left):
+  // row t sees no key before lk - q_len - window_left + t. The splits of a
+  // request start at its window (tile-aligned), so the walk tracks the window.
+  int base = 0, unit_begin = 0;
+  u.row_begin = 0;
+  if (kExt && a.window_left >= 0) {
+    u.row_begin = max(0, lk - a.q_len - a.window_left + t_row);
+    unit_begin = max(0, lk - a.q_len - a.window_left + t_first);
+    base = max(0, lk - a.q_len - a.window_left) & ~(kGqaTileTokens - 1);
+  }
+  u.c0 = base + split * a.split_tokens;
   u.c1 = min(unit_bound, u.c0 + a.split_tokens);
+  u.first = u.c0 + (max(0, unit_begin - u.c0) & ~(kGqaTileTokens - 1));
   u.row_end = min(bound, u.c1);
+  u.begin_max = INT32_MIN;   // no row has a lower bound: the mask branch folds away
+  if (kExt) {
+    int bm = u.row_valid ? u.row_begin : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) bm = max(bm, __shfl_xor(bm, off, 64));
+    u.begin_max = __builtin_amdgcn_readfirstlane(bm);
+  }
   u.ridx = ((int64_t)b * a.q_len + t_row) * a.num_q_heads + h_row;
   return u;
 }
@@ -233,6 +272,17 @@ struct WaveState {
           x[4 * t + i] = v;
           mx = fmaxf(mx, v);
         }
+      if (tok0 < u.begin_max) {   // the window's lower bound reaches this tile (scalar test)
+        mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = tok0 + 16 * t + 4 * kg + i;
+            if (j < u.row_begin) x[4 * t + i] = kNegInf;
+            mx = fmaxf(mx, x[4 * t + i]);
+          }
+      }
       mx = fmaxf(mx, wave_shfl_xor(mx, 16));
       mx = fmaxf(mx, wave_shfl_xor(mx, 32));
       const float m_new = fmaxf(m, mx);
@@ -301,8 +351,12 @@ __device__ __forceinline__ void write_empty(const DecodeGqaArgs &a, const UnitRo
 // the same token rows are dispatched together. The wave walks its split's
 // tiles in order and writes its rows itself: no cross-wave merge, and a
 // finished wave frees its slot at once.
-template <int D>
-__global__ __launch_bounds__(64, GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(const DecodeGqaArgs a) {
+//
+// kExt adds what a sliding window or packed query rows need (the
+// lower-bound mask, the packed row mapping); its extra live registers would
+// spill at the plain kernel's occupancy, so it runs at its own.
+template <int D, bool kExt>
+__global__ __launch_bounds__(64, kExt ? GqaGeom<D>::kWPEExt : GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(const DecodeGqaArgs a) {
   using G = GqaGeom<D>;
   __shared__ __attribute__((aligned(16))) __bf16 vlds[G::kVTile];
   const int lane = threadIdx.x;
@@ -314,14 +368,14 @@ __global__ __launch_bounds__(64, GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(c
   unit /= a.num_kv_heads;
   const int split = unit % a.num_splits;
   const int b = unit / a.num_splits;
-  const UnitRows u = unit_rows(a, b, kvh, qg, split, lane);
-  if (u.c0 >= u.c1) {
+  const UnitRows u = unit_rows<kExt>(a, b, kvh, qg, split, lane);
+  if (u.first >= u.c1) {       // no key of this split is visible to the unit
     write_empty<D>(a, u, lane);
     return;
   }
   WaveState<D> st;
   st.init(a, u, lane);
-  st.walk(a, u, u.c0, G::kTile, vlds, lane);
+  st.walk(a, u, u.first, G::kTile, vlds, lane);
   st.reduce_sums();
   if (!u.row_valid) return;
 
@@ -352,7 +406,10 @@ __global__ __launch_bounds__(64, GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(c
 template <int D>
 hipError_t launch_d(const DecodeGqaArgs &a, hipStream_t stream) {
   const int64_t units = (int64_t)a.batch * a.num_splits * a.num_kv_heads * a.q_groups;
-  hipLaunchKernelGGL(decode_gqa_wave_kernel<D>, dim3((unsigned)units), dim3(64), 0, stream, a);
+  if (a.packed || a.window_left >= 0)
+    hipLaunchKernelGGL((decode_gqa_wave_kernel<D, true>), dim3((unsigned)units), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_gqa_wave_kernel<D, false>), dim3((unsigned)units), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

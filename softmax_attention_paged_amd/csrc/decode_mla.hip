@@ -29,7 +29,7 @@
 //     ds_read_b64_tr_b16;
 //   - static-anchor softmax ("Flywheel Attention", section "Static-anchor
 //     softmax" and Appendix A): each row fixes its anchor at the max of its
-//     first tile and never moves it, so O is never rescaled (it stays in the
+//     first tile with a visible key and never moves it, so O is never rescaled (it stays in the
 //     accumulation registers, untouched by vector ALU work); after each tile
 //     the running sum is checked against 2^kAnchorLog2, which bounds every
 //     exponential taken so far. A failed check (a score far above the anchor,
@@ -195,7 +195,10 @@ __device__ __forceinline__ void mla_store_fp8(char *dst, int tid, const u32x4 (&
   }
 }
 
-template <bool FP8>
+// kExt adds what a sliding window or packed query rows need (the packed row
+// mapping, the window's start and lower-bound mask); the plain kernel keeps
+// those registers free.
+template <bool FP8, bool kExt>
 __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMlaArgs a) {
   __shared__ __attribute__((aligned(16))) char tiles[2 * kTileB];
   __shared__ __attribute__((aligned(16))) char qlds[kMlaRows * kQRowB];
@@ -213,23 +216,51 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
   const int b = unit / a.num_splits;
 
   const int lk = a.seq_lens[b];
-  int unit_bound = lk;
-  if (a.causal) unit_bound = min(lk, max(0, lk - a.q_len + qg * a.fold + a.fold));
-  const int c0 = split * a.split_tokens;
-  const int c1 = min(unit_bound, c0 + a.split_tokens);
-
-  // this lane's row: r = 32 * wave + lane % 32 -> query token qg*F + r/H, head r%H
+  // this lane's row r = 32 * wave + lane % 32: folded, query token qg*F + r/H
+  // and head r%H; packed ("TokenSpeed-MLA", packed-query paragraph), packed
+  // row qg*rows + r = token * H + head
   const int r = 32 * wave + r32;
-  const bool row_valid = r < a.rows;
-  const int t_row = qg * a.fold + (row_valid ? r / a.num_heads : 0);
-  const int h_row = row_valid ? r % a.num_heads : 0;
+  int t_row, h_row, t_first, t_last;
+  bool row_valid;
+  if (kExt && a.packed) {
+    const int total = a.num_heads * a.q_len;
+    const int pr = qg * a.rows + r;
+    row_valid = r < a.rows && pr < total;
+    t_row = row_valid ? pr / a.num_heads : 0;
+    h_row = row_valid ? pr % a.num_heads : 0;
+    t_first = (qg * a.rows) / a.num_heads;
+    t_last = (min(qg * a.rows + a.rows, total) - 1) / a.num_heads;
+  } else {
+    row_valid = r < a.rows;
+    t_row = qg * a.fold + (row_valid ? r / a.num_heads : 0);
+    h_row = row_valid ? r % a.num_heads : 0;
+    t_first = qg * a.fold;
+    t_last = qg * a.fold + a.fold - 1;
+  }
+  int unit_bound = lk, bound = lk;
+  if (a.causal) {
+    unit_bound = min(lk, max(0, lk - a.q_len + t_last + 1));
+    bound = min(lk, max(0, lk - a.q_len + t_row + 1));
+  }
+  // Sliding window ("TokenSpeed-MLA", kernel capability summary, window_left):
+  // row t sees no key before lk - q_len - window_left + t; a request's splits
+  // start at its window (tile-aligned), so the walk tracks the window.
+  int base = 0, unit_begin = 0, row_begin = 0;
+  if (kExt && a.window_left >= 0) {
+    row_begin = max(0, lk - a.q_len - a.window_left + t_row);
+    unit_begin = max(0, lk - a.q_len - a.window_left + t_first);
+    base = max(0, lk - a.q_len - a.window_left) & ~(kTileN - 1);
+  }
+  // wave-uniform by construction; said explicitly so the tile addresses
+  // derived from them stay in scalar registers
+  const int c0 = __builtin_amdgcn_readfirstlane(base + split * a.split_tokens);
+  const int c1 = __builtin_amdgcn_readfirstlane(min(unit_bound, c0 + a.split_tokens));
+  const int first = __builtin_amdgcn_readfirstlane(c0 + (max(0, unit_begin - c0) & ~(kTileN - 1)));
   const int64_t R = (int64_t)a.batch * a.q_len * a.num_heads;
   const int64_t ridx = ((int64_t)b * a.q_len + t_row) * a.num_heads + h_row;
-  int bound = lk;
-  if (a.causal) bound = min(lk, max(0, lk - a.q_len + t_row + 1));
   const int row_end = min(bound, c1);
 
-  if (c0 >= c1) {   // uniform: no key of this split is visible
+  if (first >= c1) {   // uniform: no key of this split is visible
     if (row_valid) {
       if (a.num_splits == 1) {
         __bf16 *dst = static_cast<__bf16 *>(a.o) + ridx * kDv + 4 * half;
@@ -245,11 +276,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
     return;
   }
 
-  // first key of the split some valid row of this wave must mask (scalar)
+  // keys some valid row of this wave must mask: from valid_min up, and below
+  // begin_max (scalars, so the per-tile tests are branches)
   int valid_min = row_valid ? row_end : 0x7fffffff;
+  int begin_max = (kExt && row_valid) ? row_begin : 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
+  for (int off = 32; off >= 1; off >>= 1) {
+    valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
+    begin_max = max(begin_max, __shfl_xor(begin_max, off, 64));
+  }
   valid_min = __builtin_amdgcn_readfirstlane(valid_min);
+  begin_max = __builtin_amdgcn_readfirstlane(begin_max);
   const bool wave_active = 32 * wave < a.rows;
 
   // Q^T operand: lane holds Q[row r][16 kb + 8 half .. +8]; a negative scale
@@ -316,7 +353,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
   float anchor = kNegInf;                     // this row's static anchor (log2 units); -inf: no key yet
   float lsum = 0.f;
   f32x16 oacc[kNB];
-  const int ntiles = (c1 - c0 + kTileN - 1) / kTileN;
+  const int ntiles = (c1 - first + kTileN - 1) / kTileN;
   u32x4 stage[kF8PerThread];
   const float sum_limit = exp2f(kAnchorLog2);
 
@@ -324,10 +361,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x16{};
     lsum = 0.f;
-    mla_issue<FP8>(x, map, c0, c1, wave, lane, tid, tiles, stage);
+    mla_issue<FP8>(x, map, first, c1, wave, lane, tid, tiles, stage);
     if constexpr (FP8) mla_store_fp8(tiles, tid, stage);
     for (int it = 0; it < ntiles; ++it) {
-      const int j0 = c0 + it * kTileN;
+      const int j0 = first + it * kTileN;
       const int p = it & 1;
       // tile it has landed for every wave; every wave is done with tile it-1,
       // whose buffer takes tile it+1
@@ -373,10 +410,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
           }
         }
         if (it == 0 && attempt == 0) {        // the anchor: the max of the row's first tile
+          // A window may hide this whole tile from a row whose keys start in
+          // the next one; its scores are still real dot products of the row's
+          // query, so they bound the row's scale just as well and the anchor
+          // is taken before the window's mask.
           float mx = kNegInf;
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
           anchor = half_max(mx) * c;
+        }
+        if (kExt && j0 < begin_max) {         // the window's lower bound (scalar test)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
+            s[i] = (j >= row_begin) ? s[i] : kNegInf;
+          }
         }
         const float a_use = (anchor == kNegInf) ? 0.f : anchor;
         bf16x8 pop[2];
@@ -466,10 +514,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
 
 hipError_t launch_decode_mla(const DecodeMlaArgs &a, hipStream_t stream) {
   const int64_t units = (int64_t)a.batch * a.num_splits * a.q_groups;
-  if (a.kv_fp8)
-    hipLaunchKernelGGL(decode_mla_kernel<true>, dim3((unsigned)units), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_mla_kernel<false>, dim3((unsigned)units), dim3(kThreads), 0, stream, a);
+  const bool ext = a.packed || a.window_left >= 0;
+  const dim3 grid((unsigned)units), block(kThreads);
+  if (a.kv_fp8) {
+    if (ext) hipLaunchKernelGGL((decode_mla_kernel<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mla_kernel<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (ext) hipLaunchKernelGGL((decode_mla_kernel<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mla_kernel<false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

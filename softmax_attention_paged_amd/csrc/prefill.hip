@@ -258,14 +258,14 @@ __device__ __forceinline__ float pp_max(const f32x16 (&s)[2]) {
   return mx;
 }
 
-// Keys at or past `bound` (this lane's row) get -inf.
-__device__ __forceinline__ void pp_mask(f32x16 (&s)[2], int j0, int bound, int h) {
+// Keys at or past `bound`, or before `begin` (this lane's row), get -inf.
+__device__ __forceinline__ void pp_mask(f32x16 (&s)[2], int j0, int begin, int bound, int h) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = j0 + 32 * sub + 8 * (i >> 2) + 4 * h + (i & 3);
-      s[sub][i] = (j < bound) ? s[sub][i] : kNegInf;
+      s[sub][i] = (j < bound && j >= begin) ? s[sub][i] : kNegInf;
     }
 }
 
@@ -320,17 +320,30 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   const bool row_valid = t >= u.q_begin && t < u.q_end;
   int bound = a.causal ? min(u.lk, max(0, u.lk - u.lq + t + 1)) : u.lk;
   if (!row_valid) bound = 0;
+  // Sliding window ("TokenSpeed-MLA", kernel capability summary,
+  // window_left): row t sees no key before lk - lq - window_left + t. The
+  // workgroup's walk starts at the tile holding its first row's first key.
+  const bool windowed = a.window_left >= 0;
+  const int begin = windowed ? max(0, u.lk - u.lq - a.window_left + t) : 0;
+  const int jb = windowed ? max(0, u.lk - u.lq - a.window_left + u.q_begin) & ~(G::kN - 1) : 0;
   int wave_max = bound, valid_min = row_valid ? bound : 0x7fffffff;
+  int begin_max = row_valid ? begin : 0, begin_min = row_valid ? begin : 0x7fffffff;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     wave_max = max(wave_max, __shfl_xor(wave_max, off, 64));
     valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
+    begin_max = max(begin_max, __shfl_xor(begin_max, off, 64));
+    begin_min = min(begin_min, __shfl_xor(begin_min, off, 64));
   }
   wave_max = __builtin_amdgcn_readfirstlane(wave_max);
   valid_min = __builtin_amdgcn_readfirstlane(valid_min);
+  begin_max = __builtin_amdgcn_readfirstlane(begin_max);
+  begin_min = __builtin_amdgcn_readfirstlane(begin_min);
   const int kv_end = a.causal ? min(u.lk, max(0, u.lk - u.lq + u.q_end)) : u.lk;
-  const int nt = (kv_end + G::kN - 1) / G::kN;        // tiles the workgroup loads
-  const int ntw = (wave_max + G::kN - 1) / G::kN;     // tiles this wave computes (ntw <= nt)
+  const int nt = kv_end > jb ? (kv_end - jb + G::kN - 1) / G::kN : 0;       // tiles the workgroup loads
+  const int ntw = wave_max > jb ? (wave_max - jb + G::kN - 1) / G::kN : 0;  // tiles this wave computes (<= nt)
+  // the wave's first tile with a key for one of its rows (0 without a window)
+  const int it0 = (windowed && begin_min != 0x7fffffff) ? (begin_min - jb) / G::kN : 0;
 
   // Q^T operands (a negative scale negates Q, exact in bf16, so c > 0)
   const float c = fabsf(a.scale_log2);
@@ -389,12 +402,12 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   auto kslot = [&](int par) { return lds + par * G::kTile; };
   auto vslot = [&](int par) { return lds + (2 + par) * G::kTile; };
   if (nt > 0) {
-    pp_fetch_pages<D, KV>(bt_row, 0, u.lk, a.page_shift, wave, lane, kpage, kpid);
-    issue_k(0, kpage, kpid, kslot(0));
-    issue_v(0, kpage, kpid, vslot(0));
-    pp_fetch_pages<D, KV>(bt_row, G::kN, u.lk, a.page_shift, wave, lane, vpage, vpid);
-    if (nt > 1) issue_k(G::kN, vpage, vpid, kslot(1));
-    pp_fetch_pages<D, KV>(bt_row, 2 * G::kN, u.lk, a.page_shift, wave, lane, kpage, kpid);
+    pp_fetch_pages<D, KV>(bt_row, jb, u.lk, a.page_shift, wave, lane, kpage, kpid);
+    issue_k(jb, kpage, kpid, kslot(0));
+    issue_v(jb, kpage, kpid, vslot(0));
+    pp_fetch_pages<D, KV>(bt_row, jb + G::kN, u.lk, a.page_shift, wave, lane, vpage, vpid);
+    if (nt > 1) issue_k(jb + G::kN, vpage, vpid, kslot(1));
+    pp_fetch_pages<D, KV>(bt_row, jb + 2 * G::kN, u.lk, a.page_shift, wave, lane, kpage, kpid);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -415,7 +428,7 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
     // with K(it) and V(it-1), whose slots take K(it+2) and V(it+1).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int j0 = it * G::kN;
+    const int j0 = jb + it * G::kN;
     const int par = it & 1;
     if (it + 2 < nt) issue_k(j0 + 2 * G::kN, kpage, kpid, kslot(par));
     if (it + 1 < nt) issue_v(j0 + G::kN, vpage, vpid, vslot(par ^ 1));
@@ -423,9 +436,14 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
       if (it + 2 < nt) pp_fetch_pages<D, KV>(bt_row, j0 + 2 * G::kN, u.lk, a.page_shift, wave, lane, vpage, vpid);
       if (it + 3 < nt) pp_fetch_pages<D, KV>(bt_row, j0 + 3 * G::kN, u.lk, a.page_shift, wave, lane, kpage, kpid);
     }
-    if (it < ntw) {
-      if (j0 + G::kN > valid_min) {
-        pp_mask(s, j0, bound, h);
+    // A wave whose rows' window starts in tile it0 skips the tiles before
+    // it0 - 1; on tile it0 - 1 every key is below every row's window, so the
+    // mask clears the stale scores, the step adds nothing and computes the
+    // scores of tile it0. (0 <= it0 < ntw when ntw > 0: a valid row's first
+    // key lies below its bound; one unsigned compare tests it0 - 1 <= it < ntw.)
+    if ((unsigned)(it + 1 - it0) < (unsigned)(ntw + 1 - it0)) {
+      if (j0 + G::kN > valid_min || j0 < begin_max) {
+        pp_mask(s, j0, begin, bound, h);
         mx = pp_max(s);
       }
       const float mt = half_max(mx) * c;

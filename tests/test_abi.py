@@ -90,6 +90,8 @@ def plan(p):
     (dict(q=FAKE + 8), _ffi.ATTN_ERR_INVALID_ARG),
     (dict(k_stride_tok=100), _ffi.ATTN_ERR_INVALID_ARG),
     (dict(num_q_heads=68, num_kv_heads=2), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(window_enabled=2), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(window_enabled=1, window_left=-3), _ffi.ATTN_ERR_INVALID_ARG),
 ])
 def test_decode_validation_errors(kw, code):
     lib = _lib()
@@ -219,3 +221,52 @@ def test_qwen3_14b_decode_plan():
     assert st == 0
     assert (info.group, info.fold, info.rows_per_unit) == (5, 1, 5)
     assert info.num_units == 64 * 8 * info.num_splits and info.num_splits > 1
+
+
+def test_packed_q_must_be_a_flag():
+    lib = _lib()
+    p = decode_params(packed_q=2)
+    assert lib.attn_decode_paged(ctypes.byref(p), None) == _ffi.ATTN_ERR_INVALID_ARG
+
+
+def _latent(**kw):
+    d = dict(num_kv_heads=1, head_dim_qk=576, head_dim_v=512, v_cache=FAKE, k_stride_page=64 * 576,
+             k_stride_tok=576, k_stride_head=576, v_stride_page=64 * 576, v_stride_tok=576,
+             v_stride_head=576, page_size=64, num_pages=10240, max_seq_len=81920, block_table_stride=1280,
+             batch=8)
+    d.update(kw)
+    return decode_params(**d)
+
+
+def test_packed_q_tiles_match_tokenspeed_h96_example():
+    # "H96/Sq4 uses three query tiles instead of four": folded rows need one
+    # 96-row group per token, packed rows fill 128-row tiles across tokens
+    st, folded = plan(_latent(num_q_heads=96, q_len=4))
+    assert st == 0 and (folded.fold, folded.q_groups, folded.rows_per_unit) == (1, 4, 96)
+    st, packed = plan(_latent(num_q_heads=96, q_len=4, packed_q=1))
+    assert st == 0
+    assert packed.q_groups == oracle.packed_query_tiles(96, 4) == 3 and packed.rows_per_unit == 128
+    # H64 q4: packing and folding coincide (two tiles of 128)
+    st, p64 = plan(_latent(num_q_heads=64, q_len=4, packed_q=1))
+    assert st == 0 and (p64.q_groups, p64.rows_per_unit) == (2, 128)
+    # GQA: 5 heads x 4 tokens = 20 rows -> ceil(20 / 16) tiles of 16
+    st, g = plan(decode_params(q_len=4, num_q_heads=40, num_kv_heads=8, packed_q=1))
+    assert st == 0 and (g.fold, g.q_groups, g.rows_per_unit) == (1, 2, 16)
+    # the workspace does not depend on the packing (partials are indexed by row)
+    st, a = plan(_latent(num_q_heads=96, q_len=4, num_splits=4))
+    st, b = plan(_latent(num_q_heads=96, q_len=4, num_splits=4, packed_q=1))
+    assert a.workspace_bytes == b.workspace_bytes == 4 * 8 * 4 * 96 * 513 * 4
+
+
+def test_window_plans_splits_over_the_window():
+    # with a window the walk covers the q_len block plus window_left keys of
+    # context (plus tile alignment), so the split plan follows the window
+    st, full = plan(_latent(num_q_heads=64, q_len=4))
+    st2, win = plan(_latent(num_q_heads=64, q_len=4, window_enabled=1, window_left=100))
+    assert st == st2 == 0
+    assert full.num_splits > 1
+    assert win.num_splits == 1 and win.split_tokens >= 100 + 4 and win.split_tokens % 32 == 0
+    st, g = plan(decode_params(max_seq_len=256, num_pages=16, block_table_stride=16, window_enabled=1,
+                               window_left=1000))
+    assert st == 0 and g.num_splits * g.split_tokens >= 256     # a window wider than the history
+

@@ -24,7 +24,7 @@ def _run(case, num_splits=0, return_lse=True):
                                 head_dim_v=c.head_dim_v,
                                 kv_dtype=c.kv_dtype if c.kv_dtype != "bf16" else None,
                                 k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits,
-                                return_lse=return_lse)
+                                return_lse=return_lse, window_left=c.window_left, packed_q=c.packed_q)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 

@@ -19,7 +19,8 @@ def _run(case, num_splits=0):
     out, lse = sap.decode_paged(c.q, c.k_cache, None, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
                                 softmax_scale=c.scale, causal=c.causal, head_dim_v=512,
                                 kv_dtype=None if c.kv_dtype == "bf16" else c.kv_dtype,
-                                k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits, return_lse=True)
+                                k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits, return_lse=True,
+                                window_left=c.window_left, packed_q=c.packed_q)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 

@@ -16,7 +16,7 @@ DEV = "cuda"
 def _run(case):
     c = case.to(DEV)
     kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale,
-              causal=c.causal, return_lse=True)
+              causal=c.causal, return_lse=True, window_left=c.window_left)
     if c.paged:
         out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv,
                                block_table=c.block_table, **kw)
