@@ -38,6 +38,8 @@
 // SIMD (its Q operand and O accumulator take most of a SIMD's registers),
 // D <= 128 at two.
 
+#include <type_traits>
+
 #include "attn_internal.h"
 #include "device_common.h"
 
@@ -121,6 +123,7 @@ template <int D>
 struct PpGeom {
   static constexpr int kW = 4;                         // waves per workgroup
   static constexpr int kWPE = D <= 128 ? 2 : 1;        // waves per SIMD the registers allow
+  static constexpr int kRing = D <= 128 ? 0 : 4;       // LDS operand reads issued ahead (0: compiler order)
   static constexpr int kN = 64;                        // keys per tile
   static constexpr int kKB = D / 16;                   // QK k-steps
   static constexpr int kNB = D / 32;                   // PV 32-channel blocks
@@ -277,30 +280,85 @@ __device__ __forceinline__ void pp_step(f32x16 (&s)[2], float &mx, float m_use, 
                                         const int (&koff)[PpGeom<D>::kKB], const int (&voff)[2][PpGeom<D>::kNB],
                                         const bf16x8 (&qop)[PpGeom<D>::kKB]) {
   using G = PpGeom<D>;
-  f32x16 sn[2];
-  pp_scores<D>(knext, koff, qop, sn);
-  bf16x8 pop[G::kKK];
-  float ps[2] = {0.f, 0.f};
+  if constexpr (G::kRing == 0) {
+    f32x16 sn[2];
+    pp_scores<D>(knext, koff, qop, sn);
+    bf16x8 pop[G::kKK];
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pe = exp2_fast(__builtin_fmaf(s[sub][i], c, -m_use));
-      pop[2 * sub + (i >> 3)][i & 7] = to_bf16(pe);
-      ps[i & 1] += pe;
+      for (int i = 0; i < 16; ++i) {
+        const float pe = exp2_fast(__builtin_fmaf(s[sub][i], c, -m_use));
+        pop[2 * sub + (i >> 3)][i & 7] = to_bf16(pe);
+        ps[i & 1] += pe;
+      }
+#pragma unroll
+    for (int kk = 0; kk < G::kKK; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < G::kNB; ++nb) {
+        const bf16x4 lo = lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2);
+        const bf16x4 hi = lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2);
+        oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
+      }
+    lsum = alpha * lsum + (ps[0] + ps[1]);
+    s[0] = sn[0];
+    s[1] = sn[1];
+    mx = pp_max(s);
+  } else {
+    // LDS operand reads run kRing MFMAs ahead in a register ring; the exp
+    // work of the current tile is spread over the QK steps and the max of
+    // the next tile's scores over the PV steps (one wave per SIMD at this D
+    // leaves no other wave to hide LDS latency behind).
+    constexpr int kQK = 2 * G::kKB;
+    constexpr int kPV = G::kKK * G::kNB;
+    constexpr int kSteps = kQK + kPV;
+    constexpr int kR = G::kRing;
+    constexpr int kExpPer = 32 / kQK;
+    constexpr int kMaxPer = 32 / kPV;
+    auto rd = [&](int t) -> bf16x8 {
+      if (t < kQK)
+        return *reinterpret_cast<const bf16x8 *>(knext + koff[t % G::kKB] + (t / G::kKB) * 32 * D * 2);
+      const int u = t - kQK, kk = u / G::kNB, nb = u % G::kNB;
+      return concat(lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2),
+                    lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2));
+    };
+    bf16x8 ring[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) ring[i] = rd(i);
+    f32x16 sn[2] = {f32x16{}, f32x16{}};
+    bf16x8 pop[G::kKK];
+    float ps[2] = {0.f, 0.f};
+    float mxn = kNegInf;
+#pragma unroll
+    for (int t = 0; t < kSteps; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < kQK) {
+        sn[t / G::kKB] = mfma32x32x16(ring[t % kR], qop[t % G::kKB], sn[t / G::kKB]);
+#pragma unroll
+        for (int e = 0; e < kExpPer; ++e) {
+          const int idx = t * kExpPer + e, sb = idx / 16, i = idx % 16;
+          const float pe = exp2_fast(__builtin_fmaf(s[sb][i], c, -m_use));
+          pop[2 * sb + (i >> 3)][i & 7] = to_bf16(pe);
+          ps[i & 1] += pe;
+        }
+      } else {
+        const int u = t - kQK;
+        oacc[u % G::kNB] = mfma32x32x16(ring[t % kR], pop[u / G::kNB], oacc[u % G::kNB]);
+#pragma unroll
+        for (int e = 0; e < kMaxPer; ++e) {
+          const int idx = u * kMaxPer + e;
+          mxn = fmaxf(mxn, sn[idx / 16][idx % 16]);
+        }
+      }
+      if (t + kR < kSteps) ring[t % kR] = rd(t + kR);
     }
-#pragma unroll
-  for (int kk = 0; kk < G::kKK; ++kk)
-#pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) {
-      const bf16x4 lo = lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2);
-      const bf16x4 hi = lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2);
-      oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
-    }
-  lsum = alpha * lsum + (ps[0] + ps[1]);
-  s[0] = sn[0];
-  s[1] = sn[1];
-  mx = pp_max(s);
+    __builtin_amdgcn_sched_barrier(0);
+    lsum = alpha * lsum + (ps[0] + ps[1]);
+    s[0] = sn[0];
+    s[1] = sn[1];
+    mx = mxn;
+  }
 }
 
 template <int D, int KV>
@@ -423,13 +481,21 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
 #pragma unroll
   for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x16{};
 
-  for (int it = 0; it < nt; ++it) {
+  // The loop is unrolled by two so each half knows its LDS slots at compile
+  // time; the per-lane offsets are made opaque once per tile, so the compiler
+  // folds every slot and block constant into the LDS reads' immediate offsets
+  // rather than computing addresses per tile or keeping each one in a register.
+  auto tile_step = [&](int it, auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb) asm volatile("" : "+v"(koff[kb]));
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) asm volatile("" : "+v"(voff[0][nb]), "+v"(voff[1][nb]));
     // K(it+1) and V(it) have landed for every wave, and every wave is done
     // with K(it) and V(it-1), whose slots take K(it+2) and V(it+1).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const int j0 = jb + it * G::kN;
-    const int par = it & 1;
     if (it + 2 < nt) issue_k(j0 + 2 * G::kN, kpage, kpid, kslot(par));
     if (it + 1 < nt) issue_v(j0 + G::kN, vpage, vpid, vslot(par ^ 1));
     if constexpr (KV != kKvDense) {
@@ -462,6 +528,10 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
       // body keeps the exp work beside the MFMAs.
       pp_step<D>(s, mx, m_use, c, alpha, lsum, oacc, knext, vbytes, koff, voff, qop);
     }
+  };
+  for (int it = 0; it < nt; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nt) tile_step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: O / l -> bf16; LSE2 = m + log2(l) ----
