@@ -32,3 +32,10 @@ from .plan_examples import (  # noqa: F401
     mla_packed_workspace_bytes,
     static_anchor_tau,
 )
+from .cache import (  # noqa: F401
+    E4M3_MAX,
+    quantize_e4m3fn,
+    cache_rows_view,
+    cache_append,
+    mla_kv_pack,
+)

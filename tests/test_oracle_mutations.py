@@ -40,10 +40,26 @@ MUTATIONS = [
 ]
 
 
-def _run_pins(tmp_root):
+# (original text in oracle/cache.py, planted mistake), caught by tests/test_oracle_cache.py
+CACHE_MUTATIONS = [
+    ("take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))", "take_hi = (d_hi <= d_lo)"),   # ties away
+    ("return np.where(np.isnan(y), np.uint8(0x7F), out)",
+     "return np.where(np.isnan(y) | (np.abs(y) > E4M3_MAX), np.uint8(0x7F), out)"),            # overflow to NaN
+    ("y = np.asarray(x, dtype=np.float32) / np.float32(scale)",
+     "y = np.asarray(x, dtype=np.float64) / float(scale)"),                                    # exact quotient
+    ("y = np.asarray(x, dtype=np.float32) / np.float32(scale)",
+     "y = np.asarray(x, dtype=np.float32) * np.float32(scale)"),                               # scale multiplies
+    ("(1.0 + m / 8.0) * 2.0 ** (e - 7)", "(1.0 + m / 8.0) * 2.0 ** (e - 8)"),                  # FNUZ bias
+    ("row = int(layer_base_rows) + max(int(slot), 0)", "row = max(int(layer_base_rows) + int(slot), 0)"),  # clamp after base
+    ("k = np.concatenate([widen_bf16(k_nope), rope], axis=-1)",
+     "k = np.concatenate([rope, widen_bf16(k_nope)], axis=-1)"),                               # rope first
+]
+
+
+def _run_pins(tmp_root, test_file="test_oracle.py"):
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                           os.path.join("tests", "test_oracle.py")],
+                           os.path.join("tests", test_file)],
                           cwd=tmp_root, env=env, capture_output=True, text=True, timeout=600)
 
 
@@ -65,3 +81,18 @@ def test_planted_mistake_is_caught(idx, tmp_path):
         assert result.returncode == 0, result.stdout[-2000:]
     else:
         assert result.returncode != 0, f"planted mistake survived the pins: {planted!r}"
+
+
+@pytest.mark.parametrize("idx", range(len(CACHE_MUTATIONS)))
+def test_planted_cache_mistake_is_caught(idx, tmp_path):
+    original, planted = CACHE_MUTATIONS[idx]
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle")
+    (tmp_path / "tests").mkdir()
+    for name in ("conftest.py", "test_oracle_cache.py"):
+        shutil.copy(os.path.join(ROOT, "tests", name), tmp_path / "tests" / name)
+    src_path = tmp_path / "oracle" / "cache.py"
+    src = src_path.read_text()
+    assert original in src, "mutation anchor not found; update the list"
+    src_path.write_text(src.replace(original, planted, 1))
+    result = _run_pins(tmp_path, "test_oracle_cache.py")
+    assert result.returncode != 0, f"planted mistake survived the pins: {planted!r}"
