@@ -163,6 +163,54 @@ def secondary_mla(kv_dtype: str, steps: int) -> dict:
                          "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
 
 
+def secondary_mla_pack(steps: int) -> dict:
+    """MLA K/V pack + FP8 quantise at the TokenSpeed-MLA prefill shape (8K
+    tokens, 128 heads, K = 128 nope + 64 rope, V = 128): HBM-bound."""
+    import torch
+    import softmax_attention_paged_amd as sap
+    from softmax_attention_paged_amd import inputs
+    case = inputs.pack_case(num_tokens=8192, heads=128, seed=7, strided=True)
+    c = case.to("cuda:0")
+    t, h, dn = case.k_nope.shape
+    dr, dv = case.k_rope.shape[1], case.v.shape[2]
+    k_out = torch.empty((t, h, dn + dr), dtype=torch.float8_e4m3fn, device="cuda:0")
+    v_out = torch.empty((t, h, dv), dtype=torch.float8_e4m3fn, device="cuda:0")
+    fn = lambda: sap.mla_kv_pack_fp8(c.k_nope, c.k_rope, c.v, k_scale=c.k_scale, v_scale=c.v_scale,
+                                     k_out=k_out, v_out=v_out)
+    for _ in range(3):
+        fn()
+    ms = time_events(fn, steps, torch.cuda.current_stream())
+    alg = t * h * (dn + dv) * 2 + t * dr * 2 + t * h * (dn + dr + dv)    # bf16 in (rope once), E4M3 out
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": f"mla_kv_pack_fp8_t{t}_h{h}_d{dn}+{dr}_v{dv}", "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "kernel": "mla_kv_pack_kernel", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": alg}}
+
+
+def secondary_append(steps: int) -> dict:
+    """K/V cache append of an 8K-token prefill chunk (8 KV heads of 128, as
+    in the Qwen3-14B-shaped decode) into a 128-row-page bf16 cache."""
+    import torch
+    import softmax_attention_paged_amd as sap
+    from softmax_attention_paged_amd import inputs
+    case = inputs.append_case(num_tokens=8192, hkv=8, dk=128, dv=128, page_size=128, pages_per_layer=1024,
+                              layers=1, layer=0, seed=8)
+    c = case.to("cuda:0")
+    fn = lambda: sap.cache_append(c.k_new, c.v_new, c.k_cache, c.v_cache, c.slot_mapping,
+                                  layer_base_rows=c.layer_base_rows)
+    for _ in range(3):
+        fn()
+    ms = time_events(fn, steps, torch.cuda.current_stream())
+    n, hkv, dk = case.k_new.shape
+    alg = 2 * (n * hkv * dk * 2) * 2 + n * 8                            # K and V read and written, slots
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": f"cache_append_bf16_n{n}_hkv{hkv}_d{dk}_ps128", "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "kernel": "cache_append_kernel<false>", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": alg}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +251,8 @@ def main() -> int:
         "ragged_paged_prefill_80k": lambda steps: secondary_prefill(inputs.ragged_paged_prefill, steps),
         "mla_decode_80k_bf16": lambda steps: secondary_mla("bf16", steps),
         "mla_decode_80k_fp8_e4m3": lambda steps: secondary_mla("fp8_e4m3", steps),
+        "mla_kv_pack_fp8_8k": secondary_mla_pack,
+        "cache_append_8k": secondary_append,
     }
     if args.only:
         print(json.dumps({args.only: secondaries[args.only](args.steps)}), flush=True)

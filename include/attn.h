@@ -235,6 +235,99 @@ attn_status_t attn_merge_lse(const float *o_parts, const float *lse_parts,
                              void *o, attn_dtype_t o_dtype, float *lse_out,
                              hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * K/V cache append: the step before a decode reads the cache ("Writing Page
+ * Attention with PyPTO", section 4.2: the current token's K and V go to the
+ * cache slot slot_mapping names; section 4.3: the slot is clamped at zero
+ * BEFORE the layer base is added, so a warm-up slot of -1 writes row 0 of
+ * the layer and never the last row of the previous layer; section 9.2: the
+ * layer base selects one layer of a packed multi-layer cache).
+ *
+ *   k_new      bf16 [num_tokens, Hkv, Dk], strides k_new_stride_tok /
+ *              k_new_stride_head.
+ *   v_new      bf16 [num_tokens, Hkv, Dv], strides v_new_stride_*; NULL
+ *              when the cache has no separate V (a latent cache, whose V is
+ *              the first Dv entries of each K row).
+ *   k_cache, v_cache   paged caches in cache_dtype viewed as token rows: row r
+ *              is slot r % page_size of page r / page_size, at
+ *              page * *_stride_page + slot * *_stride_tok + head *
+ *              *_stride_head. v_cache is ignored when v_new is NULL.
+ *   cache_dtype ATTN_BF16 (the bits are copied) or ATTN_FP8_E4M3: code =
+ *              the E4M3 value nearest to x / scale (binary32 quotient,
+ *              ties to even, |x / scale| > 448 saturating to +-448), with
+ *              k_scale / v_scale > 0; the scales must be 1.0 for bf16.
+ *   slot_mapping int64 [num_tokens] (device): row of token i within the
+ *              layer; a negative entry is taken as 0.
+ *   layer_base_rows   first token row of the layer (>= 0).
+ *   num_cache_rows    token rows the cache holds (pages * page_size); a
+ *              token whose row layer_base_rows + max(slot, 0) is at or past
+ *              it is not written (a bound check, not an error: device
+ *              contents are never read on the host).
+ * Tokens that address the same row race: each 8-element piece of the row
+ * ends up holding the same piece of one of them. NaN inputs give an
+ * unspecified code in FP8 caches.
+ * Supported: Dk, Dv multiples of 8 and <= 1024; page_size a power of two;
+ * 16-byte aligned rows (8-byte aligned for FP8 caches).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *k_new;
+  int64_t k_new_stride_tok, k_new_stride_head;
+  const void *v_new;
+  int64_t v_new_stride_tok, v_new_stride_head;
+  void *k_cache;
+  int64_t k_stride_page, k_stride_tok, k_stride_head;
+  void *v_cache;
+  int64_t v_stride_page, v_stride_tok, v_stride_head;
+  attn_dtype_t cache_dtype;
+  float k_scale, v_scale;
+  const int64_t *slot_mapping;
+  int64_t layer_base_rows;
+  int64_t num_cache_rows;
+  int32_t num_tokens, num_kv_heads, head_dim_k, head_dim_v;
+  int32_t page_size;
+} attn_cache_append_params;
+
+/* Enqueue the append. ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED or
+ * ATTN_ERR_HIP. num_tokens == 0 enqueues nothing. */
+attn_status_t attn_cache_append(const attn_cache_append_params *p, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MLA K/V pack + FP8 quantise ("TokenSpeed-MLA", kernel capability summary:
+ * one fused kernel in place of concatenate + cast + cast in chunked prefill,
+ * strided inputs and caller-provided outputs).
+ *
+ *   k_nope     bf16 [num_tokens, H, d_nope], strides k_nope_stride_tok/_head.
+ *   k_rope     bf16 [num_tokens, d_rope], stride k_rope_stride_tok: one
+ *              vector per token, shared by every head.
+ *   v          bf16 [num_tokens, H, d_v], strides v_stride_tok/_head.
+ *   k_out      E4M3 codes [num_tokens, H, d_nope + d_rope]: per head the
+ *              d_nope entries of k_nope, then the token's d_rope entries.
+ *   v_out      E4M3 codes [num_tokens, H, d_v].
+ *   k_scale, v_scale  per-tensor scales (> 0): code = E4M3(x / scale) with
+ *              the rounding and saturation of attn_cache_append (NaN
+ *              inputs give an unspecified code).
+ * Supported: d_nope, d_rope, d_v multiples of 8; 16-byte aligned input rows
+ * and 8-byte aligned output rows; per-head strides below 2^24 elements.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *k_nope;
+  int64_t k_nope_stride_tok, k_nope_stride_head;
+  const void *k_rope;
+  int64_t k_rope_stride_tok;
+  const void *v;
+  int64_t v_stride_tok, v_stride_head;
+  void *k_out;
+  int64_t k_out_stride_tok, k_out_stride_head;
+  void *v_out;
+  int64_t v_out_stride_tok, v_out_stride_head;
+  float k_scale, v_scale;
+  int32_t num_tokens, num_heads, d_nope, d_rope, d_v;
+} attn_mla_kv_pack_params;
+
+/* Enqueue the pack. ATTN_OK, ATTN_ERR_INVALID_ARG or ATTN_ERR_HIP.
+ * num_tokens == 0 enqueues nothing. */
+attn_status_t attn_mla_kv_pack_fp8(const attn_mla_kv_pack_params *p, hipStream_t stream);
+
 /* Static name of a status code. */
 const char *attn_status_string(attn_status_t s);
 

@@ -5,5 +5,7 @@ The Python layer only marshals torch tensors into the C ABI. The HIP library
 must be built in-tree first (python -m softmax_attention_paged_amd.build).
 """
 
-from .api import decode_paged, decode_params, decode_plan, default_scale, merge_lse, prefill  # noqa: F401
+from .api import (  # noqa: F401
+    cache_append, decode_paged, decode_params, decode_plan, default_scale, merge_lse, mla_kv_pack_fp8, prefill,
+)
 from ._ffi import AttnError, LIB_PATH, load  # noqa: F401

@@ -70,12 +70,39 @@ class DecodePlanInfo(ctypes.Structure):
     ]
 
 
+class CacheAppendParams(ctypes.Structure):
+    _fields_ = [
+        ("k_new", _p), ("k_new_stride_tok", _i64), ("k_new_stride_head", _i64),
+        ("v_new", _p), ("v_new_stride_tok", _i64), ("v_new_stride_head", _i64),
+        ("k_cache", _p), ("k_stride_page", _i64), ("k_stride_tok", _i64), ("k_stride_head", _i64),
+        ("v_cache", _p), ("v_stride_page", _i64), ("v_stride_tok", _i64), ("v_stride_head", _i64),
+        ("cache_dtype", ctypes.c_int), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("slot_mapping", _p), ("layer_base_rows", _i64), ("num_cache_rows", _i64),
+        ("num_tokens", _i32), ("num_kv_heads", _i32), ("head_dim_k", _i32), ("head_dim_v", _i32),
+        ("page_size", _i32),
+    ]
+
+
+class MlaKvPackParams(ctypes.Structure):
+    _fields_ = [
+        ("k_nope", _p), ("k_nope_stride_tok", _i64), ("k_nope_stride_head", _i64),
+        ("k_rope", _p), ("k_rope_stride_tok", _i64),
+        ("v", _p), ("v_stride_tok", _i64), ("v_stride_head", _i64),
+        ("k_out", _p), ("k_out_stride_tok", _i64), ("k_out_stride_head", _i64),
+        ("v_out", _p), ("v_out_stride_tok", _i64), ("v_out_stride_head", _i64),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("num_tokens", _i32), ("num_heads", _i32), ("d_nope", _i32), ("d_rope", _i32), ("d_v", _i32),
+    ]
+
+
 EXPORTS = {
     "attn_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillParams), _p]),
     "attn_decode_plan": (ctypes.c_int, [ctypes.POINTER(DecodeParams), ctypes.POINTER(DecodePlanInfo)]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(DecodeParams)]),
     "attn_decode_paged": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
     "attn_merge_lse": (ctypes.c_int, [_p, _p, _i32, _i64, _i32, _p, ctypes.c_int, _p, _p]),
+    "attn_cache_append": (ctypes.c_int, [ctypes.POINTER(CacheAppendParams), _p]),
+    "attn_mla_kv_pack_fp8": (ctypes.c_int, [ctypes.POINTER(MlaKvPackParams), _p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_last_error": (ctypes.c_char_p, []),
 }

@@ -196,3 +196,71 @@ def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out_dtype=_BF16
 
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+# --------------------------------------------------------------------------
+# The prologue: cache append and the MLA K/V pack
+# --------------------------------------------------------------------------
+
+def _cache_rows(cache: torch.Tensor) -> tuple[int, int, int, int]:
+    """(page_size, stride_page, stride_tok, stride_head) of a paged cache
+    [pages, page_size, Hkv, D] (a latent [pages, page_size, D] has one head)."""
+    c = _as_4d_cache(cache)
+    return c.shape[1], c.stride(0), c.stride(1), c.stride(2)
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, slot_mapping, *, layer_base_rows=0, k_scale=1.0,
+                 v_scale=1.0, kv_dtype: str | None = None):
+    """Write new tokens k_new / v_new [N, Hkv, D] (bf16) into the paged caches
+    at token row layer_base_rows + max(slot_mapping[i], 0) (int64 [N]). FP8
+    caches (float8_e4m3fn, or uint8 with kv_dtype='fp8_e4m3') store E4M3
+    codes of value / scale. v_new / v_cache may be None (latent caches)."""
+    _need(k_new.dtype == _BF16 and (v_new is None or v_new.dtype == _BF16), "new K/V must be bf16")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
+    _need((v_new is None) == (v_cache is None), "v_new and v_cache go together")
+    kc = _as_4d_cache(k_cache)
+    code = _kv_code(kc, kv_dtype)
+    ps, ksp, kst, ksh = _cache_rows(kc)
+    p = _ffi.CacheAppendParams()
+    p.k_new, p.k_new_stride_tok, p.k_new_stride_head = k_new.data_ptr(), k_new.stride(0), k_new.stride(1)
+    p.k_cache, p.k_stride_page, p.k_stride_tok, p.k_stride_head = kc.data_ptr(), ksp, kst, ksh
+    if v_new is not None:
+        vc = _as_4d_cache(v_cache)
+        _, vsp, vst, vsh = _cache_rows(vc)
+        p.v_new, p.v_new_stride_tok, p.v_new_stride_head = v_new.data_ptr(), v_new.stride(0), v_new.stride(1)
+        p.v_cache, p.v_stride_page, p.v_stride_tok, p.v_stride_head = vc.data_ptr(), vsp, vst, vsh
+        p.head_dim_v = v_new.shape[2]
+    p.cache_dtype = code
+    p.k_scale, p.v_scale = float(k_scale), float(v_scale)
+    p.slot_mapping = slot_mapping.data_ptr()
+    p.layer_base_rows = int(layer_base_rows)
+    p.num_cache_rows = kc.shape[0] * kc.shape[1]
+    p.num_tokens, p.num_kv_heads, p.head_dim_k = k_new.shape[0], k_new.shape[1], k_new.shape[2]
+    p.page_size = ps
+    _ffi.check(_ffi.load().attn_cache_append(ctypes.byref(p), _stream(k_new.device)), "attn_cache_append")
+
+
+def mla_kv_pack_fp8(k_nope, k_rope, v, *, k_scale=1.0, v_scale=1.0, k_out=None, v_out=None):
+    """K = concat(k_nope [T, H, dn], k_rope [T, dr] shared by all heads) and V
+    [T, H, dv] as E4M3 codes of value / scale (float8_e4m3fn tensors
+    [T, H, dn + dr] and [T, H, dv]; pre-allocated outputs may be passed)."""
+    _need(k_nope.dtype == _BF16 and k_rope.dtype == _BF16 and v.dtype == _BF16, "inputs must be bf16")
+    if k_rope.dim() == 3:
+        _need(k_rope.shape[1] == 1, "k_rope must be [T, dr] or [T, 1, dr]")
+        k_rope = k_rope[:, 0, :]
+    t, h, dn = k_nope.shape
+    dr, dv = k_rope.shape[1], v.shape[2]
+    if k_out is None:
+        k_out = torch.empty((t, h, dn + dr), dtype=torch.float8_e4m3fn, device=k_nope.device)
+    if v_out is None:
+        v_out = torch.empty((t, h, dv), dtype=torch.float8_e4m3fn, device=k_nope.device)
+    p = _ffi.MlaKvPackParams()
+    p.k_nope, p.k_nope_stride_tok, p.k_nope_stride_head = k_nope.data_ptr(), k_nope.stride(0), k_nope.stride(1)
+    p.k_rope, p.k_rope_stride_tok = k_rope.data_ptr(), k_rope.stride(0)
+    p.v, p.v_stride_tok, p.v_stride_head = v.data_ptr(), v.stride(0), v.stride(1)
+    p.k_out, p.k_out_stride_tok, p.k_out_stride_head = k_out.data_ptr(), k_out.stride(0), k_out.stride(1)
+    p.v_out, p.v_out_stride_tok, p.v_out_stride_head = v_out.data_ptr(), v_out.stride(0), v_out.stride(1)
+    p.k_scale, p.v_scale = float(k_scale), float(v_scale)
+    p.num_tokens, p.num_heads, p.d_nope, p.d_rope, p.d_v = t, h, dn, dr, dv
+    _ffi.check(_ffi.load().attn_mla_kv_pack_fp8(ctypes.byref(p), _stream(k_nope.device)), "attn_mla_kv_pack_fp8")
+    return k_out, v_out

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "attn_internal.h"
 
@@ -441,6 +442,136 @@ attn_status_t attn_merge_lse(const float *o_parts, const float *lse_parts, int32
   m.lse = lse_out;
   hipError_t err = attn::launch_merge(m, stream);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(err));
+  return ok();
+}
+
+attn_status_t attn_cache_append(const attn_cache_append_params *p, hipStream_t stream) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "num_tokens < 0");
+  if (p->num_kv_heads < 1) return fail(ATTN_ERR_INVALID_ARG, "num_kv_heads < 1");
+  const bool has_v = p->v_new != nullptr;
+  for (int d : {p->head_dim_k, has_v ? p->head_dim_v : 8})
+    if (d < 8 || d > 1024 || d % 8) return fail(ATTN_ERR_UNSUPPORTED, "head dims must be multiples of 8 in 8..1024");
+  if (p->cache_dtype != ATTN_BF16 && p->cache_dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_ERR_UNSUPPORTED, "cache_dtype must be bf16 or fp8 e4m3");
+  const bool fp8 = p->cache_dtype == ATTN_FP8_E4M3;
+  if (fp8) {
+    if (!(std::isfinite(p->k_scale) && p->k_scale > 0.f) || (has_v && !(std::isfinite(p->v_scale) && p->v_scale > 0.f)))
+      return fail(ATTN_ERR_INVALID_ARG, "fp8 scales must be finite and > 0");
+  } else if (p->k_scale != 1.f || (has_v && p->v_scale != 1.f)) {
+    return fail(ATTN_ERR_INVALID_ARG, "bf16 caches take scales of 1.0");
+  }
+  if (!pow2(p->page_size)) return fail(ATTN_ERR_INVALID_ARG, "page_size must be a power of two");
+  if (p->layer_base_rows < 0 || p->num_cache_rows < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "layer_base_rows and num_cache_rows must be >= 0");
+  if (p->num_tokens == 0) return ok();
+  if (!p->k_new || !p->k_cache || !p->slot_mapping || (has_v && !p->v_cache))
+    return fail(ATTN_ERR_INVALID_ARG, "k_new, k_cache, slot_mapping (and v_cache with v_new) are required");
+  if ((reinterpret_cast<uintptr_t>(p->slot_mapping) & 7u) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  // every 8-element chunk starts 16-byte aligned in the inputs, and 16-byte
+  // (bf16) or 8-byte (fp8) aligned in the cache
+  const uintptr_t cache_align = fp8 ? 7u : 15u;
+  auto chunk_ok = [&](const void *ptr, uintptr_t mask, std::initializer_list<int64_t> strides) {
+    if (reinterpret_cast<uintptr_t>(ptr) & mask) return false;
+    for (int64_t st : strides)
+      if (st < 0 || st % 8) return false;
+    return true;
+  };
+  if (!chunk_ok(p->k_new, 15u, {p->k_new_stride_tok, p->k_new_stride_head}) ||
+      (has_v && !chunk_ok(p->v_new, 15u, {p->v_new_stride_tok, p->v_new_stride_head})))
+    return fail(ATTN_ERR_INVALID_ARG, "k_new/v_new need 16-byte aligned rows and non-negative strides that are multiples of 8");
+  if (!chunk_ok(p->k_cache, cache_align, {p->k_stride_page, p->k_stride_tok, p->k_stride_head}) ||
+      (has_v && !chunk_ok(p->v_cache, cache_align, {p->v_stride_page, p->v_stride_tok, p->v_stride_head})))
+    return fail(ATTN_ERR_INVALID_ARG, "cache rows must be aligned to 8 elements with non-negative strides that are multiples of 8");
+  attn::CacheAppendArgs a{};
+  a.k_new = p->k_new;
+  a.v_new = p->v_new;
+  a.k_new_stride_tok = p->k_new_stride_tok;
+  a.k_new_stride_head = p->k_new_stride_head;
+  a.v_new_stride_tok = p->v_new_stride_tok;
+  a.v_new_stride_head = p->v_new_stride_head;
+  a.k_cache = p->k_cache;
+  a.v_cache = p->v_cache;
+  a.k_stride_page = p->k_stride_page;
+  a.k_stride_tok = p->k_stride_tok;
+  a.k_stride_head = p->k_stride_head;
+  a.v_stride_page = p->v_stride_page;
+  a.v_stride_tok = p->v_stride_tok;
+  a.v_stride_head = p->v_stride_head;
+  a.fp8 = fp8;
+  a.k_scale = p->k_scale;
+  a.v_scale = p->v_scale;
+  a.slot_mapping = p->slot_mapping;
+  a.layer_base_rows = p->layer_base_rows;
+  a.num_cache_rows = p->num_cache_rows;
+  a.num_tokens = p->num_tokens;
+  a.num_kv_heads = p->num_kv_heads;
+  a.head_dim_k = p->head_dim_k;
+  a.head_dim_v = has_v ? p->head_dim_v : 0;
+  a.page_shift = log2i(p->page_size);
+  hipError_t err = attn::launch_cache_append(a, stream);
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "cache append launch: %s", hipGetErrorString(err));
+  return ok();
+}
+
+attn_status_t attn_mla_kv_pack_fp8(const attn_mla_kv_pack_params *p, hipStream_t stream) {
+  if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_tokens < 0 || p->num_heads < 1) return fail(ATTN_ERR_INVALID_ARG, "num_tokens < 0 or num_heads < 1");
+  if (p->d_nope < 8 || p->d_rope < 0 || p->d_v < 8 || p->d_nope % 8 || p->d_rope % 8 || p->d_v % 8 ||
+      p->d_nope + p->d_rope > 4096 || p->d_v > 4096)
+    return fail(ATTN_ERR_INVALID_ARG, "d_nope, d_v >= 8 and d_rope >= 0 must be multiples of 8 (<= 4096)");
+  if (!(std::isfinite(p->k_scale) && p->k_scale > 0.f && std::isfinite(p->v_scale) && p->v_scale > 0.f))
+    return fail(ATTN_ERR_INVALID_ARG, "scales must be finite and > 0");
+  if (p->num_tokens == 0) return ok();
+  if (!p->k_nope || !p->v || !p->k_out || !p->v_out || (p->d_rope > 0 && !p->k_rope))
+    return fail(ATTN_ERR_INVALID_ARG, "k_nope, k_rope, v, k_out and v_out are required");
+  auto ok_in = [](const void *ptr, std::initializer_list<int64_t> strides) {
+    if (reinterpret_cast<uintptr_t>(ptr) & 15u) return false;
+    for (int64_t st : strides)
+      if (st < 0 || st % 8) return false;
+    return true;
+  };
+  auto ok_out = [](const void *ptr, std::initializer_list<int64_t> strides) {
+    if (reinterpret_cast<uintptr_t>(ptr) & 7u) return false;
+    for (int64_t st : strides)
+      if (st < 0 || st % 8) return false;
+    return true;
+  };
+  if (!ok_in(p->k_nope, {p->k_nope_stride_tok, p->k_nope_stride_head}) || !ok_in(p->v, {p->v_stride_tok, p->v_stride_head}) ||
+      (p->d_rope > 0 && !ok_in(p->k_rope, {p->k_rope_stride_tok})))
+    return fail(ATTN_ERR_INVALID_ARG, "inputs need 16-byte aligned rows and non-negative strides that are multiples of 8");
+  if (!ok_out(p->k_out, {p->k_out_stride_tok, p->k_out_stride_head}) || !ok_out(p->v_out, {p->v_out_stride_tok, p->v_out_stride_head}))
+    return fail(ATTN_ERR_INVALID_ARG, "outputs need 8-byte aligned rows and non-negative strides that are multiples of 8");
+  // the kernel addresses rows within a token with 24-bit multiplies
+  for (int64_t st : {p->k_nope_stride_head, p->v_stride_head, p->k_out_stride_head, p->v_out_stride_head})
+    if (st >= (int64_t(1) << 24) || int64_t(p->num_heads) * st + 4096 >= (int64_t(1) << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "per-head strides must be below 2^24 elements and one token's rows below 2^31");
+  if (p->num_heads >= (1 << 24)) return fail(ATTN_ERR_UNSUPPORTED, "num_heads must be below 2^24");
+  attn::MlaPackArgs a{};
+  a.k_nope = p->k_nope;
+  a.k_rope = p->k_rope;
+  a.v = p->v;
+  a.k_nope_stride_tok = p->k_nope_stride_tok;
+  a.k_nope_stride_head = p->k_nope_stride_head;
+  a.k_rope_stride_tok = p->k_rope_stride_tok;
+  a.v_stride_tok = p->v_stride_tok;
+  a.v_stride_head = p->v_stride_head;
+  a.k_out = p->k_out;
+  a.v_out = p->v_out;
+  a.k_out_stride_tok = p->k_out_stride_tok;
+  a.k_out_stride_head = p->k_out_stride_head;
+  a.v_out_stride_tok = p->v_out_stride_tok;
+  a.v_out_stride_head = p->v_out_stride_head;
+  a.k_scale = p->k_scale;
+  a.v_scale = p->v_scale;
+  a.num_tokens = p->num_tokens;
+  a.num_heads = p->num_heads;
+  a.d_nope = p->d_nope;
+  a.d_rope = p->d_rope;
+  a.d_v = p->d_v;
+  hipError_t err = attn::launch_mla_kv_pack(a, stream);
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "MLA K/V pack launch: %s", hipGetErrorString(err));
   return ok();
 }
 

@@ -92,11 +92,40 @@ struct PrefillArgs {
   float *lse;
 };
 
+// K/V cache append, validated: row of token i = layer_base + max(slot[i], 0).
+struct CacheAppendArgs {
+  const void *k_new, *v_new;     // bf16; v_new null: K only
+  int64_t k_new_stride_tok, k_new_stride_head;
+  int64_t v_new_stride_tok, v_new_stride_head;
+  void *k_cache, *v_cache;
+  int64_t k_stride_page, k_stride_tok, k_stride_head;
+  int64_t v_stride_page, v_stride_tok, v_stride_head;
+  int32_t fp8;                   // 1: E4M3 codes, 0: bf16
+  float k_scale, v_scale;
+  const int64_t *slot_mapping;
+  int64_t layer_base_rows, num_cache_rows;
+  int32_t num_tokens, num_kv_heads, head_dim_k, head_dim_v;
+  int32_t page_shift;
+};
+
+// MLA K/V pack: K = concat(k_nope[t, h], k_rope[t]) and V, quantised to E4M3.
+struct MlaPackArgs {
+  const void *k_nope, *k_rope, *v;
+  int64_t k_nope_stride_tok, k_nope_stride_head, k_rope_stride_tok;
+  int64_t v_stride_tok, v_stride_head;
+  void *k_out, *v_out;
+  int64_t k_out_stride_tok, k_out_stride_head, v_out_stride_tok, v_out_stride_head;
+  float k_scale, v_scale;
+  int32_t num_tokens, num_heads, d_nope, d_rope, d_v;
+};
+
 // Launchers; each returns hipSuccess or the launch error.
 hipError_t launch_decode_gqa(const DecodeGqaArgs &a, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeMlaArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_cache_append(const CacheAppendArgs &a, hipStream_t stream);
+hipError_t launch_mla_kv_pack(const MlaPackArgs &a, hipStream_t stream);
 
 // Kernel geometry the planner needs.
 constexpr int kGqaRowsPerTile = 16;   // MFMA N rows of the GQA decode kernel

@@ -359,3 +359,108 @@ def sha256_of(*tensors) -> str:
             h.update(t.contiguous().view(torch.uint8).numpy().tobytes() if t.dtype != torch.uint8
                      else t.contiguous().numpy().tobytes())
     return h.hexdigest()
+
+
+# --------------------------------------------------------------------------
+# The prologue: cache append and the MLA K/V pack
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class AppendCase:
+    name: str
+    k_new: torch.Tensor                 # bf16 [N, Hkv, Dk]
+    v_new: torch.Tensor | None          # bf16 [N, Hkv, Dv] (None: latent cache)
+    k_cache: torch.Tensor               # [pages, page_size, Hkv, Dk] bf16, or uint8 E4M3 codes
+    v_cache: torch.Tensor | None
+    slot_mapping: torch.Tensor          # int64 [N]: row within the layer, -1 for warm-up tokens
+    layer_base_rows: int
+    page_size: int
+    kv_dtype: str                       # "bf16" or "fp8_e4m3"
+    k_scale: float
+    v_scale: float
+    seed: int
+
+    def to(self, device) -> "AppendCase":
+        f = lambda t: None if t is None else t.to(device)
+        return dataclasses.replace(self, k_new=f(self.k_new), v_new=f(self.v_new), k_cache=f(self.k_cache),
+                                   v_cache=f(self.v_cache), slot_mapping=f(self.slot_mapping))
+
+
+def append_case(*, num_tokens: int, hkv: int, dk: int, dv: int | None, page_size: int, pages_per_layer: int,
+                layers: int = 2, layer: int = 1, kv_dtype: str = "bf16", warmup_tokens: int = 0,
+                seed: int, name: str = "") -> AppendCase:
+    """New tokens for one layer of a packed multi-layer paged cache.
+
+    The cache holds `layers` layers of pages_per_layer pages each, every byte
+    drawn at random (a canary: any write shows). Slots are distinct random
+    rows of the layer; the first warmup_tokens tokens get slot -1. FP8
+    caches use one scale per tensor of amax / 400 (so the largest values of
+    each tensor saturate at 448)."""
+    s_layout, _, s_k, s_v = _streams(seed)
+    rng = np.random.Generator(np.random.PCG64(s_layout))
+    rows = pages_per_layer * page_size
+    slots = rng.choice(rows, size=num_tokens, replace=False).astype(np.int64)
+    slots[:warmup_tokens] = -1
+    k = _normal_f32(s_k, (num_tokens, hkv, dk))
+    v = None if dv is None else _normal_f32(s_v, (num_tokens, hkv, dv))
+    cache_rng = np.random.Generator(np.random.PCG64(s_layout.spawn(1)[0]))
+    total_pages = layers * pages_per_layer
+    if kv_dtype == "bf16":
+        draw = lambda d: torch.from_numpy(cache_rng.integers(0, 1 << 16, size=(total_pages, page_size, hkv, d),
+                                                             dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+        k_scale = v_scale = 1.0
+    elif kv_dtype == "fp8_e4m3":
+        draw = lambda d: torch.from_numpy(cache_rng.integers(0, 256, size=(total_pages, page_size, hkv, d),
+                                                             dtype=np.uint8))
+        k_scale = float(np.abs(k).max()) / 400.0
+        v_scale = 1.0 if v is None else float(np.abs(v).max()) / 400.0
+    else:
+        raise ValueError(kv_dtype)
+    kc = draw(dk)
+    vc = None if dv is None else draw(dv)
+    return AppendCase(name=name, k_new=torch.from_numpy(k).to(torch.bfloat16),
+                      v_new=None if v is None else torch.from_numpy(v).to(torch.bfloat16),
+                      k_cache=kc, v_cache=vc, slot_mapping=torch.from_numpy(slots),
+                      layer_base_rows=layer * rows, page_size=page_size, kv_dtype=kv_dtype,
+                      k_scale=k_scale, v_scale=v_scale, seed=seed)
+
+
+@dataclasses.dataclass
+class PackCase:
+    name: str
+    k_nope: torch.Tensor     # bf16 [T, H, dn] (possibly a strided view)
+    k_rope: torch.Tensor     # bf16 [T, dr] (possibly a strided view)
+    v: torch.Tensor          # bf16 [T, H, dv] (possibly a strided view)
+    k_scale: float
+    v_scale: float
+    seed: int
+
+    def to(self, device) -> "PackCase":
+        return dataclasses.replace(self, k_nope=self.k_nope.to(device), k_rope=self.k_rope.to(device),
+                                   v=self.v.to(device))
+
+
+def pack_case(*, num_tokens: int, heads: int, d_nope: int = 128, d_rope: int = 64, d_v: int = 128,
+              seed: int, strided: bool = False, name: str = "") -> PackCase:
+    """Chunked-prefill MLA inputs: k_nope, a per-token rope vector, V. With
+    strided=True each is a view into a wider buffer (the layouts a fused
+    kv_b projection leaves: k_nope and v side by side per head, rope with a
+    padded row). Scales are amax / 448 per tensor (K over nope and rope)."""
+    _, s_q, s_k, s_v = _streams(seed)
+    if strided:
+        kv = _normal_f32(s_k, (num_tokens, heads, d_nope + d_v))
+        rope_buf = _normal_f32(s_q, (num_tokens, 1, d_rope + 16))
+        k_nope_f, v_f, rope_f = kv[:, :, :d_nope], kv[:, :, d_nope:], rope_buf[:, 0, :d_rope]
+        t_kv = torch.from_numpy(kv).to(torch.bfloat16)
+        t_rope = torch.from_numpy(rope_buf).to(torch.bfloat16)
+        k_nope_t, v_t, rope_t = t_kv[:, :, :d_nope], t_kv[:, :, d_nope:], t_rope[:, 0, :d_rope]
+    else:
+        k_nope_f = _normal_f32(s_k, (num_tokens, heads, d_nope))
+        v_f = _normal_f32(s_v, (num_tokens, heads, d_v))
+        rope_f = _normal_f32(s_q, (num_tokens, d_rope))
+        k_nope_t = torch.from_numpy(k_nope_f).to(torch.bfloat16)
+        v_t = torch.from_numpy(v_f).to(torch.bfloat16)
+        rope_t = torch.from_numpy(rope_f).to(torch.bfloat16)
+    k_amax = max(float(np.abs(k_nope_f).max()), float(np.abs(rope_f).max()) if d_rope else 0.0)
+    return PackCase(name=name, k_nope=k_nope_t, k_rope=rope_t, v=v_t, k_scale=k_amax / FP8_MAX,
+                    v_scale=float(np.abs(v_f).max()) / FP8_MAX, seed=seed)

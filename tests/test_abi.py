@@ -35,6 +35,36 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_ffi.EXPORTS), "binding and header disagree"
 
 
+def test_ctypes_mirrors_match_the_c_compiler_layout(tmp_path):
+    # gcc compiles a probe against include/attn.h that prints sizeof and the
+    # offset of every field the ctypes mirrors declare; the two must agree.
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    structs = {"attn_prefill_params": _ffi.PrefillParams, "attn_decode_params": _ffi.DecodeParams,
+               "attn_decode_plan_info": _ffi.DecodePlanInfo, "attn_cache_append_params": _ffi.CacheAppendParams,
+               "attn_mla_kv_pack_params": _ffi.MlaKvPackParams}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{os.path.join(ROOT, "include", "attn.h")}"',
+             "int main(void) {"]
+    expect = []
+    for cname, cls in structs.items():
+        lines.append(f'  printf("%zu\\n", sizeof({cname}));')
+        expect.append(ctypes.sizeof(cls))
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("%zu\\n", offsetof({cname}, {fname}));')
+            expect.append(getattr(cls, fname).offset)
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    cc = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", str(src), "-o", str(exe)],
+                        capture_output=True, text=True)
+    assert cc.returncode == 0, cc.stderr
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == expect
+
+
 def test_struct_sizes_match_c_layout():
     # ctypes mirrors must match the C layout (checked against offsets the C
     # compiler would use: pointers and int64 are 8-aligned, int32/float 4).
@@ -270,3 +300,82 @@ def test_window_plans_splits_over_the_window():
                                window_left=1000))
     assert st == 0 and g.num_splits * g.split_tokens >= 256     # a window wider than the history
 
+
+
+def append_params(**kw):
+    p = _ffi.CacheAppendParams()
+    d = dict(k_new=FAKE, k_new_stride_tok=8 * 128, k_new_stride_head=128, v_new=FAKE, v_new_stride_tok=8 * 128,
+             v_new_stride_head=128, k_cache=FAKE, k_stride_page=16 * 8 * 128, k_stride_tok=8 * 128,
+             k_stride_head=128, v_cache=FAKE, v_stride_page=16 * 8 * 128, v_stride_tok=8 * 128, v_stride_head=128,
+             cache_dtype=_ffi.ATTN_BF16, k_scale=1.0, v_scale=1.0, slot_mapping=FAKE, layer_base_rows=0,
+             num_cache_rows=1024, num_tokens=4, num_kv_heads=8, head_dim_k=128, head_dim_v=128, page_size=16)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_tokens=-1), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(head_dim_k=100), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(head_dim_v=2048), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(cache_dtype=_ffi.ATTN_FP32), _ffi.ATTN_ERR_UNSUPPORTED),
+    (dict(k_scale=2.0), _ffi.ATTN_ERR_INVALID_ARG),                    # bf16 takes scale 1
+    (dict(cache_dtype=_ffi.ATTN_FP8_E4M3, k_scale=0.0), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(cache_dtype=_ffi.ATTN_FP8_E4M3, v_scale=float("nan")), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(page_size=24), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(layer_base_rows=-16), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(slot_mapping=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(slot_mapping=FAKE + 4), _ffi.ATTN_ERR_INVALID_ARG),          # int64 alignment
+    (dict(k_new=FAKE + 8), _ffi.ATTN_ERR_INVALID_ARG),                 # 16-byte chunks
+    (dict(k_stride_tok=8 * 128 + 4), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(v_cache=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(k_new_stride_head=-128), _ffi.ATTN_ERR_INVALID_ARG),
+])
+def test_cache_append_validation_errors(kw, code):
+    lib = _lib()
+    assert lib.attn_cache_append(ctypes.byref(append_params(**kw)), None) == code
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_cache_append_accepts_a_latent_fp8_cache_without_v_and_zero_tokens():
+    lib = _lib()
+    # FP8 latent cache: 8-byte aligned rows suffice, no V; zero tokens enqueue nothing
+    p = append_params(v_new=None, v_cache=None, head_dim_v=0, cache_dtype=_ffi.ATTN_FP8_E4M3, k_scale=0.5,
+                      head_dim_k=576, k_new_stride_tok=576, k_new_stride_head=576, k_cache=FAKE + 8,
+                      k_stride_page=64 * 576, k_stride_tok=576, k_stride_head=576, num_kv_heads=1, num_tokens=0)
+    assert lib.attn_cache_append(ctypes.byref(p), None) == _ffi.ATTN_OK
+
+
+def pack_params(**kw):
+    p = _ffi.MlaKvPackParams()
+    d = dict(k_nope=FAKE, k_nope_stride_tok=16 * 128, k_nope_stride_head=128, k_rope=FAKE, k_rope_stride_tok=64,
+             v=FAKE, v_stride_tok=16 * 128, v_stride_head=128, k_out=FAKE, k_out_stride_tok=16 * 192,
+             k_out_stride_head=192, v_out=FAKE, v_out_stride_tok=16 * 128, v_out_stride_head=128,
+             k_scale=0.01, v_scale=0.01, num_tokens=0, num_heads=16, d_nope=128, d_rope=64, d_v=128)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads=0), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(d_nope=100), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(d_rope=-8), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(k_scale=0.0), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(v_scale=float("inf")), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_tokens=4, k_rope=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_tokens=4, v=FAKE + 8), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_tokens=4, k_out=FAKE + 4), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_tokens=4, k_out_stride_head=196), _ffi.ATTN_ERR_INVALID_ARG),
+])
+def test_mla_pack_validation_errors(kw, code):
+    lib = _lib()
+    assert lib.attn_mla_kv_pack_fp8(ctypes.byref(pack_params(**kw)), None) == code
+
+
+def test_mla_pack_zero_tokens_and_no_rope_are_accepted():
+    lib = _lib()
+    assert lib.attn_mla_kv_pack_fp8(ctypes.byref(pack_params()), None) == _ffi.ATTN_OK
+    assert lib.attn_mla_kv_pack_fp8(ctypes.byref(pack_params(d_rope=0, k_rope=None)), None) == _ffi.ATTN_OK
