@@ -19,6 +19,8 @@ from .attention import (  # noqa: F401
     decode_paged,
     decode_paged_rows,
     prefill_dense,
+    prefill_dense_fp8,
+    prefill_dense_fp8_rows,
     prefill_paged,
     prefill_paged_rows,
     merge_lse,

@@ -277,6 +277,40 @@ def prefill_dense(q, k, v, cu_seqlens_q, cu_seqlens_kv, scale, causal, window_le
     return o, lse2
 
 
+def prefill_dense_fp8(q_codes, k_codes, v_codes, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_kv,
+                      scale, causal, window_left=-1):
+    """FP8 prefill ("TokenSpeed-MLA": the prefill command's FP8 E4M3 inputs,
+    q and k 192 wide, v 128 wide; kernel capability summary: BF16 output and
+    FP32 LSE): q, k, v are E4M3 codes (uint8) with per-tensor dequantisation
+    scales, value = code * scale; the attention is prefill_dense on those
+    values. Returns o [Tq, Hq, Dv] and lse2 [Tq, Hq]."""
+    return prefill_dense(widen_e4m3fn(q_codes, q_scale), widen_e4m3fn(k_codes, k_scale),
+                         widen_e4m3fn(v_codes, v_scale), cu_seqlens_q, cu_seqlens_kv, scale, causal, window_left)
+
+
+def prefill_dense_fp8_rows(q_codes, k_codes, v_codes, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_kv,
+                           scale, causal, rows, window_left=-1):
+    """prefill_dense_fp8 for the listed (token, head) rows only: ([n, Dv], [n])."""
+    hq, hkv = q_codes.shape[1], k_codes.shape[1]
+    group = hq // hkv
+    cu_q = np.asarray(cu_seqlens_q)
+    cu_k = np.asarray(cu_seqlens_kv)
+    o = np.zeros((len(rows), v_codes.shape[2]), dtype=np.float64)
+    lse2 = np.full(len(rows), NEG_INF, dtype=np.float64)
+    for n, (tok, h) in enumerate(rows):
+        b = int(np.searchsorted(cu_q, tok, side="right") - 1)
+        lq, k0, k1 = int(cu_q[b + 1] - cu_q[b]), int(cu_k[b]), int(cu_k[b + 1])
+        lk, i = k1 - k0, tok - int(cu_q[b])
+        bound = causal_key_bound(np.array([i]), lq, lk) if causal else np.array([lk])
+        start = window_key_start(np.array([i]), lq, lk, window_left)
+        g = h // group
+        oo, ll = attention_rows(widen_e4m3fn(q_codes[tok:tok + 1, h], q_scale),
+                                widen_e4m3fn(k_codes[k0:k1, g], k_scale), widen_e4m3fn(v_codes[k0:k1, g], v_scale),
+                                scale, bound, np.atleast_1d(start))
+        o[n], lse2[n] = oo[0], ll[0]
+    return o, lse2
+
+
 def prefill_paged_rows(q, k_cache, v_cache, cu_seqlens_q, seq_lens_kv, block_table,
                        page_size, scale, causal, head_dim_v, rows, kv_format="f64", q_format="f64",
                        window_left=-1):

@@ -461,3 +461,50 @@ def test_flywheel_static_anchor_tau():
     assert abs(tau - math.log(g["n_keys"]) - g["expect_tau_minus_lnN_about"]) < g["about_tolerance"]
     assert round(tau / math.log(10)) == g["expect_exp_tau_about_pow10"]
     assert oracle.static_anchor_tau(2 ** 40, 2.0 ** 60, 2.0) < g["refuse_below_nats"]
+
+
+# ------------------------------------------------------------ FP8 prefill --
+
+def _e4m3_codes(r, shape):
+    c = r.integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((c & 0x7F) == 0x7F, np.uint8(0x38), c)          # no NaN codes
+
+
+def _torch_values(codes, scale):
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_matches_sdpa_on_torch_decoded_values(causal):
+    # the MLA prefill shape (q, k 192 wide, v 128 wide), one square request
+    r = _rng(91)
+    n, h = 40, 2
+    q, k, v = _e4m3_codes(r, (n, h, 192)), _e4m3_codes(r, (n, h, 192)), _e4m3_codes(r, (n, h, 128))
+    qs, ks, vs, scale = 0.011, 0.013, 0.7, 0.0721
+    cu = np.array([0, n])
+    o, _ = oracle.prefill_dense_fp8(q, k, v, qs, ks, vs, cu, cu, scale, causal)
+    for hh in range(h):
+        ref = _sdpa(_torch_values(q[:, hh], qs), _torch_values(k[:, hh], ks), _torch_values(v[:, hh], vs), scale, causal)
+        assert np.max(np.abs(o[:, hh] - ref)) < 1e-10
+
+
+def test_fp8_prefill_scales_enter_as_the_pages_describe():
+    r = _rng(92)
+    q, k, v = _e4m3_codes(r, (12, 1, 192)), _e4m3_codes(r, (30, 1, 192)), _e4m3_codes(r, (30, 1, 128))
+    cu_q, cu_k = np.array([0, 5, 12]), np.array([0, 14, 30])
+    o1, l1 = oracle.prefill_dense_fp8(q, k, v, 0.02, 0.01, 1.0, cu_q, cu_k, 0.07, True)
+    o2, l2 = oracle.prefill_dense_fp8(q, k, v, 0.04, 0.01, 1.0, cu_q, cu_k, 0.035, True)   # q_scale x softmax_scale
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    o3, l3 = oracle.prefill_dense_fp8(q, k, v, 0.02, 0.01, 2.5, cu_q, cu_k, 0.07, True)     # v_scale scales o only
+    assert np.allclose(o3, 2.5 * o1, atol=1e-12) and np.array_equal(l3, l1)
+
+
+def test_fp8_prefill_sampled_rows_equal_full():
+    r = _rng(93)
+    q, k, v = _e4m3_codes(r, (20, 4, 192)), _e4m3_codes(r, (50, 2, 192)), _e4m3_codes(r, (50, 2, 128))
+    cu_q, cu_k = np.array([0, 7, 20]), np.array([0, 21, 50])
+    o, l = oracle.prefill_dense_fp8(q, k, v, 0.03, 0.02, 0.5, cu_q, cu_k, 0.09, True, window_left=9)
+    rows = [(0, 0), (6, 3), (7, 1), (19, 2), (12, 0)]
+    orow, lrow = oracle.prefill_dense_fp8_rows(q, k, v, 0.03, 0.02, 0.5, cu_q, cu_k, 0.09, True, rows, window_left=9)
+    for n, (t, hh) in enumerate(rows):
+        assert np.allclose(orow[n], o[t, hh], atol=1e-12) and abs(lrow[n] - l[t, hh]) < 1e-12
