@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 MFMA, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
 
@@ -163,6 +164,35 @@ def secondary_mla(kv_dtype: str, steps: int) -> dict:
                          "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
 
 
+def secondary_prefill_fp8(steps: int) -> dict:
+    """FP8 MLA-shaped prefill (8K x 8K causal, 128 heads, q/k 192, v 128).
+    QK runs on FP8 MFMA and P.V on bf16 MFMA, so the roof is the blend of the
+    two published peaks weighted by each part's flops."""
+    import torch
+    import softmax_attention_paged_amd as sap
+    from softmax_attention_paged_amd import inputs
+    case = inputs.fp8_mla_prefill()
+    c = case.to("cuda:0")
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    tq, hq, dqk = case.q.shape
+    dv = case.v.shape[2]
+    out = torch.empty((tq, hq, dv), dtype=torch.bfloat16, device="cuda:0")
+    fn = lambda: sap.prefill(f8(c.q), f8(c.k), f8(c.v), c.cu_seqlens_q, cu_seqlens_kv=c.cu_seqlens_kv,
+                             max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale,
+                             causal=True, out=out, q_scale=c.q_scale, k_scale=c.k_scale, v_scale=c.v_scale)
+    for _ in range(3):
+        fn()
+    ms = time_events(fn, steps, torch.cuda.current_stream())
+    pairs = causal_pairs(case.cu_seqlens_q.tolist(), case.cu_seqlens_kv.diff().tolist(), True) * hq
+    qk, pv = pairs * 2 * dqk, pairs * 2 * dv
+    tf = (qk + pv) / (ms * 1e-3) / 1e12
+    peak = (qk + pv) / (qk / FP8_PEAK_TFLOPS + pv / BF16_PEAK_TFLOPS)
+    return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+            "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel", "achieved": round(tf, 1),
+                         "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                         "peak_note": "QK flops at the FP8 peak, P.V flops at the bf16 peak"}}
+
+
 def secondary_mla_pack(steps: int) -> dict:
     """MLA K/V pack + FP8 quantise at the TokenSpeed-MLA prefill shape (8K
     tokens, 128 heads, K = 128 nope + 64 rope, V = 128): HBM-bound."""
@@ -251,6 +281,7 @@ def main() -> int:
         "ragged_paged_prefill_80k": lambda steps: secondary_prefill(inputs.ragged_paged_prefill, steps),
         "mla_decode_80k_bf16": lambda steps: secondary_mla("bf16", steps),
         "mla_decode_80k_fp8_e4m3": lambda steps: secondary_mla("fp8_e4m3", steps),
+        "fp8_mla_prefill_8k": secondary_prefill_fp8,
         "mla_kv_pack_fp8_8k": secondary_mla_pack,
         "cache_append_8k": secondary_append,
     }

@@ -90,8 +90,16 @@ typedef enum {
  *          j < Lk - Lq - window_left + i (window_left >= 0 keys of context
  *          before the query block); window_enabled = 0 (a zeroed struct)
  *          is the full history.
- * Supported: Dqk == Dv in {64, 128, 256}; Hq % Hkv == 0; page_size a power of
- * two >= 16 (paged mode).
+ *   qkv_dtype  ATTN_BF16 (a zeroed struct; the scales are ignored), or
+ *          ATTN_FP8_E4M3: q, k and v hold E4M3 codes with per-tensor
+ *          dequantisation scales q_scale, k_scale, v_scale > 0 (value = code
+ *          * scale), the MLA-shaped FP8 prefill of "TokenSpeed-MLA" (prefill
+ *          command: FP8 E4M3 inputs, q and k 192 wide; kernel capability
+ *          summary: V d_v wide, output BF16, LSE FP32). Strides count
+ *          elements of one byte.
+ * Supported: bf16: Dqk == Dv in {64, 128, 256}, dense or paged; FP8: dense
+ * mode with Dqk = 192 and Dv = 128. Hq % Hkv == 0; page_size a power of two
+ * >= 16 (paged mode).
  * ---------------------------------------------------------------------- */
 typedef struct {
   const void *q;
@@ -115,6 +123,8 @@ typedef struct {
   float *lse;
   int32_t window_enabled;            /* 0: full history */
   int32_t window_left;               /* keys of context when window_enabled */
+  attn_dtype_t qkv_dtype;            /* ATTN_BF16 (0) or ATTN_FP8_E4M3 */
+  float q_scale, k_scale, v_scale;   /* FP8 dequantisation scales */
 } attn_prefill_params;
 
 /* Enqueue ragged prefill. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,

@@ -42,6 +42,8 @@ class PrefillParams(ctypes.Structure):
         ("softmax_scale", ctypes.c_float), ("causal", _i32),
         ("o", _p), ("o_stride_tok", _i64), ("o_stride_head", _i64),
         ("lse", _p), ("window_enabled", _i32), ("window_left", _i32),
+        ("qkv_dtype", ctypes.c_int), ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 

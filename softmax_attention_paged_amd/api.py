@@ -129,14 +129,18 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
 
 def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale, causal=False,
             cu_seqlens_kv=None, seq_lens_kv=None, block_table=None, out=None, return_lse=False,
-            window_left=-1):
+            window_left=-1, q_scale=1.0, k_scale=1.0, v_scale=1.0):
     """Ragged prefill over dense (cu_seqlens_kv) or paged (block_table +
     seq_lens_kv) KV. q [Tq, Hq, D] bf16; dense k/v [Tk, Hkv, D]; paged k/v
-    [pages, page_size, Hkv, D]. window_left >= 0: row i of a request sees no
-    key before Lk - Lq - window_left + i (-1: full history). Returns
+    [pages, page_size, Hkv, D]. FP8: q, k, v all float8_e4m3fn codes (dense,
+    D = 192 for q/k and 128 for v) with per-tensor scales (value = code *
+    scale); the output stays bf16. window_left >= 0: row i of a request sees
+    no key before Lk - Lq - window_left + i (-1: full history). Returns
     out [Tq, Hq, Dv], or (out, lse)."""
-    _need(q.is_cuda and q.dtype == _BF16 and q.stride(2) == 1, "q must be bf16 CUDA with contiguous channels")
-    _need(k.dtype == _BF16 and v.dtype == _BF16, "k and v must be bf16")
+    fp8 = q.dtype == torch.float8_e4m3fn
+    _need(q.is_cuda and q.dtype in (_BF16, torch.float8_e4m3fn) and q.stride(2) == 1,
+          "q must be bf16 or float8_e4m3fn CUDA with contiguous channels")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share one dtype")
     _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous(), "cu_seqlens_q must be contiguous int32")
     paged = block_table is not None
     tq, hq, dqk = q.shape
@@ -168,6 +172,9 @@ def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale
     p.o, p.o_stride_tok, p.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
     p.lse = _ptr(lse)
     p.window_enabled, p.window_left = int(window_left >= 0), max(int(window_left), 0)
+    if fp8:
+        p.qkv_dtype = _ffi.ATTN_FP8_E4M3
+        p.q_scale, p.k_scale, p.v_scale = float(q_scale), float(k_scale), float(v_scale)
     _ffi.check(_ffi.load().attn_prefill(ctypes.byref(p), _stream(q.device)), "attn_prefill")
     return (out, lse) if return_lse else out
 

@@ -199,9 +199,21 @@ attn_status_t validate_prefill(const attn_prefill_params *p) {
   if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
     return fail(ATTN_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 p->num_q_heads, p->num_kv_heads);
-  if (p->head_dim_qk != p->head_dim_v || (p->head_dim_qk != 64 && p->head_dim_qk != 128 && p->head_dim_qk != 256))
+  if (p->qkv_dtype != ATTN_BF16 && p->qkv_dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_ERR_UNSUPPORTED, "prefill qkv_dtype must be bf16 or fp8 e4m3");
+  const bool fp8 = p->qkv_dtype == ATTN_FP8_E4M3;
+  if (fp8) {
+    if (p->head_dim_qk != 192 || p->head_dim_v != 128)
+      return fail(ATTN_ERR_UNSUPPORTED, "FP8 prefill head dims (%d, %d) unsupported: need (192, 128)",
+                  p->head_dim_qk, p->head_dim_v);
+    if (p->block_table) return fail(ATTN_ERR_UNSUPPORTED, "FP8 prefill reads dense K/V only");
+    for (float sc : {p->q_scale, p->k_scale, p->v_scale})
+      if (!(std::isfinite(sc) && sc > 0.f)) return fail(ATTN_ERR_INVALID_ARG, "FP8 scales must be finite and > 0");
+  } else if (p->head_dim_qk != p->head_dim_v ||
+             (p->head_dim_qk != 64 && p->head_dim_qk != 128 && p->head_dim_qk != 256)) {
     return fail(ATTN_ERR_UNSUPPORTED, "prefill head dims (%d, %d) unsupported: need equal 64/128/256",
                 p->head_dim_qk, p->head_dim_v);
+  }
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0)
     return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_q/max_seqlen_kv must be >= 0");
   if (!std::isfinite(p->softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
@@ -227,11 +239,14 @@ attn_status_t validate_prefill(const attn_prefill_params *p) {
     return fail(ATTN_ERR_INVALID_ARG, paged ? "paged mode needs seq_lens_kv" : "dense mode needs cu_seqlens_kv");
   if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-  const int64_t strides[] = {p->q_stride_tok, p->q_stride_head, p->k_stride_tok, p->k_stride_head,
-                             p->v_stride_tok, p->v_stride_head, p->o_stride_tok, p->o_stride_head,
-                             paged ? p->k_stride_page : 8, paged ? p->v_stride_page : 8};
+  // every stride a multiple of 16 bytes (elements of 2 bytes, or of 1 byte for FP8 inputs)
+  const int64_t in_bytes = fp8 ? 1 : 2;
+  const int64_t strides[] = {p->q_stride_tok * in_bytes, p->q_stride_head * in_bytes, p->k_stride_tok * in_bytes,
+                             p->k_stride_head * in_bytes, p->v_stride_tok * in_bytes, p->v_stride_head * in_bytes,
+                             p->o_stride_tok * 2, p->o_stride_head * 2,
+                             paged ? p->k_stride_page * in_bytes : 16, paged ? p->v_stride_page * in_bytes : 16};
   for (int64_t st : strides)
-    if (st < 0 || (st * 2) % 16) return fail(ATTN_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+    if (st < 0 || st % 16) return fail(ATTN_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
   if (p->q_stride_tok < 1 || p->k_stride_tok < 1 || p->v_stride_tok < 1 || p->o_stride_tok < 1)
     return fail(ATTN_ERR_INVALID_ARG, "token strides must be positive");
   return ok();
@@ -404,14 +419,18 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
   a.max_seqlen_q = p->max_seqlen_q;
   a.max_seqlen_kv = p->max_seqlen_kv;
   a.q_tiles = (int)cdiv(p->max_seqlen_q, kPrefillRows);
-  a.scale_log2 = p->softmax_scale * attn::kLog2eHost;
+  a.fp8 = p->qkv_dtype == ATTN_FP8_E4M3;
+  // FP8: the dequantisation scales of q and k fold into the score scale and
+  // v's into the final normalisation
+  a.scale_log2 = p->softmax_scale * attn::kLog2eHost * (a.fp8 ? p->q_scale * p->k_scale : 1.f);
+  a.v_scale = a.fp8 ? p->v_scale : 1.f;
   a.causal = p->causal;
   a.window_left = p->window_enabled ? p->window_left : -1;
   a.o = p->o;
   a.o_stride_tok = p->o_stride_tok;
   a.o_stride_head = p->o_stride_head;
   a.lse = p->lse;
-  hipError_t err = attn::launch_prefill(a, stream);
+  hipError_t err = a.fp8 ? attn::launch_prefill_fp8(a, stream) : attn::launch_prefill(a, stream);
   if (err == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(err));
   return ok();

@@ -87,6 +87,8 @@ struct PrefillArgs {
   float scale_log2;
   int32_t causal;
   int32_t window_left;           // keys of context before the query block; -1: full history
+  int32_t fp8;                   // 1: E4M3 q/k/v codes (scale_log2 carries q_scale * k_scale)
+  float v_scale;                 // FP8: V dequantisation scale (1 for bf16)
   void *o;
   int64_t o_stride_tok, o_stride_head;
   float *lse;
@@ -124,6 +126,7 @@ hipError_t launch_decode_gqa(const DecodeGqaArgs &a, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeMlaArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_prefill_fp8(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_cache_append(const CacheAppendArgs &a, hipStream_t stream);
 hipError_t launch_mla_kv_pack(const MlaPackArgs &a, hipStream_t stream);
 

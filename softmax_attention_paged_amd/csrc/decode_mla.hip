@@ -86,26 +86,6 @@ __device__ __forceinline__ int xcd_unit(int i, int n) {
   return x * per + min(x, rem) + k;
 }
 
-// Exact e4m3 -> bf16 of 16 codes (the hardware FP8 convert reads the OCP format on gfx950).
-__device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, bf16x8 &lo, bf16x8 &hi) {
-  float f[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int word = (int)w[q];
-    const auto p01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);   // bytes 0, 1
-    const auto p23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);    // bytes 2, 3
-    f[4 * q + 0] = p01[0];
-    f[4 * q + 1] = p01[1];
-    f[4 * q + 2] = p23[0];
-    f[4 * q + 3] = p23[1];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lo[e] = to_bf16(f[e]);
-    hi[e] = to_bf16(f[8 + e]);
-  }
-}
-
 // Where this thread's tile loads go. bf16: load k of the wave fills LDS slot
 // (k kW + wave) 64 + lane; fp8: chunk c of the thread is fp8 chunk
 // c kThreads + tid of the tile (row, 16 codes).

@@ -1,0 +1,68 @@
+// Pieces the prefill kernels share: the work unit a workgroup owns, the LDS
+// swizzle of bf16 tiles, and the lazy re-base threshold. Internal header.
+#pragma once
+
+#include "attn_internal.h"
+#include "device_common.h"
+
+namespace attn {
+namespace {
+
+constexpr float kRebase = 8.0f;   // log2 units a row max may rise before the row re-bases
+
+// LDS tiles are unpadded [keys][D] with the 16-byte chunks of row r stored at
+// slot chunk ^ f(r). f spreads the 16 rows a K-operand read touches over all
+// 64 banks, and gives the 4 rows x 4 chunks of a transposing V read (32
+// lanes) distinct banks too.
+template <int D>
+__device__ __forceinline__ int pf_swz(int row) {
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+struct PfUnit {
+  int b, kvh, h0;              // request, KV head, first query head of the workgroup
+  int gh, tq;                  // query heads and query tokens per workgroup
+  int q_begin, q_end;          // query rows of the request covered by this workgroup (relative)
+  int lq, lk;                  // request lengths
+  int64_t q_off;               // first query token of the request in the packed Q
+  int64_t kv_off;              // dense: first key of the request in packed K/V
+};
+
+// Heads per workgroup for a GQA group: the largest of 4, 2, 1 dividing it.
+__host__ __device__ __forceinline__ int pf_heads_per_wg(int group) {
+  return (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
+// The rows workgroup blockIdx.x owns when it holds `blocks` 32-row blocks:
+// gh heads of one KV group times tq = 32 blocks / gh tokens, tiles counted
+// from the end of the request (index slowest, so the longest rows of every
+// request start first). False when the request has no tile of that index.
+__device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit &u) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  u.gh = pf_heads_per_wg(group);
+  u.tq = 32 * (blocks / u.gh);
+  const int head_groups = a.num_q_heads / u.gh;
+  int L = blockIdx.x;
+  const int qt = L / (a.batch * head_groups);
+  L %= a.batch * head_groups;
+  u.b = L / head_groups;
+  u.h0 = (L % head_groups) * u.gh;
+  u.kvh = u.h0 / group;
+  const int q_lo = a.cu_seqlens_q[u.b];
+  u.lq = a.cu_seqlens_q[u.b + 1] - q_lo;
+  u.q_off = q_lo;
+  if (a.block_table) {
+    u.lk = a.seq_lens_kv[u.b];
+    u.kv_off = 0;
+  } else {
+    u.kv_off = a.cu_seqlens_kv[u.b];
+    u.lk = a.cu_seqlens_kv[u.b + 1] - (int)u.kv_off;
+  }
+  u.q_end = u.lq - qt * u.tq;
+  u.q_begin = max(0, u.q_end - u.tq);
+  return u.q_end > 0;
+}
+
+}  // namespace
+}  // namespace attn

@@ -352,6 +352,58 @@ def mla_decode(kv_dtype: str = "bf16", seed: int = 5, causal: bool = True) -> De
                        name=f"mla_decode_b8_q4_h64_kv80k_d576-512_ps64_{kv_dtype}")
 
 
+@dataclasses.dataclass
+class Fp8PrefillCase:
+    name: str
+    q: torch.Tensor                  # E4M3 codes (uint8) [Tq, Hq, 192]
+    k: torch.Tensor                  # [Tk, Hkv, 192]
+    v: torch.Tensor                  # [Tk, Hkv, 128]
+    q_scale: float
+    k_scale: float
+    v_scale: float
+    cu_seqlens_q: torch.Tensor       # int32 [B+1]
+    cu_seqlens_kv: torch.Tensor      # int32 [B+1]
+    scale: float
+    causal: bool
+    max_seqlen_q: int
+    max_seqlen_kv: int
+    seed: int
+    window_left: int = -1
+
+    def to(self, device) -> "Fp8PrefillCase":
+        return dataclasses.replace(self, q=self.q.to(device), k=self.k.to(device), v=self.v.to(device),
+                                   cu_seqlens_q=self.cu_seqlens_q.to(device),
+                                   cu_seqlens_kv=self.cu_seqlens_kv.to(device))
+
+
+def fp8_prefill_case(*, q_lens: list[int], kv_lens: list[int], hq: int, hkv: int, seed: int, causal: bool = True,
+                     dqk: int = 192, dv: int = 128, scale: float | None = None, q_mult: float = 1.0,
+                     window_left: int = -1, name: str = "") -> Fp8PrefillCase:
+    """FP8 MLA-shaped prefill inputs: float32 N(0, 1) Q, K, V (Q times
+    q_mult) quantised to E4M3 codes with one scale per tensor (amax / 448).
+    The softmax scale defaults to 1 / sqrt(dqk)."""
+    _, s_q, s_k, s_v = _streams(seed)
+    tq, tk = sum(q_lens), sum(kv_lens)
+    q, qs = _fp8_codes(_normal_f32(s_q, (tq, hq, dqk), q_mult))
+    k, ks = _fp8_codes(_normal_f32(s_k, (tk, hkv, dqk)))
+    v, vs = _fp8_codes(_normal_f32(s_v, (tk, hkv, dv)))
+    return Fp8PrefillCase(name=name, q=q, k=k, v=v, q_scale=qs, k_scale=ks, v_scale=vs,
+                          cu_seqlens_q=torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32),
+                          cu_seqlens_kv=torch.tensor(np.concatenate([[0], np.cumsum(kv_lens)]), dtype=torch.int32),
+                          scale=float(scale if scale is not None else 1.0 / math.sqrt(dqk)), causal=causal,
+                          max_seqlen_q=max(q_lens, default=0), max_seqlen_kv=max(kv_lens, default=0), seed=seed,
+                          window_left=window_left)
+
+
+def fp8_mla_prefill(seed: int = 6, seq: int = 8192, kv: int | None = None) -> Fp8PrefillCase:
+    """The FP8 MLA prefill workload: batch 1, seq query tokens over kv keys
+    (default seq), 128 heads, q/k 192 wide, v 128 wide, E4M3 inputs with
+    per-tensor scales, causal bottom-right, softmax scale 1/sqrt(192)."""
+    kv = seq if kv is None else kv
+    return fp8_prefill_case(q_lens=[seq], kv_lens=[kv], hq=128, hkv=128, seed=seed, causal=True,
+                            name=f"fp8_mla_prefill_q{seq}_kv{kv}_h128_d192-128")
+
+
 def sha256_of(*tensors) -> str:
     h = hashlib.sha256()
     for t in tensors:
