@@ -11,9 +11,9 @@
 // and output o per row (the online recurrence of "Flywheel Attention",
 // section 1, and "Writing Page Attention with PyPTO", section 6.3). Per tile:
 //   - K and V rows are gathered through the block table into registers with
-//     full-row loads (16 lanes per 256-byte row slice), one tile ahead; the
-//     page of a 16-key half-tile is one table entry (pages hold a power of
-//     two >= 16 keys), read once. K goes through the wave's LDS tile to the
+//     full-row loads (16 lanes per 256-byte row slice), both issued at the
+//     top of the tile's iteration; the page of a 16-key half-tile is one
+//     table entry (pages hold a power of two >= 16 keys), read once. K goes through the wave's LDS tile to the
 //     MFMA A-operand layout (token = l % 16, 8 channels per lane), then V
 //     takes the same tile.
 //   - S^T = K Q^T on v_mfma_f32_16x16x32_bf16, so each lane ends up holding
@@ -53,10 +53,11 @@ struct GqaGeom {
   static constexpr int kVTile = kTile * kVStride;               // bf16 elements per wave
   static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per V row
   static constexpr int kVChunks = kTile * kChunksPerRow / 64;   // 16-byte chunks per lane per V tile
-  // waves per SIMD the registers are budgeted for: more waves keep more
-  // K/V loads in flight per CU (D = 128 fits 3 in 167 VGPRs without spills)
-  static constexpr int kWPE = D <= 64 ? 4 : (D <= 128 ? 3 : 1);
-  static constexpr int kWPEExt = D <= 64 ? 4 : (D <= 128 ? 2 : 1);   // window / packed rows
+  // waves per SIMD the registers are budgeted for: three (twelve streaming
+  // waves per CU) is the best measured for the paged read; D = 128 fits in
+  // 149 VGPRs (167 with a window or packed rows), D = 256 fits two
+  static constexpr int kWPE = D <= 64 ? 4 : (D <= 128 ? 3 : 2);
+  static constexpr int kWPEExt = D <= 64 ? 4 : (D <= 128 ? 3 : 1);   // window / packed rows
 };
 
 // Gather one 32-key tile of K (MFMA A layout) or V (linear 16-byte chunks).
@@ -208,11 +209,13 @@ struct WaveState {
     for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Walk tiles first, first + stride, ... below u.c1. The registers rotate:
-  // the next tile's K loads are issued as soon as the QK MFMAs have taken
-  // the current K, and its V loads as soon as the current V is in LDS, so a
-  // wave keeps a whole tile of loads in flight while it does the softmax
-  // and PV of the current one.
+  // Walk tiles first, first + stride, ... below u.c1. Each iteration issues
+  // its tile's K and V loads together and then waits for them; nothing is
+  // fetched a tile ahead. Measured: with twelve waves per CU streaming, a
+  // wave that keeps the next tile's 16 KB in flight while it computes makes
+  // the HBM less efficient (more concurrent requests, worse locality) than
+  // one whose loads stop while it computes (its neighbours' loads fill the
+  // gap): 0.220 vs 0.228 ms on the Qwen3-14B-shaped decode.
   __device__ __forceinline__ void walk(const DecodeGqaArgs &a, const UnitRows &u, int first, int stride,
                                        __bf16 *vlds, int lane) {
     const int kg = lane >> 4;
@@ -223,15 +226,10 @@ struct WaveState {
     if (first >= u.c1) return;
     bf16x8 kr[G::kVChunks];
     bf16x8 vr[G::kVChunks];
-    TilePages tp = tile_pages(a, bt_row, first, u.c1);
-    load_k<D>(a, kbase, tp, first, lane, kr);
-    load_v<D>(a, vbase, tp, first, u.c1, lane, vr);
-    // table entries of the next tile, fetched one iteration before its loads
-    TilePages tn = tp;
-    if (first + stride < u.c1) tn = tile_pages(a, bt_row, first + stride, u.c1);
     for (int tok0 = first; tok0 < u.c1; tok0 += stride) {
-      const int nxt = tok0 + stride;
-      const bool more = nxt < u.c1;
+      const TilePages tp = tile_pages(a, bt_row, tok0, u.c1);
+      load_k<D>(a, kbase, tp, tok0, lane, kr);
+      load_v<D>(a, vbase, tp, tok0, u.c1, lane, vr);
       // K tile -> the wave's LDS tile (token-major, padded rows), read back
       // in the MFMA A layout (token = l % 16, 8 channels per lane). LDS
       // operations of one wave execute in order, so the V rows written
@@ -242,7 +240,6 @@ struct WaveState {
         store_bf16x8_lds(vlds + (idx / G::kChunksPerRow) * G::kVStride + (idx % G::kChunksPerRow) * 8, kr[c]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (more) load_k<D>(a, kbase, tn, nxt, lane, kr);
       // S^T tiles: sacc[0] keys tok0 + 4kg + i, sacc[1] keys tok0 + 16 + 4kg + i.
       f32x4 sacc[2];
 #pragma unroll
@@ -259,8 +256,6 @@ struct WaveState {
         const int idx = c * 64 + lane;
         store_bf16x8_lds(vlds + (idx / G::kChunksPerRow) * G::kVStride + (idx % G::kChunksPerRow) * 8, vr[c]);
       }
-      if (more) load_v<D>(a, vbase, tn, nxt, u.c1, lane, vr);
-      if (nxt + stride < u.c1) tn = tile_pages(a, bt_row, nxt + stride, u.c1);
       float x[8];
       float mx = kNegInf;
 #pragma unroll
@@ -353,8 +348,9 @@ __device__ __forceinline__ void write_empty(const DecodeGqaArgs &a, const UnitRo
 // finished wave frees its slot at once.
 //
 // kExt adds what a sliding window or packed query rows need (the
-// lower-bound mask, the packed row mapping); its extra live registers would
-// spill at the plain kernel's occupancy, so it runs at its own.
+// lower-bound mask, the packed row mapping); it is a separate instantiation
+// so the plain kernel keeps its registers (at D = 256 it also runs at a
+// lower occupancy than the plain one).
 template <int D, bool kExt>
 __global__ __launch_bounds__(64, kExt ? GqaGeom<D>::kWPEExt : GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(const DecodeGqaArgs a) {
   using G = GqaGeom<D>;
