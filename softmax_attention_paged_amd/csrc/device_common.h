@@ -130,4 +130,20 @@ __device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, bf16x8 &lo, bf16x8 &hi) 
   }
 }
 
+// Exact e4m3 -> bf16 of 8 codes.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  bf16x8 r;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int word = (int)w[q];
+    const auto p01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    const auto p23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+    r[4 * q + 0] = to_bf16(p01[0]);
+    r[4 * q + 1] = to_bf16(p01[1]);
+    r[4 * q + 2] = to_bf16(p23[0]);
+    r[4 * q + 3] = to_bf16(p23[1]);
+  }
+  return r;
+}
+
 }  // namespace attn

@@ -16,7 +16,7 @@
 //   - K tiles move HBM -> LDS by direct loads, as codes (192-byte rows, the
 //     16-byte chunks of row r XOR-swizzled by (r >> 2) & 3 so the 16 rows of
 //     an operand read fall on distinct banks).
-//   - V tiles pass through registers: each thread loads two 16-code chunks a
+//   - V tiles pass through registers: each thread loads four 8-code pieces a
 //     tile ahead, widens them exactly to bf16 and stores them into a bf16 LDS
 //     tile laid out as the bf16 kernel's, so P.V is the same bf16 MFMA with
 //     P rounded to bf16 (an E4M3 P would lose the row sums' precision).
@@ -44,12 +44,12 @@ constexpr int kF8KTileB = kF8N * kF8KRowB;                // bytes of a K tile
 constexpr int kF8KLoads = kF8N * kF8KChunks / 64 / kF8W;  // direct loads per wave per K tile
 constexpr int kF8VRowB = kF8Dv * 2;                       // bytes of a widened V row in LDS
 constexpr int kF8VTileB = kF8N * kF8VRowB;                // bytes of a V tile in LDS
-constexpr int kF8VCodeChunks = kF8Dv / 16;                // 16-code chunks per V row
-constexpr int kF8VLoads = kF8N * kF8VCodeChunks / (64 * kF8W);   // V chunks per thread per tile
+constexpr int kF8VPieces = kF8Dv / 8;                     // 8-code pieces per V row
+constexpr int kF8VLoads = kF8N * kF8VPieces / (64 * kF8W);  // V pieces per thread per tile
 constexpr int kF8NB = kF8Dv / 32;                         // PV 32-channel blocks
 constexpr int kF8KK = kF8N / 16;                          // PV k-steps
 static_assert(kF8N * kF8KChunks % (64 * kF8W) == 0, "whole K loads per wave");
-static_assert(kF8N * kF8VCodeChunks % (64 * kF8W) == 0, "whole V chunks per thread");
+static_assert(kF8N * kF8VPieces % (64 * kF8W) == 0, "whole V pieces per thread");
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
@@ -215,29 +215,27 @@ __global__ __launch_bounds__(64 * kF8W, 2) void prefill_fp8_kernel(const Prefill
       }
     }
   };
-  // V: thread chunk q = k * 256 + tid is row q / 8, codes 16 (q % 8) .. + 15;
-  // rows past the request are zero (P is 0 there, and 0 * NaN would not be)
-  u32x4 vstage[kF8VLoads];
+  // V: thread piece q = k * 256 + tid is row q / 16, codes 8 (q % 16) .. + 7,
+  // widened to the row's bf16 chunk q % 16: the 16 lanes of a quarter-wave
+  // write one whole 256-byte row, every bank once. Rows past the request are
+  // zero (P is 0 there, and 0 * NaN would not be).
+  u32x2 vstage[kF8VLoads];
   auto load_v = [&](int j0) {
 #pragma unroll
     for (int k = 0; k < kF8VLoads; ++k) {
       const int q = k * 64 * kF8W + tid;
-      const int row = q / kF8VCodeChunks, cc = q % kF8VCodeChunks;
+      const int row = q / kF8VPieces, pc = q % kF8VPieces;
       vstage[k] = (j0 + row < u.lk)
-                      ? *reinterpret_cast<const u32x4 *>(vsrc + (int64_t)(j0 + row) * a.v_stride_tok + cc * 16)
-                      : u32x4{0u, 0u, 0u, 0u};
+                      ? *reinterpret_cast<const u32x2 *>(vsrc + (int64_t)(j0 + row) * a.v_stride_tok + pc * 8)
+                      : u32x2{0u, 0u};
     }
   };
   auto store_v = [&](char *dst) {
 #pragma unroll
     for (int k = 0; k < kF8VLoads; ++k) {
       const int q = k * 64 * kF8W + tid;
-      const int row = q / kF8VCodeChunks, cc = q % kF8VCodeChunks;
-      bf16x8 lo, hi;
-      fp8x16_to_bf16(vstage[k], lo, hi);
-      char *r = dst + row * kF8VRowB;
-      store_bf16x8_lds(r + ((2 * cc) ^ pf_swz<kF8Dv>(row)) * 16, lo);
-      store_bf16x8_lds(r + ((2 * cc + 1) ^ pf_swz<kF8Dv>(row)) * 16, hi);
+      const int row = q / kF8VPieces, pc = q % kF8VPieces;
+      store_bf16x8_lds(dst + row * kF8VRowB + (pc ^ pf_swz<kF8Dv>(row)) * 16, fp8x8_to_bf16(vstage[k]));
     }
   };
 
