@@ -137,29 +137,28 @@ def causal_pairs(cu_q: list[int], kv_lens: list[int], causal: bool) -> int:
     return tot
 
 
-def secondary_prefill(name_fn, steps: int) -> dict:
+def secondary_prefill(name_fn, steps: int, kv_splits: int = 0) -> dict:
     import torch
     import softmax_attention_paged_amd as sap
     case = name_fn()
     c = case.to("cuda:0")
-    hq, d = case.q.shape[1], case.q.shape[2]
+    tq, hq, d = case.q.shape
     flops = causal_pairs(case.cu_seqlens_q.tolist(), case.seq_lens_kv.tolist(), case.causal) * hq * 2 * (d + d)
     out = torch.empty_like(c.q)
-    lse = torch.empty((c.q.shape[0], hq), dtype=torch.float32, device=c.q.device)
-    kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale, causal=c.causal,
-              out=out)
-    if c.paged:
-        fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv,
-                                 block_table=c.block_table, **kw)
-    else:
-        fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, cu_seqlens_kv=c.cu_seqlens_kv, **kw)
+    kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, causal=c.causal, kv_splits=kv_splits)
+    kv = dict(seq_lens_kv=c.seq_lens_kv, block_table=c.block_table) if c.paged else dict(cu_seqlens_kv=c.cu_seqlens_kv)
+    # key-split partials: one workspace, allocated before the timed region
+    ws_bytes = sap.prefill_workspace_size(c.q, c.k, c.v, c.cu_seqlens_q, **kv, **kw)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=c.q.device)
+    splits = ws_bytes // (tq * hq * (d + 1) * 4) if ws_bytes else 1
+    fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, softmax_scale=c.scale, out=out, workspace=ws, **kv, **kw)
     for _ in range(3):
         fn()
     ms = time_events(fn, steps, torch.cuda.current_stream())
-    del lse
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
-            "roofline": {"bound": "mfma", "kernel": f"prefill_pipe_kernel<{d}, {1 if c.paged else 0}>",
+    kernel = f"prefill_pipe_kernel<{d}, {1 if c.paged else 0}>" + (" + merge" if splits > 1 else "")
+    return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "kv_splits": splits,
+            "roofline": {"bound": "mfma", "kernel": kernel,
                          "achieved": round(tf, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
 
@@ -276,10 +275,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--num-splits", type=int, default=0, help="override the planner's KV split count")
+    ap.add_argument("--prefill-kv-splits", type=int, default=0,
+                    help="override the prefill planner's key split count (1: unsplit)")
     ap.add_argument("--no-secondary", action="store_true", help="time only the main workload")
     ap.add_argument("--only", default="", metavar="WORKLOAD",
                     help="time one secondary workload alone (for profiling): dense_causal_prefill_d128, "
-                         "dense_causal_prefill_d256, ragged_paged_prefill_80k, mla_decode_80k_bf16, "
+                         "dense_causal_prefill_d256, ragged_paged_prefill_80k, single_chunk_prefill_80k, mla_decode_80k_bf16, "
                          "mla_decode_80k_fp8_e4m3")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (reference for HBM counters)")
@@ -303,9 +304,14 @@ def main() -> int:
     from softmax_attention_paged_amd import inputs
 
     secondaries = {
-        "dense_causal_prefill_d128": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=128), steps),
-        "dense_causal_prefill_d256": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=256), steps),
-        "ragged_paged_prefill_80k": lambda steps: secondary_prefill(inputs.ragged_paged_prefill, steps),
+        "dense_causal_prefill_d128": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=128), steps,
+                                                                     args.prefill_kv_splits),
+        "dense_causal_prefill_d256": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=256), steps,
+                                                                     args.prefill_kv_splits),
+        "ragged_paged_prefill_80k": lambda steps: secondary_prefill(inputs.ragged_paged_prefill, steps,
+                                                                    args.prefill_kv_splits),
+        "single_chunk_prefill_80k": lambda steps: secondary_prefill(inputs.single_chunk_prefill, steps,
+                                                                    args.prefill_kv_splits),
         "mla_decode_80k_bf16": lambda steps: secondary_mla("bf16", steps),
         "mla_decode_80k_fp8_e4m3": lambda steps: secondary_mla("fp8_e4m3", steps),
         "fp8_mla_prefill_8k": secondary_prefill_fp8,

@@ -90,6 +90,15 @@ typedef enum {
  *          j < Lk - Lq - window_left + i (window_left >= 0 keys of context
  *          before the query block); window_enabled = 0 (a zeroed struct)
  *          is the full history.
+ *   total_q, kv_splits, workspace   key splits (bf16 only): with a
+ *          workspace of attn_prefill_workspace_size(p) bytes (16-byte
+ *          aligned) and total_q set, the keys of each query tile may be
+ *          walked by several workgroups whose partials are merged by log-sum-
+ *          exp; without one (or if it is too small, or o is not contiguous)
+ *          the call runs unsplit. Results equal the unsplit ones up to
+ *          rounding. total_q must equal cu_seqlens_q[batch]: query rows at
+ *          or past a smaller total_q are not written (nor is the workspace
+ *          beyond its size).
  *   qkv_dtype  ATTN_BF16 (a zeroed struct; the scales are ignored), or
  *          ATTN_FP8_E4M3: q, k and v hold E4M3 codes with per-tensor
  *          dequantisation scales q_scale, k_scale, v_scale > 0 (value = code
@@ -125,7 +134,20 @@ typedef struct {
   int32_t window_left;               /* keys of context when window_enabled */
   attn_dtype_t qkv_dtype;            /* ATTN_BF16 (0) or ATTN_FP8_E4M3 */
   float q_scale, k_scale, v_scale;   /* FP8 dequantisation scales */
+  int32_t total_q;                   /* query rows of q (sum of q_lens); needed for key splits */
+  int32_t kv_splits;                 /* 0: the planner chooses; 1: no split; > 1: forced */
+  void *workspace;                   /* key-split partials; NULL runs without splits */
+  size_t workspace_bytes;
 } attn_prefill_params;
+
+/* Workspace bytes attn_prefill will use for p: S * total_q * Hq * (Dv + 1) * 4
+ * when the plan splits the keys of each query tile into S > 1 ranges (bf16,
+ * contiguous o [total_q, Hq, Dv], total_q > 0), else 0. With kv_splits = 0
+ * the planner splits only when the query tiles alone would not fill the CUs
+ * once (long keys, very few query rows; splits of >= 2048 keys); each
+ * split's normalised partial and LSE are then merged by attn_merge_lse's
+ * reducer. Only shapes and scalars are examined. */
+size_t attn_prefill_workspace_size(const attn_prefill_params *p);
 
 /* Enqueue ragged prefill. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,
  * ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP. */

@@ -43,7 +43,8 @@ class PrefillParams(ctypes.Structure):
         ("o", _p), ("o_stride_tok", _i64), ("o_stride_head", _i64),
         ("lse", _p), ("window_enabled", _i32), ("window_left", _i32),
         ("qkv_dtype", ctypes.c_int), ("q_scale", ctypes.c_float), ("k_scale", ctypes.c_float),
-        ("v_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float), ("total_q", _i32), ("kv_splits", _i32),
+        ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -99,6 +100,7 @@ class MlaKvPackParams(ctypes.Structure):
 
 EXPORTS = {
     "attn_prefill": (ctypes.c_int, [ctypes.POINTER(PrefillParams), _p]),
+    "attn_prefill_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(PrefillParams)]),
     "attn_decode_plan": (ctypes.c_int, [ctypes.POINTER(DecodeParams), ctypes.POINTER(DecodePlanInfo)]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(DecodeParams)]),
     "attn_decode_paged": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),

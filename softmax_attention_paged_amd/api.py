@@ -127,16 +127,8 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
 # Prefill
 # --------------------------------------------------------------------------
 
-def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale, causal=False,
-            cu_seqlens_kv=None, seq_lens_kv=None, block_table=None, out=None, return_lse=False,
-            window_left=-1, q_scale=1.0, k_scale=1.0, v_scale=1.0):
-    """Ragged prefill over dense (cu_seqlens_kv) or paged (block_table +
-    seq_lens_kv) KV. q [Tq, Hq, D] bf16; dense k/v [Tk, Hkv, D]; paged k/v
-    [pages, page_size, Hkv, D]. FP8: q, k, v all float8_e4m3fn codes (dense,
-    D = 192 for q/k and 128 for v) with per-tensor scales (value = code *
-    scale); the output stays bf16. window_left >= 0: row i of a request sees
-    no key before Lk - Lq - window_left + i (-1: full history). Returns
-    out [Tq, Hq, Dv], or (out, lse)."""
+def _prefill_params(q, k, v, cu_seqlens_q, out, lse, max_seqlen_q, max_seqlen_kv, softmax_scale, causal,
+                    cu_seqlens_kv, seq_lens_kv, block_table, window_left, q_scale, k_scale, v_scale, kv_splits):
     fp8 = q.dtype == torch.float8_e4m3fn
     _need(q.is_cuda and q.dtype in (_BF16, torch.float8_e4m3fn) and q.stride(2) == 1,
           "q must be bf16 or float8_e4m3fn CUDA with contiguous channels")
@@ -146,9 +138,6 @@ def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale
     tq, hq, dqk = q.shape
     dv = v.shape[-1]
     hkv = k.shape[2] if paged else k.shape[1]
-    if out is None:
-        out = torch.empty((tq, hq, dv), dtype=_BF16, device=q.device)
-    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device) if return_lse else None
     p = _ffi.PrefillParams()
     p.q, p.q_stride_tok, p.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
     p.k, p.v = k.data_ptr(), v.data_ptr()
@@ -169,12 +158,53 @@ def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale
     p.num_q_heads, p.num_kv_heads, p.head_dim_qk, p.head_dim_v = hq, hkv, dqk, dv
     p.max_seqlen_q, p.max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
     p.softmax_scale, p.causal = float(softmax_scale), int(bool(causal))
-    p.o, p.o_stride_tok, p.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
+    if out is not None:
+        p.o, p.o_stride_tok, p.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
+    else:                                   # sizing only: the layout a fresh output gets
+        p.o, p.o_stride_tok, p.o_stride_head = 0, hq * dv, dv
     p.lse = _ptr(lse)
     p.window_enabled, p.window_left = int(window_left >= 0), max(int(window_left), 0)
     if fp8:
         p.qkv_dtype = _ffi.ATTN_FP8_E4M3
         p.q_scale, p.k_scale, p.v_scale = float(q_scale), float(k_scale), float(v_scale)
+    p.total_q, p.kv_splits = tq, int(kv_splits)
+    return p
+
+
+def prefill_workspace_size(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, causal=False, cu_seqlens_kv=None,
+                           seq_lens_kv=None, block_table=None, window_left=-1, kv_splits=0):
+    """Bytes of workspace prefill() with these arguments (and a fresh,
+    contiguous output) would use for key splits; 0 when it runs unsplit."""
+    p = _prefill_params(q, k, v, cu_seqlens_q, None, None, max_seqlen_q, max_seqlen_kv, 1.0, causal, cu_seqlens_kv,
+                        seq_lens_kv, block_table, window_left, 1.0, 1.0, 1.0, kv_splits)
+    return int(_ffi.load().attn_prefill_workspace_size(ctypes.byref(p)))
+
+
+def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale, causal=False,
+            cu_seqlens_kv=None, seq_lens_kv=None, block_table=None, out=None, return_lse=False,
+            window_left=-1, q_scale=1.0, k_scale=1.0, v_scale=1.0, kv_splits=0, workspace=None):
+    """Ragged prefill over dense (cu_seqlens_kv) or paged (block_table +
+    seq_lens_kv) KV. q [Tq, Hq, D] bf16; dense k/v [Tk, Hkv, D]; paged k/v
+    [pages, page_size, Hkv, D]. FP8: q, k, v all float8_e4m3fn codes (dense,
+    D = 192 for q/k and 128 for v) with per-tensor scales (value = code *
+    scale); the output stays bf16. window_left >= 0: row i of a request sees
+    no key before Lk - Lq - window_left + i (-1: full history). kv_splits
+    (0: the planner's choice, 1: none) splits each query tile's keys over
+    several workgroups merged by LSE; the workspace for it (a uint8 CUDA
+    tensor) is allocated here unless passed. Returns out [Tq, Hq, Dv], or
+    (out, lse)."""
+    tq, hq, _ = q.shape
+    if out is None:
+        out = torch.empty((tq, hq, v.shape[-1]), dtype=_BF16, device=q.device)
+    lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    p = _prefill_params(q, k, v, cu_seqlens_q, out, lse, max_seqlen_q, max_seqlen_kv, softmax_scale, causal,
+                        cu_seqlens_kv, seq_lens_kv, block_table, window_left, q_scale, k_scale, v_scale, kv_splits)
+    need = _ffi.load().attn_prefill_workspace_size(ctypes.byref(p))
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous CUDA tensor")
+        p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _ffi.check(_ffi.load().attn_prefill(ctypes.byref(p), _stream(q.device)), "attn_prefill")
     return (out, lse) if return_lse else out
 

@@ -193,7 +193,8 @@ DecodePlan plan_decode(const attn_decode_params *p) {
 
 constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
 
-attn_status_t validate_prefill(const attn_prefill_params *p) {
+// shapes_only: the checks a workspace query makes (no pointers or strides).
+attn_status_t validate_prefill(const attn_prefill_params *p, bool shapes_only = false) {
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
   if (p->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch %d < 0", p->batch);
   if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
@@ -216,6 +217,9 @@ attn_status_t validate_prefill(const attn_prefill_params *p) {
   }
   if (p->max_seqlen_q < 0 || p->max_seqlen_kv < 0)
     return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_q/max_seqlen_kv must be >= 0");
+  if (p->kv_splits < 0 || p->kv_splits > attn::kMaxSplits)
+    return fail(ATTN_ERR_INVALID_ARG, "kv_splits %d outside 0..%d", p->kv_splits, attn::kMaxSplits);
+  if (p->total_q < 0) return fail(ATTN_ERR_INVALID_ARG, "total_q < 0");
   if (!std::isfinite(p->softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (p->window_enabled != 0 && p->window_enabled != 1)
@@ -232,7 +236,7 @@ attn_status_t validate_prefill(const attn_prefill_params *p) {
     if (p->block_table_stride < cdiv(p->max_seqlen_kv, p->page_size))
       return fail(ATTN_ERR_INVALID_ARG, "block_table_stride %d < pages of max_seqlen_kv", p->block_table_stride);
   }
-  if (p->batch == 0 || p->max_seqlen_q == 0) return ok();
+  if (shapes_only || p->batch == 0 || p->max_seqlen_q == 0) return ok();
   if (!p->q || !p->k || !p->v || !p->cu_seqlens_q || !p->o)
     return fail(ATTN_ERR_INVALID_ARG, "a required pointer (q, k, v, cu_seqlens_q, o) is NULL");
   if (paged ? !p->seq_lens_kv : !p->cu_seqlens_kv)
@@ -250,6 +254,47 @@ attn_status_t validate_prefill(const attn_prefill_params *p) {
   if (p->q_stride_tok < 1 || p->k_stride_tok < 1 || p->v_stride_tok < 1 || p->o_stride_tok < 1)
     return fail(ATTN_ERR_INVALID_ARG, "token strides must be positive");
   return ok();
+}
+
+// Key splits of a bf16 prefill: workgroups per query tile along the keys.
+// The launch has q_tiles * batch * head_groups workgroups (an upper bound:
+// requests shorter than max_seqlen_q have fewer tiles); only when that does
+// not fill one round of the CUs' slots are the keys split, into enough
+// ranges to fill it, none shorter than 2048 keys. Splitting costs more than
+// the merge: workgroups that share a query tile's K/V stream in step and
+// hit in L2, and a split halves how many do, so a launch that already fills
+// the CUs (even over uneven rounds) runs faster unsplit.
+struct PrefillPlan {
+  int splits;
+  int split_tokens;
+  size_t workspace;
+};
+
+PrefillPlan plan_prefill(const attn_prefill_params *p) {
+  PrefillPlan pl{1, 0, 0};
+  const bool contiguous_o = p->o_stride_head == p->head_dim_v && p->o_stride_tok == (int64_t)p->num_q_heads * p->head_dim_v;
+  if (p->qkv_dtype != ATTN_BF16 || p->total_q <= 0 || !contiguous_o || p->max_seqlen_kv <= 0 || p->batch <= 0 ||
+      p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads)
+    return pl;
+  int splits = p->kv_splits;
+  if (splits <= 0) {
+    const int group = p->num_q_heads / p->num_kv_heads;
+    const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
+    const int64_t units = cdiv(p->max_seqlen_q, kPrefillRows / gh) * p->batch * (p->num_q_heads / gh);
+    const int64_t slots = (int64_t)attn::kNumCUs * (p->head_dim_qk <= 128 ? 2 : 1);
+    splits = 1;
+    if (units < slots) splits = (int)std::min<int64_t>(cdiv(slots, std::max<int64_t>(units, 1)),
+                                                       std::max<int64_t>(1, p->max_seqlen_kv / 2048));
+  }
+  splits = std::min(splits, attn::kMaxSplits);
+  if (splits <= 1) return pl;
+  int64_t st = cdiv(cdiv(p->max_seqlen_kv, splits), 64) * 64;
+  splits = (int)cdiv(p->max_seqlen_kv, st);
+  if (splits <= 1) return pl;
+  pl.splits = splits;
+  pl.split_tokens = (int)st;
+  pl.workspace = (size_t)splits * p->total_q * p->num_q_heads * (p->head_dim_v + 1) * sizeof(float);
+  return pl;
 }
 
 }  // namespace
@@ -430,10 +475,24 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
   a.o_stride_tok = p->o_stride_tok;
   a.o_stride_head = p->o_stride_head;
   a.lse = p->lse;
+  a.kv_splits = 1;
+  const PrefillPlan pl = plan_prefill(p);
+  if (pl.splits > 1 && p->workspace && p->workspace_bytes >= pl.workspace && aligned16(p->workspace)) {
+    a.kv_splits = pl.splits;
+    a.split_tokens = pl.split_tokens;
+    a.total_q = p->total_q;
+    a.o_parts = static_cast<float *>(p->workspace);
+    a.lse_parts = a.o_parts + (size_t)pl.splits * p->total_q * p->num_q_heads * p->head_dim_v;
+  }
   hipError_t err = a.fp8 ? attn::launch_prefill_fp8(a, stream) : attn::launch_prefill(a, stream);
   if (err == hipErrorNotSupported) return fail(ATTN_ERR_UNSUPPORTED, "no prefill kernel for this shape");
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(err));
   return ok();
+}
+
+size_t attn_prefill_workspace_size(const attn_prefill_params *p) {
+  if (!p || validate_prefill(p, true) != ATTN_OK) return 0;
+  return plan_prefill(p).workspace;
 }
 
 attn_status_t attn_merge_lse(const float *o_parts, const float *lse_parts, int32_t num_splits,

@@ -89,6 +89,11 @@ struct PrefillArgs {
   int32_t window_left;           // keys of context before the query block; -1: full history
   int32_t fp8;                   // 1: E4M3 q/k/v codes (scale_log2 carries q_scale * k_scale)
   float v_scale;                 // FP8: V dequantisation scale (1 for bf16)
+  int32_t total_q;               // query tokens of all requests (rows of the partials / Hq)
+  int32_t kv_splits;             // workgroups per query tile along the keys (1: no partials)
+  int32_t split_tokens;          // keys per split, a multiple of 64
+  float *o_parts;                // kv_splits > 1: [S, total_q * Hq, Dv] normalised partial outputs
+  float *lse_parts;              // kv_splits > 1: [S, total_q * Hq] base-2 LSE of each split
   void *o;
   int64_t o_stride_tok, o_stride_head;
   float *lse;

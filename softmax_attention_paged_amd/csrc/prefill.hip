@@ -328,7 +328,14 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   // workgroup's walk starts at the tile holding its first row's first key.
   const bool windowed = a.window_left >= 0;
   const int begin = windowed ? max(0, u.lk - u.lq - a.window_left + t) : 0;
-  const int jb = windowed ? max(0, u.lk - u.lq - a.window_left + u.q_begin) & ~(G::kN - 1) : 0;
+  // The workgroup's keys: from the tile holding its first row's first key,
+  // within its split (splits are whole tiles) when the keys are split.
+  int jb = windowed ? max(0, u.lk - u.lq - a.window_left + u.q_begin) & ~(G::kN - 1) : 0;
+  int split_end = 0x7fffffff;
+  if (a.kv_splits > 1) {
+    jb = max(jb, u.split * a.split_tokens);
+    split_end = (u.split + 1) * a.split_tokens;
+  }
   int wave_max = bound, valid_min = row_valid ? bound : 0x7fffffff;
   int begin_max = row_valid ? begin : 0, begin_min = row_valid ? begin : 0x7fffffff;
 #pragma unroll
@@ -342,11 +349,12 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   valid_min = __builtin_amdgcn_readfirstlane(valid_min);
   begin_max = __builtin_amdgcn_readfirstlane(begin_max);
   begin_min = __builtin_amdgcn_readfirstlane(begin_min);
-  const int kv_end = a.causal ? min(u.lk, max(0, u.lk - u.lq + u.q_end)) : u.lk;
+  const int kv_end = min(split_end, a.causal ? min(u.lk, max(0, u.lk - u.lq + u.q_end)) : u.lk);
   const int nt = kv_end > jb ? (kv_end - jb + G::kN - 1) / G::kN : 0;       // tiles the workgroup loads
-  const int ntw = wave_max > jb ? (wave_max - jb + G::kN - 1) / G::kN : 0;  // tiles this wave computes (<= nt)
+  // tiles this wave computes (<= nt)
+  const int ntw = min(nt, wave_max > jb ? (wave_max - jb + G::kN - 1) / G::kN : 0);
   // the wave's first tile with a key for one of its rows (0 without a window)
-  const int it0 = (windowed && begin_min != 0x7fffffff) ? (begin_min - jb) / G::kN : 0;
+  const int it0 = (windowed && begin_min != 0x7fffffff && begin_min > jb) ? (begin_min - jb) / G::kN : 0;
 
   // Q^T operands (a negative scale negates Q, exact in bf16, so c > 0)
   const float c = fabsf(a.scale_log2);
@@ -483,6 +491,27 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   const float l = half_sum(lsum);
   if (!row_valid) return;
   const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (a.kv_splits > 1) {
+    // this split's normalised partial (FP32) and LSE, merged by the LSE
+    // reducer; a split without keys for the row leaves only its -inf LSE
+    const int64_t rows = (int64_t)a.total_q * a.num_q_heads;
+    const int64_t r = (u.q_off + t) * a.num_q_heads + head;
+    if (u.q_off + t >= a.total_q) return;              // total_q too small: outside the workspace
+    if (h == 0) a.lse_parts[u.split * rows + r] = (l > 0.f) ? ((m == kNegInf) ? 0.f : m) + __log2f(l) : kNegInf;
+    if (l > 0.f) {
+      float *prow = a.o_parts + (u.split * rows + r) * D;
+#pragma unroll
+      for (int nb = 0; nb < G::kNB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = oacc[nb][4 * g + i] * inv;
+          *reinterpret_cast<f32x4 *>(prow + 32 * nb + 8 * g + 4 * h) = ov;
+        }
+    }
+    return;
+  }
   __bf16 *orow = static_cast<__bf16 *>(a.o) + (u.q_off + t) * a.o_stride_tok + (int64_t)head * a.o_stride_head;
 #pragma unroll
   for (int nb = 0; nb < G::kNB; ++nb)
@@ -505,9 +534,20 @@ hipError_t launch_pp(const PrefillArgs &a, hipStream_t stream) {
   const int gh = pf_heads_per_wg(a.num_q_heads / a.num_kv_heads);
   const int tq = 32 * G::kW / gh;
   const int64_t q_tiles = (a.max_seqlen_q + tq - 1) / tq;
-  const int64_t blocks = q_tiles * a.batch * (a.num_q_heads / gh);
+  const int64_t blocks = q_tiles * (a.kv_splits > 1 ? a.kv_splits : 1) * a.batch * (a.num_q_heads / gh);
   hipLaunchKernelGGL((prefill_pipe_kernel<D, KV>), dim3((unsigned)blocks), dim3(64 * G::kW), 0, stream, a);
-  return hipGetLastError();
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.kv_splits <= 1) return err;
+  MergeArgs m{};
+  m.o_parts = a.o_parts;
+  m.lse_parts = a.lse_parts;
+  m.num_splits = a.kv_splits;
+  m.num_rows = (int64_t)a.total_q * a.num_q_heads;
+  m.head_dim_v = D;
+  m.o = a.o;
+  m.o_bf16 = 1;
+  m.lse = a.lse;
+  return launch_merge(m, stream);
 }
 
 template <int D>

@@ -27,6 +27,7 @@ struct PfUnit {
   int lq, lk;                  // request lengths
   int64_t q_off;               // first query token of the request in the packed Q
   int64_t kv_off;              // dense: first key of the request in packed K/V
+  int split;                   // the workgroup's split of the keys (0 without splits)
 };
 
 // Heads per workgroup for a GQA group: the largest of 4, 2, 1 dividing it.
@@ -37,14 +38,18 @@ __host__ __device__ __forceinline__ int pf_heads_per_wg(int group) {
 // The rows workgroup blockIdx.x owns when it holds `blocks` 32-row blocks:
 // gh heads of one KV group times tq = 32 blocks / gh tokens, tiles counted
 // from the end of the request (index slowest, so the longest rows of every
-// request start first). False when the request has no tile of that index.
+// request start first), and with key splits the split it walks. False when
+// the request has no tile of that index.
 __device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit &u) {
   const int group = a.num_q_heads / a.num_kv_heads;
   u.gh = pf_heads_per_wg(group);
   u.tq = 32 * (blocks / u.gh);
   const int head_groups = a.num_q_heads / u.gh;
+  const int splits = a.kv_splits > 1 ? a.kv_splits : 1;
   int L = blockIdx.x;
-  const int qt = L / (a.batch * head_groups);
+  const int qt = L / (splits * a.batch * head_groups);
+  L %= splits * a.batch * head_groups;
+  u.split = L / (a.batch * head_groups);
   L %= a.batch * head_groups;
   u.b = L / head_groups;
   u.h0 = (L % head_groups) * u.gh;

@@ -341,6 +341,14 @@ def ragged_paged_prefill(seed: int = 4) -> PrefillCase:
                         name="ragged_paged_prefill_q512-1024_kv80k_h32kv8_d128_ps64")
 
 
+def single_chunk_prefill(seed: int = 6) -> PrefillCase:
+    """One request's 512-token prefill chunk appended to an 80K-token context
+    (kv_len 81920, bottom-right causal), otherwise as ragged_paged_prefill:
+    too few query tiles to fill the CUs without key splits."""
+    return prefill_case(q_lens=[512], kv_lens=[81920], hq=32, hkv=8, d=128, seed=seed, causal=True, paged=True,
+                        page_size=64, name="single_chunk_prefill_q512_kv80k_h32kv8_d128_ps64")
+
+
 def mla_decode(kv_dtype: str = "bf16", seed: int = 5, causal: bool = True) -> DecodeCase:
     """MLA-shaped split-KV decode: batch 8, 4 query tokens, 64 heads folded
     with 2 tokens into 128 rows, one latent KV head of width 576 (K = all 576,
