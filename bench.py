@@ -5,6 +5,13 @@ the path) on the Qwen3-14B-shaped paged decode: batch 64, one query token,
 40 query / 8 KV heads, head_dim 128, page_size 128, seq_lens uniform on
 [256, 8192], bf16. Inputs are resident in HBM before timing starts.
 
+Beside the average over the timed steps (ms_per_step, value), the line holds
+the per-step median and p10-p90 range with warm caches and with L2 and the
+MALL evicted before each step (a 512 MB read), the split kernel's
+roofline, the secondary workloads (prefill, MLA decode, FP8 prefill, the
+prologue kernels), ceilings measured on the GPU with library kernels, a
+sha256 of the input bytes, and the oracle timed on the host.
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
@@ -18,6 +25,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -64,6 +73,115 @@ def time_events(fn, steps: int, stream) -> float:
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def time_each(fn, steps: int, stream, before=None) -> list[float]:
+    """Milliseconds of each of `steps` calls of fn, one HIP event pair per
+    call on `stream`; `before` (untimed) runs ahead of each call."""
+    import torch
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        if before is not None:
+            before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def spread(ms: list[float]) -> dict:
+    q = np.percentile(np.asarray(ms), [10, 50, 90])
+    return {"median_ms": round(float(q[1]), 5), "p10_ms": round(float(q[0]), 5), "p90_ms": round(float(q[2]), 5),
+            "n": len(ms)}
+
+
+def ceilings_lib():
+    """The ceiling kernels (softmax_attention_paged_amd/ceilings), built
+    beside the attention library."""
+    import ctypes
+    path = os.path.join(ROOT, "softmax_attention_paged_amd", "libattn_ceilings.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build first (python -m softmax_attention_paged_amd.build)")
+    lib = ctypes.CDLL(path)
+    lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+class Evictor:
+    """Reads a 512 MB buffer with the streaming-read kernel: evicts the
+    inputs from L2 and the 256 MB MALL without leaving dirty lines whose
+    write-back would load the next timed step."""
+
+    def __init__(self, dev):
+        import torch
+        self.lib = ceilings_lib()
+        self.buf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        self.sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def __call__(self):
+        rc = self.lib.ceil_stream_read(self.buf.data_ptr(), self.buf.numel(), self.sink.data_ptr(), 4096,
+                                       self.stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"ceil_stream_read failed: {rc}")
+
+
+def measured_peaks() -> dict:
+    """Ceilings measured on this GPU, as secondary denominators: a 1 GiB
+    streaming read and a bf16 32x32x16 MFMA loop (the ceiling kernels), and
+    for context a 1 GiB torch copy (bytes read + written) and a bf16 8192^3
+    GEMM through torch.matmul (hipBLASLt)."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    lib = ceilings_lib()
+    x = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+
+    def read():
+        if lib.ceil_stream_read(x.data_ptr(), x.numel(), sink.data_ptr(), 4096, stream.cuda_stream) != 0:
+            raise RuntimeError("ceil_stream_read failed")
+
+    iters, blocks = 4096, 2048            # 2048 workgroups of 4 waves: 8 per SIMD
+
+    def mfma():
+        if lib.ceil_mfma_bf16(sink.data_ptr(), iters, blocks, stream.cuda_stream) != 0:
+            raise RuntimeError("ceil_mfma_bf16 failed")
+
+    for f in (read, mfma):
+        f()
+    read_ms = time_events(read, 10, stream)
+    mfma_ms = time_events(mfma, 5, stream)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    copy_ms = time_events(lambda: y.copy_(x), 10, stream)
+    del x, y
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    gemm_ms = time_events(lambda: torch.matmul(a, b, out=c), 10, stream)
+    del a, b, c, sink
+    torch.cuda.empty_cache()
+    mfma_flops = blocks * 4 * iters * 4 * 32768
+    return {"stream_read_GBs": round((1 << 30) / (read_ms * 1e-3) / 1e9, 1),
+            "mfma_bf16_loop_TFLOPs": round(mfma_flops / (mfma_ms * 1e-3) / 1e12, 1),
+            "torch_copy_GBs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "hipblaslt_bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+
+
+def input_sha256(tensors) -> str:
+    """sha256 over the bytes of the workload's host-side input tensors."""
+    import torch
+    h = hashlib.sha256()
+    for t in tensors:
+        h.update(memoryview(t.contiguous().view(-1).view(torch.uint8).numpy()))
+    return h.hexdigest()
 
 
 def time_graph(fn, steps: int) -> float:
@@ -348,6 +466,13 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     ms = time_events(step, args.steps, stream)
+    # Per-step spread, warm (inputs as the previous step left the caches) and
+    # cold (a 512 MB read ahead of each step evicts L2 and the MALL).
+    warm = spread(time_each(step, args.steps, stream))
+    evict = Evictor(dev)
+    cold = spread(time_each(step, args.steps, stream, before=evict))
+    del evict
+    cold["GBs_at_median"] = round(kv_bytes / (cold["median_ms"] * 1e-3) / 1e9, 2)
     # The merge alone on the same partials, to separate the split kernel.
     s, r = plan["num_splits"], b_n * q_len * hq
     merge_ms = 0.0
@@ -386,7 +511,10 @@ def main() -> int:
                    "num_kv_heads": case.k_cache.shape[2], "head_dim": d, "page_size": case.page_size,
                    "total_kv_tokens": tokens, "kv_bytes": kv_bytes, "seed": args.seed,
                    "num_splits": plan["num_splits"], "split_tokens": plan["split_tokens"],
+                   "input_sha256": input_sha256([case.q, case.k_cache, case.v_cache, case.block_table,
+                                                 case.seq_lens]),
                    "parallelism": "single GPU"},
+        "step_spread": {"warm": warm, "cold": cold},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "decode_gqa_wave_kernel<128, false>", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -397,6 +525,8 @@ def main() -> int:
     }
     if not args.no_secondary:
         del c, ws, out
+        torch.cuda.empty_cache()
+        line["measured_peaks"] = measured_peaks()
         torch.cuda.empty_cache()
         sec = {}
         for key, fn in secondaries.items():

@@ -1,7 +1,9 @@
 """Build the gfx950 HIP library in-tree: softmax_attention_paged_amd/libattn_mi355x.so.
 
 Every source under csrc/ is compiled with hipcc for gfx950 only, then linked
-into one shared library exporting the C ABI declared in include/attn.h.
+into one shared library exporting the C ABI declared in include/attn.h. The
+benchmark's ceiling kernels (ceilings/ceilings.hip) go into a second object,
+libattn_ceilings.so.
 
     python -m softmax_attention_paged_amd.build [-v]
 """
@@ -19,6 +21,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+# The benchmark's ceiling kernels (a streaming read, an MFMA loop): their own
+# shared object, not part of the attention library.
+CEIL_SRC = os.path.join(PKG_DIR, "ceilings", "ceilings.hip")
+CEIL_PATH = os.path.join(PKG_DIR, "libattn_ceilings.so")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -62,15 +68,20 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+    _link(LIB_PATH, objs, verbose)
+    _link(CEIL_PATH, [_compile(CEIL_SRC, verbose)], verbose)
+    return LIB_PATH
+
+
+def _link(path: str, objs: list[str], verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,84 @@
+// Ceilings of the GPU measured with two plain kernels, for the benchmark's
+// secondary denominators (beside the published peaks): how fast a kernel can
+// stream reads from HBM, and how fast the matrix cores run a bf16
+// 32x32x16 MFMA loop with no memory traffic. Not part of the attention
+// library: built into its own shared object, loaded by the benchmark only.
+//
+//   int ceil_stream_read(const void *src, size_t bytes, unsigned *sink,
+//                        int blocks, hipStream_t stream);
+//     reads every byte of src once (16-byte loads, four in flight per lane);
+//     bytes must be a positive multiple of 16384 and src 16-byte aligned;
+//     sink holds `blocks` words (written only on a value no input of zeros
+//     and ones produces, so in practice never). Returns 0, or -1 on bad
+//     arguments, or the HIP error code of the launch.
+//   int ceil_mfma_bf16(float *sink, int iters, int blocks, hipStream_t stream);
+//     each wave of `blocks` workgroups of four waves runs 4 * iters
+//     independent-chain MFMAs (32768 flops each); sink holds blocks * 4
+//     floats. Returns 0, -1 on bad arguments, or the HIP error code.
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kGroup = 4 * kThreads;   // 16-byte chunks a workgroup reads per round
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *__restrict__ src, size_t groups,
+                                                               unsigned *sink) {
+  unsigned acc = 0;
+  for (size_t g = blockIdx.x; g < groups; g += gridDim.x) {
+    const u32x4 *p = src + g * kGroup + threadIdx.x;
+    const u32x4 a = p[0], b = p[kThreads], c = p[2 * kThreads], d = p[3 * kThreads];
+    acc ^= a.x ^ b.y ^ c.z ^ d.w ^ (a.w + b.x + c.y + d.z);
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float *sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = static_cast<__bf16>(0.001f * (lane + e));
+    b[e] = static_cast<__bf16>(0.002f * (lane - e));
+  }
+  f32x16 c0{}, c1{}, c2{}, c3{};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  if (lane == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ceil_stream_read(const void *src, size_t bytes, unsigned *sink, int blocks, hipStream_t stream) {
+  if (!src || !sink || blocks < 1 || bytes == 0 || bytes % (16 * kGroup) ||
+      reinterpret_cast<uintptr_t>(src) % 16)
+    return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4 *>(src), bytes / (16 * kGroup), sink);
+  return static_cast<int>(hipGetLastError());
+}
+
+int ceil_mfma_bf16(float *sink, int iters, int blocks, hipStream_t stream) {
+  if (!sink || iters < 1 || blocks < 1) return -1;
+  hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(kThreads), 0, stream, sink, iters);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // extern "C"

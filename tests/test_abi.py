@@ -35,6 +35,21 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_ffi.EXPORTS), "binding and header disagree"
 
 
+def test_ceiling_kernels_library_loads_and_rejects_bad_arguments():
+    # the benchmark's measured ceilings: a separate object, checked on the
+    # host only (every call below fails validation before any launch)
+    path = os.path.join(ROOT, "softmax_attention_paged_amd", "libattn_ceilings.so")
+    assert os.path.exists(path), "ceiling kernels not built"
+    lib = ctypes.CDLL(path)
+    lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.ceil_stream_read(FAKE, 1000, FAKE, 64, None) == -1        # not a multiple of 16 KiB
+    assert lib.ceil_stream_read(FAKE + 8, 16384, FAKE, 64, None) == -1   # misaligned
+    assert lib.ceil_stream_read(None, 16384, FAKE, 64, None) == -1
+    assert lib.ceil_mfma_bf16(FAKE, 0, 8, None) == -1
+    assert lib.ceil_mfma_bf16(None, 8, 8, None) == -1
+
+
 def test_ctypes_mirrors_match_the_c_compiler_layout(tmp_path):
     # gcc compiles a probe against include/attn.h that prints sizeof and the
     # offset of every field the ctypes mirrors declare; the two must agree.
