@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1,          /* null pointer, bad size, inconsistent shapes  */
-  ATTN_ERR_UNSUPPORTED = 2,          /* valid request this build has no kernel for     */
+  ATTN_ERR_UNSUPPORTED = 2,          /* valid request the library has no kernel for    */
   ATTN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < attn_decode_workspace_size() */
   ATTN_ERR_HIP = 4                   /* a kernel launch failed                         */
 } attn_status_t;
