@@ -98,7 +98,8 @@ typedef enum {
  *          the call runs unsplit. Results equal the unsplit ones up to
  *          rounding. total_q must equal cu_seqlens_q[batch]: query rows at
  *          or past a smaller total_q are not written (nor is the workspace
- *          beyond its size).
+ *          beyond its size); with a larger one, the rows of o (and lse)
+ *          past cu_seqlens_q[batch] receive unspecified values.
  *   qkv_dtype  ATTN_BF16 (a zeroed struct; the scales are ignored), or
  *          ATTN_FP8_E4M3: q, k and v hold E4M3 codes with per-tensor
  *          dequantisation scales q_scale, k_scale, v_scale > 0 (value = code
