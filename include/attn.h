@@ -144,10 +144,12 @@ typedef struct {
 /* Workspace bytes attn_prefill will use for p: S * total_q * Hq * (Dv + 1) * 4
  * when the plan splits the keys of each query tile into S > 1 ranges (bf16,
  * contiguous o [total_q, Hq, Dv], total_q > 0), else 0. With kv_splits = 0
- * the planner splits only when the query tiles alone would not fill the CUs
- * once (long keys, very few query rows; splits of >= 2048 keys); each
- * split's normalised partial and LSE are then merged by attn_merge_lse's
- * reducer. Only shapes and scalars are examined. */
+ * the planner splits when the workgroups of the query tiles (counted from
+ * total_q) fill at most half of the CUs' slots (toward one full round) or
+ * leave a last round at most three quarters full (four splits), with no
+ * split under 8192 keys (long keys, few query rows); each split's
+ * normalised partial and LSE are then merged by attn_merge_lse's reducer.
+ * Only shapes and scalars are examined. */
 size_t attn_prefill_workspace_size(const attn_prefill_params *p);
 
 /* Enqueue ragged prefill. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,

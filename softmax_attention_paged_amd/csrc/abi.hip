@@ -257,13 +257,20 @@ attn_status_t validate_prefill(const attn_prefill_params *p, bool shapes_only = 
 }
 
 // Key splits of a bf16 prefill: workgroups per query tile along the keys.
-// The launch has q_tiles * batch * head_groups workgroups (an upper bound:
-// requests shorter than max_seqlen_q have fewer tiles); only when that does
-// not fill one round of the CUs' slots are the keys split, into enough
-// ranges to fill it, none shorter than 2048 keys. Splitting costs more than
-// the merge: workgroups that share a query tile's K/V stream in step and
-// hit in L2, and a split halves how many do, so a launch that already fills
-// the CUs (even over uneven rounds) runs faster unsplit.
+// Workgroups are counted from total_q (query tiles of tq = kPrefillRows / gh
+// tokens, times the head groups) against the CUs' slots (two workgroups per
+// CU at D <= 128, one above). Measured on 80K-key paged prefills:
+//   - at most half a round (under one workgroup per CU): split by the largest
+//     power of two that keeps the launch within one round (one 512-query
+//     chunk, 128 workgroups: 1.56 -> 0.67 ms at four splits);
+//   - more than one round with a last round at most three quarters full:
+//     four splits (768 workgroups over 512 slots: 4.67 -> 4.40 ms);
+//   - otherwise unsplit: between half and one round, or whole rounds, the
+//     splits cost more than they balance (384 workgroups: 1.68 ms unsplit,
+//     1.75-1.81 split).
+// No split is shorter than 8192 keys. Splits are numbered slowest, so the
+// workgroups running together still share each K/V tile they stream as
+// widely in L2 as without splits.
 struct PrefillPlan {
   int splits;
   int split_tokens;
@@ -280,11 +287,15 @@ PrefillPlan plan_prefill(const attn_prefill_params *p) {
   if (splits <= 0) {
     const int group = p->num_q_heads / p->num_kv_heads;
     const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
-    const int64_t units = cdiv(p->max_seqlen_q, kPrefillRows / gh) * p->batch * (p->num_q_heads / gh);
+    const int64_t units = std::max<int64_t>(1, cdiv(p->total_q, kPrefillRows / gh)) * (p->num_q_heads / gh);
     const int64_t slots = (int64_t)attn::kNumCUs * (p->head_dim_qk <= 128 ? 2 : 1);
-    splits = 1;
-    if (units < slots) splits = (int)std::min<int64_t>(cdiv(slots, std::max<int64_t>(units, 1)),
-                                                       std::max<int64_t>(1, p->max_seqlen_kv / 2048));
+    int64_t sp = 1;
+    if (2 * units <= slots) {
+      while (2 * sp * units <= slots) sp *= 2;
+    } else if (units > slots && units < 4 * slots && units % slots != 0 && 4 * (units % slots) <= 3 * slots) {
+      sp = 4;
+    }
+    splits = (int)std::max<int64_t>(1, std::min<int64_t>(sp, p->max_seqlen_kv / 8192));
   }
   splits = std::min(splits, attn::kMaxSplits);
   if (splits <= 1) return pl;

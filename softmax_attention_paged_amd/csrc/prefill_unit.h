@@ -37,19 +37,22 @@ __host__ __device__ __forceinline__ int pf_heads_per_wg(int group) {
 
 // The rows workgroup blockIdx.x owns when it holds `blocks` 32-row blocks:
 // gh heads of one KV group times tq = 32 blocks / gh tokens, tiles counted
-// from the end of the request (index slowest, so the longest rows of every
-// request start first), and with key splits the split it walks. False when
-// the request has no tile of that index.
+// from the end of the request (index slow, so the longest rows of every
+// request start first), and with key splits the split it walks (slowest:
+// the workgroups running together walk the same key range of as many query
+// tiles as without splits, so each K/V tile they stream is shared as widely
+// in L2). False when the request has no tile of that index.
 __device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit &u) {
   const int group = a.num_q_heads / a.num_kv_heads;
   u.gh = pf_heads_per_wg(group);
   u.tq = 32 * (blocks / u.gh);
   const int head_groups = a.num_q_heads / u.gh;
-  const int splits = a.kv_splits > 1 ? a.kv_splits : 1;
+  const int q_tiles = (a.max_seqlen_q + u.tq - 1) / u.tq;
   int L = blockIdx.x;
-  const int qt = L / (splits * a.batch * head_groups);
-  L %= splits * a.batch * head_groups;
-  u.split = L / (a.batch * head_groups);
+  const int per_split = q_tiles * a.batch * head_groups;
+  u.split = L / per_split;
+  L %= per_split;
+  const int qt = L / (a.batch * head_groups);
   L %= a.batch * head_groups;
   u.b = L / head_groups;
   u.h0 = (L % head_groups) * u.gh;

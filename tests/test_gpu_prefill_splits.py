@@ -91,7 +91,7 @@ def test_without_lse_and_with_a_caller_workspace():
     print(compare(f64(out2), ref2, lse2.numpy(), lref2))
 
 
-def test_planner_splits_only_launches_that_do_not_fill_the_cus():
+def test_planner_splits_launches_of_few_long_units():
     def ws(q_lens, kv_lens, hq=32, hkv=8):
         case = inputs.prefill_case(q_lens=q_lens, kv_lens=kv_lens, hq=hq, hkv=hkv, d=128, seed=1, paged=True,
                                    page_size=64, name="plan")
@@ -99,17 +99,27 @@ def test_planner_splits_only_launches_that_do_not_fill_the_cus():
         return sap.prefill_workspace_size(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv,
                                           block_table=c.block_table, max_seqlen_q=c.max_seqlen_q,
                                           max_seqlen_kv=c.max_seqlen_kv, causal=True)
+    row = 32 * 129 * 4                     # bytes of one query token's partials per split
     # one request of 512 queries over 40K keys: 16 query tiles x 8 head
-    # groups = 128 workgroups; split four ways, each split over 10K keys
-    assert ws([512], [40000]) == 4 * 512 * 32 * 129 * 4
-    # four requests of 1024 queries fill the CUs twice over: unsplit
+    # groups = 128 workgroups, a quarter of the 512 slots: four splits
+    assert ws([512], [40000]) == 4 * 512 * row
+    # ... over 24K keys: no split under 8192 keys, so two
+    assert ws([512], [24000]) == 2 * 512 * row
+    # 1024 queries: 256 workgroups, half the slots: two splits
+    assert ws([1024], [40000]) == 2 * 1024 * row
+    # 512 + 1024 queries: 384 workgroups, between half and one round: unsplit
+    assert ws([512, 1024], [40000, 40000]) == 0
+    # four requests of 512-1024 queries over 80K keys: 768 workgroups over 512
+    # slots, the second round half full: four splits
+    assert ws([512, 1024, 512, 1024], [81920] * 4) == 4 * 3072 * row
+    # 1024 workgroups are two whole rounds: unsplit
     assert ws([1024] * 4, [40000] * 4) == 0
-    # short keys are never split below 2048 per split
-    assert ws([64], [3000]) == 0
+    # short keys are never split
+    assert ws([64], [8000]) == 0
 
 
 def test_planner_split_matches_the_oracle():
-    case = inputs.prefill_case(q_lens=[300], kv_lens=[20000], hq=8, hkv=2, d=128, seed=350, paged=True,
+    case = inputs.prefill_case(q_lens=[300], kv_lens=[40000], hq=8, hkv=2, d=128, seed=350, paged=True,
                                page_size=64, name="planned")
     c = case.to(DEV)
     assert sap.prefill_workspace_size(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv,
