@@ -163,10 +163,24 @@ DecodePlan plan_decode(const attn_decode_params *p) {
   if (p->num_splits > 0) {
     splits = p->num_splits;
   } else if (pl.mla) {
-    // MFMA-bound: about two workgroups per CU, but no split shorter than 1024 keys.
-    const int64_t want = cdiv(2 * attn::kNumCUs, base_units > 0 ? base_units : 1);
-    const int64_t by_len = cdiv(window_span(p), 1024);
-    splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
+    // MFMA-bound, one workgroup per CU: the launch takes ceil(U S / CUs)
+    // rounds of units 1/S as long, and each split adds its own prologue,
+    // epilogue and merge work (about 0.5 % of a unit per split, from the
+    // 80K-key timings: 16 splits = one round 0.426 ms, 32 = two rounds
+    // 0.457 ms, 24 = a round and a half 0.551 ms). Take the S that
+    // minimises ceil(U S / CUs) / S * (1 + S / 200), the smallest on ties;
+    // no split shorter than 1024 keys.
+    const int64_t u = base_units > 0 ? base_units : 1;
+    const int64_t by_len = std::max<int64_t>(1, std::min<int64_t>(cdiv(window_span(p), 1024), attn::kMaxSplits));
+    double best = 0.0;
+    splits = 1;
+    for (int64_t s = 1; s <= by_len; ++s) {
+      const double cost = (double)cdiv(u * s, attn::kNumCUs) / (double)s * (1.0 + (double)s / 200.0);
+      if (s == 1 || cost < best * 0.999) {
+        best = cost;
+        splits = (int)s;
+      }
+    }
   } else {
     // HBM-bound: many small units so ragged lengths balance across 256 CUs,
     // but no split shorter than 256 keys.

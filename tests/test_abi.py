@@ -236,6 +236,19 @@ def test_latent_workspace_equals_tokenspeed_formula():
         assert info.workspace_bytes == oracle.mla_packed_workspace_bytes(8, 64, 4, splits)
 
 
+@pytest.mark.parametrize("batch,splits", [(8, 16), (12, 10), (24, 16), (64, 2)])
+def test_latent_planner_fills_whole_rounds(batch, splits):
+    # one workgroup per CU: units = batch x 2 query groups x S; the planner
+    # takes whole rounds of 256 (16 x 16, 48 x 16 = 3 x 256, 128 x 2)
+    # or just under one (24 x 10 = 240) rather than a partial last round
+    p = decode_params(num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, q_len=4,
+                      v_cache=FAKE, k_stride_page=64 * 576, k_stride_tok=576, k_stride_head=576,
+                      v_stride_page=64 * 576, v_stride_tok=576, v_stride_head=576, page_size=64,
+                      num_pages=10240 * 8, max_seq_len=81920, block_table_stride=1280, batch=batch)
+    st, info = plan(p)
+    assert st == 0 and info.num_splits == splits
+
+
 def test_gqa_plan_folds_heads_and_tokens_into_16_rows():
     for q_len, hq, hkv, expect_f in [(1, 40, 8, 1), (4, 8, 2, 4), (4, 20, 4, 2), (3, 8, 8, 3), (4, 16, 1, 1)]:
         st, info = plan(decode_params(q_len=q_len, num_q_heads=hq, num_kv_heads=hkv, block_table_stride=8))
