@@ -48,16 +48,18 @@ def kernel_source_hash(names: list[str]) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, sources: list[str]) -> dict | None:
+def load_traffic(kernel: str, sources: list[str], plan: dict) -> dict | None:
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
     WRITE_SIZE), stored under profiles/; only used while the kernel sources
-    are unchanged since the measurement."""
+    and the launch's split plan are unchanged since the measurement."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_hash") != kernel_source_hash(sources):
+        return None
+    if (rec.get("num_splits"), rec.get("split_tokens")) != (plan["num_splits"], plan["split_tokens"]):
         return None
     return rec
 
@@ -493,7 +495,7 @@ def main() -> int:
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     achieved = alg_bytes / (split_ms * 1e-3) / 1e9
     sources = ["decode_gqa.hip", "device_common.h", "attn_internal.h"]
-    traffic = load_traffic("decode_gqa_qwen3_14b", sources)
+    traffic = load_traffic("decode_gqa_qwen3_14b", sources, plan)
     line = {
         "metric": "decode KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
         "value": round(gbs, 2),
