@@ -9,7 +9,8 @@ Beside the average over the timed steps (ms_per_step, value), the line holds
 the per-step median and p10-p90 range with warm caches and with L2 and the
 MALL evicted before each step (a 512 MB read), the split kernel's
 roofline, the secondary workloads (prefill, MLA decode, FP8 prefill, the
-prologue kernels), ceilings measured on the GPU with library kernels, a
+prologue kernels; each timed once the GPU's clocks have settled under it, as
+the median of five event windows), ceilings measured on the GPU, a
 sha256 of the input bytes, and the oracle timed on the host.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -186,6 +187,26 @@ def input_sha256(tensors) -> str:
     return h.hexdigest()
 
 
+def settle(fn, seconds: float = 0.3) -> None:
+    """Run fn untimed for about `seconds`: the GPU's clocks ramp up over the
+    first tens of milliseconds of sustained work (an 80K MLA decode runs
+    0.46-0.55 ms per call in its first 20 calls and 0.41 ms after), so a
+    short workload is timed only once they have settled."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
+def time_settled(fn, steps: int, stream, windows: int = 5) -> float:
+    """Median over `windows` HIP-event windows of `steps` calls each, after
+    the clocks have settled."""
+    settle(fn)
+    return float(np.median([time_events(fn, steps, stream) for _ in range(windows)]))
+
+
 def time_graph(fn, steps: int) -> float:
     """Average milliseconds per call of fn, with the calls captured in one HIP
     graph and the replay timed by HIP events: for kernels shorter than the
@@ -272,9 +293,7 @@ def secondary_prefill(name_fn, steps: int, kv_splits: int = 0) -> dict:
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=c.q.device)
     splits = ws_bytes // (tq * hq * (d + 1) * 4) if ws_bytes else 1
     fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, softmax_scale=c.scale, out=out, workspace=ws, **kv, **kw)
-    for _ in range(3):
-        fn()
-    ms = time_events(fn, steps, torch.cuda.current_stream())
+    ms = time_settled(fn, steps, torch.cuda.current_stream())
     tf = flops / (ms * 1e-3) / 1e12
     kernel = f"prefill_pipe_kernel<{d}, {1 if c.paged else 0}>" + (" + merge" if splits > 1 else "")
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "kv_splits": splits,
@@ -296,9 +315,7 @@ def secondary_mla(kv_dtype: str, steps: int) -> dict:
     ws = torch.empty(plan["workspace_bytes"] + 16, dtype=torch.uint8, device=c.q.device)
     out = torch.empty((b_n, q_len, hq, 512), dtype=torch.bfloat16, device=c.q.device)
     fn = lambda: sap.decode_paged(c.q, c.k_cache, None, c.block_table, c.seq_lens, workspace=ws, out=out, **kw)
-    for _ in range(3):
-        fn()
-    ms = time_events(fn, steps, torch.cuda.current_stream())
+    ms = time_settled(fn, steps, torch.cuda.current_stream())
     lens = case.seq_lens.tolist()
     pairs = hq * sum(min(lk, max(0, lk - q_len + t + 1)) if case.causal else lk for lk in lens for t in range(q_len))
     flops = pairs * 2 * (dqk + 512)
@@ -326,9 +343,7 @@ def secondary_prefill_fp8(steps: int) -> dict:
     fn = lambda: sap.prefill(f8(c.q), f8(c.k), f8(c.v), c.cu_seqlens_q, cu_seqlens_kv=c.cu_seqlens_kv,
                              max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale,
                              causal=True, out=out, q_scale=c.q_scale, k_scale=c.k_scale, v_scale=c.v_scale)
-    for _ in range(3):
-        fn()
-    ms = time_events(fn, steps, torch.cuda.current_stream())
+    ms = time_settled(fn, steps, torch.cuda.current_stream())
     pairs = causal_pairs(case.cu_seqlens_q.tolist(), case.cu_seqlens_kv.diff().tolist(), True) * hq
     qk, pv = pairs * 2 * dqk, pairs * 2 * dv
     tf = (qk + pv) / (ms * 1e-3) / 1e12
@@ -353,9 +368,7 @@ def secondary_mla_pack(steps: int) -> dict:
     v_out = torch.empty((t, h, dv), dtype=torch.float8_e4m3fn, device="cuda:0")
     fn = lambda: sap.mla_kv_pack_fp8(c.k_nope, c.k_rope, c.v, k_scale=c.k_scale, v_scale=c.v_scale,
                                      k_out=k_out, v_out=v_out)
-    for _ in range(3):
-        fn()
-    ms = time_events(fn, steps, torch.cuda.current_stream())
+    ms = time_settled(fn, steps, torch.cuda.current_stream())
     alg = t * h * (dn + dv) * 2 + t * dr * 2 + t * h * (dn + dr + dv)    # bf16 in (rope once), E4M3 out
     gbs = alg / (ms * 1e-3) / 1e9
     return {"workload": f"mla_kv_pack_fp8_t{t}_h{h}_d{dn}+{dr}_v{dv}", "ms": round(ms, 4), "GB/s": round(gbs, 1),
@@ -375,9 +388,8 @@ def secondary_append(steps: int) -> dict:
     c = case.to("cuda:0")
     fn = lambda: sap.cache_append(c.k_new, c.v_new, c.k_cache, c.v_cache, c.slot_mapping,
                                   layer_base_rows=c.layer_base_rows)
-    for _ in range(3):
-        fn()
-    ms = time_graph(fn, max(steps, 20))     # a 14 us kernel: replayed from a graph
+    settle(fn)
+    ms = float(np.median([time_graph(fn, max(steps, 20)) for _ in range(5)]))   # a 14 us kernel: replayed from a graph
     n, hkv, dk = case.k_new.shape
     alg = 2 * (n * hkv * dk * 2) * 2 + n * 8                            # K and V read and written, slots
     gbs = alg / (ms * 1e-3) / 1e9
