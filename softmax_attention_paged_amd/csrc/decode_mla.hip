@@ -13,9 +13,10 @@
 //
 // Workgroup: 4 waves x 32 rows at one wave per SIMD, so that the 32 x 512
 // FP32 output block of a wave (256 registers per lane) fills the accumulation
-// registers; the query operand of the first 288 columns stays in vector
-// registers, the other 288 columns wait in LDS (rows padded to 592 bytes,
-// bank-conflict-free). Per 32-key tile:
+// registers; the query operand of the first 256 columns stays in vector
+// registers, the other 320 columns wait in LDS (rows padded to 656 bytes,
+// bank-conflict-free; 84 KB, with the two 36 KB tiles 156 KB of the CU's
+// 160 KB). Per 32-key tile:
 //   - the latent tile is gathered through the block table ONCE into LDS
 //     (double-buffered, one tile ahead): bf16 rows by direct HBM -> LDS
 //     loads, fp8 e4m3 rows through registers, widened to bf16 exactly on the
@@ -55,8 +56,8 @@ constexpr int kRowB = kDk * 2;                     // bytes of a latent row in L
 constexpr int kChunks = kDk / 8;                   // 16-byte chunks per row
 constexpr int kTileB = kTileN * kRowB;             // bytes of one LDS tile
 constexpr int kKB = kDk / 16;                      // 36 QK k-steps
-constexpr int kKBReg = 18;                         // k-steps whose Q operand stays in registers
-constexpr int kRing = 4;                           // LDS operand reads in flight ahead of the MFMAs
+constexpr int kKBReg = 16;                         // k-steps whose Q operand stays in registers
+constexpr int kRing = 3;                           // LDS operand reads in flight ahead of the MFMAs
 constexpr int kQRowB = (kDk - 16 * kKBReg) * 2 + 16;   // LDS bytes per row of the other Q columns (padded)
 constexpr int kNB = kDv / 32;                      // 16 PV channel blocks
 constexpr int kDma = kTileN * kChunks / 64 / kW;   // 9 direct loads per wave per bf16 tile
