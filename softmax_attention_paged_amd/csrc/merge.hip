@@ -11,9 +11,11 @@
 // One wave per row: the lanes read the split LSEs once and reduce M and the
 // weights with wave shuffles. The row's float4 chunks are spread over the
 // lanes; when they do not fill the wave, lane groups take every G-th split
-// and are summed with shuffles at the end. Within a group, partial rows are
-// read four splits at a time so their loads are in flight together. Splits
-// with weight 0 (lse = -inf, an empty split) are never read.
+// and are summed with shuffles at the end. A lane holding CPL chunks of a
+// row reads 16 / CPL partial rows at once, so up to 16 float4 loads per lane
+// are in flight together (a 22-split decode of 128-wide rows is read in one
+// batch: one round trip for the LSEs, one for the partials). Splits with
+// weight 0 (lse = -inf, an empty split) are never read.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -22,10 +24,12 @@ namespace attn {
 namespace {
 
 constexpr int kMergeWaves = 4;
-constexpr int kMaxChunksPerLane = 4;   // float4 chunks: head_dim_v <= 1024
-constexpr int kBatch = 4;              // partial rows read together
+constexpr int kLoadsInFlight = 16;     // float4 loads per lane issued together
 
+// CPL: float4 chunks per lane (1, 2 or 4; head_dim_v <= 1024).
+template <int CPL>
 __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
+  constexpr int kBatch = kLoadsInFlight / CPL;   // partial rows read together
   const int lane = threadIdx.x & 63;
   const int64_t rowi = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (rowi >= a.num_rows) return;
@@ -56,13 +60,13 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
   const int G = nchunks >= 64 ? 1 : (nchunks >= 32 ? 2 : 4);
   const int glanes = 64 / G;
   const int g = lane / glanes, gl = lane % glanes;
-  f32x4 acc[kMaxChunksPerLane];
+  f32x4 acc[CPL];
 #pragma unroll
-  for (int k = 0; k < kMaxChunksPerLane; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < CPL; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int s0 = 0; s0 < a.num_splits; s0 += kBatch * G) {
     float w[kBatch];
-    f32x4 v[kBatch][kMaxChunksPerLane];
+    f32x4 v[kBatch][CPL];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int sg = s0 + u * G;            // this batch slot's split for group 0; group g adds g
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
       const int s = sg + g;
       const float *src = a.o_parts + ((int64_t)s * a.num_rows + rowi) * a.head_dim_v;
 #pragma unroll
-      for (int k = 0; k < kMaxChunksPerLane; ++k) {
+      for (int k = 0; k < CPL; ++k) {
         const int c = gl + glanes * k;
         v[u][k] = (wu != 0.f && c < nchunks) ? *reinterpret_cast<const f32x4 *>(src + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -85,19 +89,19 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-      for (int k = 0; k < kMaxChunksPerLane; ++k) acc[k] += w[u] * v[u][k];
+      for (int k = 0; k < CPL; ++k) acc[k] += w[u] * v[u][k];
   }
   // sum the lane groups (lanes gl, gl + glanes, ... hold the same chunks)
   for (int off = glanes; off < 64; off <<= 1)
 #pragma unroll
-    for (int k = 0; k < kMaxChunksPerLane; ++k)
+    for (int k = 0; k < CPL; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[k][e] += wave_shfl_xor(acc[k][e], off);
 
   const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
   if (g == 0) {
 #pragma unroll
-    for (int k = 0; k < kMaxChunksPerLane; ++k) {
+    for (int k = 0; k < CPL; ++k) {
       const int c = gl + glanes * k;
       if (c >= nchunks) continue;
       const f32x4 r = acc[k] * inv;
@@ -119,7 +123,17 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
   const int64_t blocks = (a.num_rows + kMergeWaves - 1) / kMergeWaves;
-  hipLaunchKernelGGL(merge_lse_kernel, dim3((unsigned)blocks), dim3(64 * kMergeWaves), 0, stream, a);
+  // the kernel's lane layout: G groups of 64 / G lanes over the row's chunks
+  const int nchunks = a.head_dim_v >> 2;
+  const int glanes = 64 / (nchunks >= 64 ? 1 : (nchunks >= 32 ? 2 : 4));
+  const int cpl = (nchunks + glanes - 1) / glanes;
+  const dim3 grid((unsigned)blocks), block(64 * kMergeWaves);
+  if (cpl <= 1)
+    hipLaunchKernelGGL(merge_lse_kernel<1>, grid, block, 0, stream, a);
+  else if (cpl == 2)
+    hipLaunchKernelGGL(merge_lse_kernel<2>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_lse_kernel<4>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
