@@ -464,8 +464,11 @@ def main() -> int:
     alg_bytes = kv_bytes + case.q.numel() * 2 + b_n * q_len * hq * (case.head_dim_v * 2 + 4)
     flops = tokens * q_len * hq * 2 * (d + case.head_dim_v)
 
+    # the host knows the batch's total of keys (a serving scheduler does): the
+    # planner uses it to keep every split unit resident at once
     params = sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
-                               max_seq_len=c.max_seq_len, softmax_scale=c.scale, num_splits=args.num_splits)
+                               max_seq_len=c.max_seq_len, softmax_scale=c.scale, num_splits=args.num_splits,
+                               total_kv_tokens=tokens)
     plan = sap.decode_plan(params)
     ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=dev)
     out = torch.empty((b_n, q_len, hq, case.head_dim_v), dtype=torch.bfloat16, device=dev)
@@ -473,7 +476,8 @@ def main() -> int:
 
     def step():
         sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
-                         softmax_scale=c.scale, num_splits=args.num_splits, workspace=ws, out=out)
+                         softmax_scale=c.scale, num_splits=args.num_splits, workspace=ws, out=out,
+                         total_kv_tokens=tokens)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):

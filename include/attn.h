@@ -192,6 +192,12 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  *              query paragraph), so H96 with q_len 4 needs 3 tiles of 128
  *              rows instead of 4; the last tile may be partial. Output and
  *              LSE layouts are unchanged.
+ *   total_kv_tokens   optional host-side sum of seq_lens (0: unknown). With
+ *              it and num_splits = 0 the GQA planner sizes the splits so
+ *              that every unit is resident at once (units <= (total / S_len
+ *              + batch) * Hkv * q_groups fit one round of the GPU's waves),
+ *              which on ragged batches beats a fixed split length; it only
+ *              changes the plan, never the result.
  * Supported: (Dqk, Dv) in {(64,64), (128,128), (256,256)} with bf16 KV and
  * (576, 512) with Hkv == 1 and bf16 or FP8 KV; Hq % Hkv == 0; page_size a
  * power of two >= 16.
@@ -218,6 +224,7 @@ typedef struct {
   int32_t window_enabled;   /* 0: full history */
   int32_t window_left;      /* keys of context when window_enabled */
   int32_t packed_q;         /* 0: folded rows; 1: continuous token * G + head rows */
+  int64_t total_kv_tokens;  /* planner hint: host sum of seq_lens, 0 = unknown */
 } attn_decode_params;
 
 /* How attn_decode_paged will decompose a call (host-only; no device access). */

@@ -53,7 +53,7 @@ def _as_4d_cache(cache: torch.Tensor) -> torch.Tensor:
 def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                   causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
                   num_splits=0, workspace=None, out=None, lse=None, window_left=-1,
-                  packed_q=False) -> _ffi.DecodeParams:
+                  packed_q=False, total_kv_tokens=0) -> _ffi.DecodeParams:
     """Fill the C parameter struct from tensors (no device access)."""
     k4 = _as_4d_cache(k_cache)
     v4 = _as_4d_cache(v_cache if v_cache is not None else k_cache)
@@ -77,6 +77,7 @@ def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, so
     p.o, p.lse = _ptr(out), _ptr(lse)
     p.window_enabled, p.window_left = int(window_left >= 0), max(int(window_left), 0)
     p.packed_q = int(bool(packed_q))
+    p.total_kv_tokens = int(total_kv_tokens)
     return p
 
 
@@ -89,14 +90,16 @@ def decode_plan(params: _ffi.DecodeParams) -> dict:
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                  causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
                  num_splits=0, workspace=None, out=None, return_lse=False, window_left=-1,
-                 packed_q=False):
+                 packed_q=False, total_kv_tokens=0):
     """Paged decode (split-KV + LSE merge). Returns out, or (out, lse).
 
     q [B, q_len, Hq, Dqk] bf16; caches [pages, page_size, Hkv, D] (or a 3-D
     latent cache, pass v_cache=None and head_dim_v=512); block_table
     [B, max_pages] int32; seq_lens [B] int32. window_left >= 0 limits each
     row to the q_len block plus window_left keys of context (-1: full
-    history); packed_q packs rows as token * G + head.
+    history); packed_q packs rows as token * G + head. total_kv_tokens (the
+    host's sum of seq_lens, 0 if unknown) lets the planner size the splits
+    so every unit is resident at once.
     """
     _need(q.is_cuda and q.dtype == _BF16 and q.is_contiguous(), "q must be a contiguous bf16 CUDA tensor")
     _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
@@ -111,7 +114,8 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, max_seq_len=max_seq_len,
                       softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
                       k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=workspace,
-                      out=out, lse=lse, window_left=window_left, packed_q=packed_q)
+                      out=out, lse=lse, window_left=window_left, packed_q=packed_q,
+                      total_kv_tokens=total_kv_tokens)
     lib = _ffi.load()
     if workspace is None:
         need = lib.attn_decode_workspace_size(ctypes.byref(p))

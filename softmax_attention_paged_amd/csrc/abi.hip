@@ -75,6 +75,7 @@ attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) 
   if (p->batch < 0) return fail(ATTN_ERR_INVALID_ARG, "batch %d < 0", p->batch);
   if (p->q_len < 1 || p->q_len > 4)
     return fail(ATTN_ERR_UNSUPPORTED, "q_len %d outside 1..4", p->q_len);
+  if (p->total_kv_tokens < 0) return fail(ATTN_ERR_INVALID_ARG, "total_kv_tokens < 0");
   if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->num_q_heads % p->num_kv_heads)
     return fail(ATTN_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
                 p->num_q_heads, p->num_kv_heads);
@@ -182,25 +183,53 @@ DecodePlan plan_decode(const attn_decode_params *p) {
       }
     }
   } else {
-    // HBM-bound: many small units so ragged lengths balance across 256 CUs,
-    // but no split shorter than 256 keys. 44 units per CU: from interleaved
-    // median timings of three 64-request decodes (lengths uniform on
-    // 256..8192, Hkv 8, D 128), 22 splits of 384 keys ran 5-6 % faster than
-    // 16 of 512 (and than 18-20), while 23 of 352 ran 6-9 % slower.
-    const int64_t want = cdiv(44 * attn::kNumCUs, base_units > 0 ? base_units : 1);
-    const int64_t by_len = cdiv(window_span(p), 256);
-    splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
+    // HBM-bound, one single-wave unit per (request, KV head, q-group, split).
+    splits = 0;
+    if (p->total_kv_tokens > 0) {
+      // With the host's total of the keys: the split length L for which every
+      // unit is resident at once. A request walking n keys has at most
+      // n / L + 1 units per (KV head, q-group), so with
+      // (total / L + batch) * Hkv * q_groups <= the waves the CUs hold, the
+      // launch is one round. Measured on three 64-request decodes (lengths
+      // uniform on 256..8192, Hkv 8, D 128): 0.194-0.204 ms against
+      // 0.203-0.213 ms for the fixed rule below; one more split than fits
+      // (a few units in a second round) costs 20-30 %.
+      const bool ext = p->window_enabled || p->packed_q;
+      const int64_t slots = (int64_t)attn::kNumCUs * attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext);
+      const int64_t room = slots / ((int64_t)p->num_kv_heads * pl.q_groups) - p->batch;
+      const int span = window_span(p);
+      if (room > 0 && span > 0) {
+        const int64_t total = std::min<int64_t>(p->total_kv_tokens, (int64_t)p->batch * span);
+        int64_t st = std::max<int64_t>(256, cdiv(cdiv(total, room), tile) * tile);
+        st = std::max<int64_t>(st, cdiv(cdiv(span, attn::kMaxSplits), tile) * tile);
+        pl.splits = (int)std::max<int64_t>(1, cdiv(span, st));
+        pl.split_tokens = (int)std::min<int64_t>(st, cdiv(span, tile) * tile);
+        splits = -1;   // split length fixed above
+      }
+    }
+    if (splits == 0) {
+      // Otherwise many small units so ragged lengths balance across 256 CUs,
+      // but no split shorter than 256 keys. 44 units per CU: from interleaved
+      // median timings of three 64-request decodes (lengths uniform on
+      // 256..8192, Hkv 8, D 128), 22 splits of 384 keys ran 5-6 % faster than
+      // 16 of 512 (and than 18-20), while 23 of 352 ran 6-9 % slower.
+      const int64_t want = cdiv(44 * attn::kNumCUs, base_units > 0 ? base_units : 1);
+      const int64_t by_len = cdiv(window_span(p), 256);
+      splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
+    }
   }
   // Split length: a whole number of tiles; then keep only non-empty splits of
   // the longest request. With a window, splits cover each request's window
   // (from its tile-aligned start), so the walk and the split count track the
   // window rather than the cache.
   const int span = window_span(p);
-  int64_t split_tokens = cdiv(std::max(span, 1), splits);
-  split_tokens = cdiv(split_tokens, tile) * tile;
-  splits = (int)std::max<int64_t>(1, cdiv(span, split_tokens));
-  pl.splits = splits;
-  pl.split_tokens = (int)split_tokens;
+  if (splits > 0) {
+    int64_t split_tokens = cdiv(std::max(span, 1), splits);
+    split_tokens = cdiv(split_tokens, tile) * tile;
+    pl.splits = (int)std::max<int64_t>(1, cdiv(span, split_tokens));
+    pl.split_tokens = (int)split_tokens;
+  }
+  splits = pl.splits;
   pl.units = base_units * splits;
   const int64_t rows_total = (int64_t)p->batch * p->q_len * p->num_q_heads;
   pl.workspace = splits > 1 ? (size_t)splits * rows_total * (p->head_dim_v + 1) * sizeof(float) : 0;

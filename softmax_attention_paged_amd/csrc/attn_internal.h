@@ -127,6 +127,9 @@ struct MlaPackArgs {
 };
 
 // Launchers; each returns hipSuccess or the launch error.
+// Waves of the GQA decode kernel one CU holds at once (its occupancy by
+// registers), for the planner.
+int decode_gqa_waves_per_cu(int head_dim, bool ext);
 hipError_t launch_decode_gqa(const DecodeGqaArgs &a, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeMlaArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);

@@ -411,6 +411,14 @@ hipError_t launch_d(const DecodeGqaArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+int decode_gqa_waves_per_cu(int head_dim, bool ext) {
+  switch (head_dim) {
+    case 64: return 4 * (ext ? GqaGeom<64>::kWPEExt : GqaGeom<64>::kWPE);
+    case 128: return 4 * (ext ? GqaGeom<128>::kWPEExt : GqaGeom<128>::kWPE);
+    default: return 4 * (ext ? GqaGeom<256>::kWPEExt : GqaGeom<256>::kWPE);
+  }
+}
+
 hipError_t launch_decode_gqa(const DecodeGqaArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
     case 64: return launch_d<64>(a, stream);

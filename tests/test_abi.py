@@ -249,6 +249,31 @@ def test_latent_planner_fills_whole_rounds(batch, splits):
     assert st == 0 and info.num_splits == splits
 
 
+@pytest.mark.parametrize("batch,max_len,total,hkv,d", [
+    (64, 8192, 256194, 8, 128), (64, 8192, 64 * 8192, 8, 128), (8, 65536, 300000, 8, 128),
+    (17, 513, 2000, 2, 64), (200, 4096, 400000, 8, 256), (64, 8192, 1000, 8, 128)])
+def test_gqa_planner_with_total_keys_fits_one_round(batch, max_len, total, hkv, d):
+    # a request walking n keys has at most n / L + 1 units per KV head, so the
+    # plan must keep (total / L + batch) * Hkv within the resident waves
+    # (12 per CU at D 128, 16 at D 64, 8 at D 256), unless even one split per
+    # request does not fit
+    p = decode_params(num_q_heads=hkv * 4, num_kv_heads=hkv, head_dim_qk=d, head_dim_v=d, q_len=1, batch=batch,
+                      max_seq_len=max_len, page_size=128, num_pages=(max_len // 128 + 1) * batch,
+                      block_table_stride=max_len // 128 + 1, k_stride_page=128 * hkv * d, k_stride_tok=hkv * d,
+                      k_stride_head=d, v_stride_page=128 * hkv * d, v_stride_tok=hkv * d, v_stride_head=d)
+    p.total_kv_tokens = total
+    st, info = plan(p)
+    assert st == 0
+    L = info.split_tokens
+    assert L % 32 == 0 and info.num_splits * L >= max_len and (info.num_splits - 1) * L < max_len
+    slots = 256 * {64: 16, 128: 12, 256: 8}[d]
+    if slots // hkv > batch:
+        assert min(total / L + batch, batch * info.num_splits) * hkv <= slots
+        assert L >= 256 or info.num_splits == 1
+    p.total_kv_tokens = -1
+    assert plan(p)[0] == _ffi.ATTN_ERR_INVALID_ARG
+
+
 def test_gqa_plan_folds_heads_and_tokens_into_16_rows():
     for q_len, hq, hkv, expect_f in [(1, 40, 8, 1), (4, 8, 2, 4), (4, 20, 4, 2), (3, 8, 8, 3), (4, 16, 1, 1)]:
         st, info = plan(decode_params(q_len=q_len, num_q_heads=hq, num_kv_heads=hkv, block_table_stride=8))

@@ -17,14 +17,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(case, num_splits=0, return_lse=True):
+def _run(case, num_splits=0, return_lse=True, total_kv_tokens=0):
     c = case.to(DEV)
     out, lse = sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
                                 max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal,
                                 head_dim_v=c.head_dim_v,
                                 kv_dtype=c.kv_dtype if c.kv_dtype != "bf16" else None,
                                 k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits,
-                                return_lse=return_lse, window_left=c.window_left, packed_q=c.packed_q)
+                                return_lse=return_lse, window_left=c.window_left, packed_q=c.packed_q,
+                                total_kv_tokens=total_kv_tokens)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
@@ -57,6 +58,10 @@ def test_boundary_lengths(d, page_size):
     print("boundary", d, page_size, flush=True)
     for splits in (0, 1, 3):
         _check(case, num_splits=splits)
+    # planned from the host's total of the keys (one round of resident units)
+    out, lse = _run(case, total_kv_tokens=sum(lens))
+    ref, lref = oracle_decode(case)
+    print(compare(f64(out), ref, lse.numpy(), lref))
 
 
 @pytest.mark.parametrize("q_len,hq,hkv", [(2, 8, 2), (3, 8, 8), (4, 8, 2), (4, 20, 4), (4, 16, 1)])
@@ -151,12 +156,15 @@ def test_peaky_scores_force_rescale():
         _check(case, num_splits=splits)
 
 
-def test_qwen3_14b_decode_sampled_rows_full_size():
+@pytest.mark.parametrize("hint", [False, True])
+def test_qwen3_14b_decode_sampled_rows_full_size(hint):
     """The Qwen3-14B-shaped workload at full size, planned as the benchmark
-    plans it, checked on 256 sampled (request, head) rows."""
+    plans it (with the host's total of the keys) and without that hint,
+    checked on 256 sampled (request, head) rows."""
     case = inputs.qwen3_14b_decode()
-    print("case", case.name, "tokens", int(case.seq_lens.sum()), flush=True)
-    out, lse = _run(case)
+    tokens = int(case.seq_lens.sum())
+    print("case", case.name, "tokens", tokens, "hint", hint, flush=True)
+    out, lse = _run(case, total_kv_tokens=tokens if hint else 0)
     rng = np.random.default_rng(0)
     rows = [(int(rng.integers(64)), 0, int(rng.integers(40))) for _ in range(256)]
     ref, lref = oracle_decode(case, rows)
