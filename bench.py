@@ -513,7 +513,7 @@ def main() -> int:
     sources = ["decode_gqa.hip", "device_common.h", "attn_internal.h"]
     traffic = load_traffic("decode_gqa_qwen3_14b", sources, plan)
     line = {
-        "metric": "decode KV-read GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)",
+        "metric": "prefill attn TFLOP/s (% MFMA peak); decode KV-read GB/s (% HBM peak)",
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
