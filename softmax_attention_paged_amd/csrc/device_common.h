@@ -110,23 +110,19 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
-// Exact e4m3 -> bf16 of 16 codes (the hardware FP8 convert reads the OCP format on gfx950).
+// Exact e4m3 -> bf16 of 16 codes: one hardware convert per pair of codes, at
+// scale 1 (every E4M3 value is a bf16 value; the OCP format on gfx950).
 __device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, bf16x8 &lo, bf16x8 &hi) {
-  float f[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int word = (int)w[q];
-    const auto p01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);   // bytes 0, 1
-    const auto p23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);    // bytes 2, 3
-    f[4 * q + 0] = p01[0];
-    f[4 * q + 1] = p01[1];
-    f[4 * q + 2] = p23[0];
-    f[4 * q + 3] = p23[1];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lo[e] = to_bf16(f[e]);
-    hi[e] = to_bf16(f[8 + e]);
+    const auto p01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, false);   // codes 0, 1
+    const auto p23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, true);    // codes 2, 3
+    bf16x8 &d = (q < 2) ? lo : hi;
+    const int o = 4 * (q & 1);
+    d[o + 0] = p01[0];
+    d[o + 1] = p01[1];
+    d[o + 2] = p23[0];
+    d[o + 3] = p23[1];
   }
 }
 
@@ -135,13 +131,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
   bf16x8 r;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int word = (int)w[q];
-    const auto p01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-    const auto p23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-    r[4 * q + 0] = to_bf16(p01[0]);
-    r[4 * q + 1] = to_bf16(p01[1]);
-    r[4 * q + 2] = to_bf16(p23[0]);
-    r[4 * q + 3] = to_bf16(p23[1]);
+    const auto p01 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, false);
+    const auto p23 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], 1.0f, true);
+    r[4 * q + 0] = p01[0];
+    r[4 * q + 1] = p01[1];
+    r[4 * q + 2] = p23[0];
+    r[4 * q + 3] = p23[1];
   }
   return r;
 }
