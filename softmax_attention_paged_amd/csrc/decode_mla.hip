@@ -161,6 +161,28 @@ __device__ __forceinline__ void mla_issue(const MlaCtx &x, const MlaLoadMap &map
   }
 }
 
+// Pull the cache lines of the whole tile at key j0 (inside one page) into
+// L2 ahead of its loads: one dword per 128-byte line of each row, loaded
+// straight into a scratch LDS word of the lane (`sink`: the wave's 256 bytes,
+// never read), so no register waits for it. The tile's own loads, issued an
+// iteration later, then hit in L2 instead of waiting out an HBM round trip
+// with only one tile in flight per CU.
+template <bool FP8>
+__device__ __forceinline__ void mla_prefetch(const MlaCtx &x, int j0, int tid, uint32_t sink) {
+  constexpr int kLines = (kDk * (FP8 ? 1 : 2) + 127) / 128;   // 128-byte lines a row spans
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const int64_t page = reinterpret_cast<const_i32 *>(reinterpret_cast<uintptr_t>(x.bt_row))[j0 >> x.page_shift];
+  const char *tile = x.kv + page * x.page_b + (int64_t)(j0 & x.pmask) * x.tok_b;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < kTileN * kLines) {
+      const uint32_t off = static_cast<uint32_t>((i / kLines) * x.tok_b + (i % kLines) * 128);
+      asm volatile("global_load_lds_dword %0, %1" : : "v"(off), "s"(tile), "{m0}"(sink) : "memory");
+    }
+  }
+}
+
 // fp8: widen the staged codes and store them as bf16 rows.
 __device__ __forceinline__ void mla_store_fp8(char *dst, int tid, const u32x4 (&stage)[kF8PerThread]) {
 #pragma unroll
@@ -336,6 +358,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
   f32x16 oacc[kNB];
   const int ntiles = (c1 - first + kTileN - 1) / kTileN;
   u32x4 stage[kF8PerThread];
+  __shared__ __attribute__((aligned(16))) char sink_lds[kW * 256];   // prefetch destinations, never read
+  const uint32_t sink = lds_address(sink_lds + wave * 256);
   const float sum_limit = exp2f(kAnchorLog2);
 
   for (int attempt = 0;; ++attempt) {
@@ -343,16 +367,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
     for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x16{};
     lsum = 0.f;
     mla_issue<FP8>(x, map, first, c1, wave, lane, tid, tiles, stage);
+    if (x.wide && first + 2 * kTileN <= c1) mla_prefetch<FP8>(x, first + kTileN, tid, sink);
     if constexpr (FP8) mla_store_fp8(tiles, tid, stage);
     for (int it = 0; it < ntiles; ++it) {
       const int j0 = first + it * kTileN;
       const int p = it & 1;
       // tile it has landed for every wave; every wave is done with tile it-1,
-      // whose buffer takes tile it+1
+      // whose buffer takes tile it+1 (whose lines the previous iteration
+      // pulled into L2); the lines of tile it+2 are prefetched next
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (restart) break;                     // uniform: read after the barrier
       if (it + 1 < ntiles) mla_issue<FP8>(x, map, j0 + kTileN, c1, wave, lane, tid, tiles + (p ^ 1) * kTileB, stage);
+      if (x.wide && j0 + 3 * kTileN <= c1) mla_prefetch<FP8>(x, j0 + 2 * kTileN, tid, sink);
 
       if (wave_active) {
         const char *tile = tiles + p * kTileB;
