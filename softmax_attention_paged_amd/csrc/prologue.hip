@@ -25,6 +25,7 @@ namespace {
 constexpr int kPrologueThreads = 256;
 constexpr int kBatch = 4;              // 16-byte chunks each lane loads before it stores
 constexpr float kE4m3Max = 448.0f;
+constexpr int kMaxRopeChunks = 4096 / 8;   // d_nope + d_rope <= 4096
 
 // x / scale rounded once to binary32, from inv = RN(1 / scale): q0 = x * inv
 // is within one ulp of the quotient, and one fma correction with the exact
@@ -107,8 +108,8 @@ __global__ __launch_bounds__(kPrologueThreads) void cache_append_kernel(const Ca
 }
 
 // Quantise one region of a token's rows: `heads` rows of `chunks` 16-byte
-// chunks, row h read at src + h * src_stride (a stride of 0 re-reads one
-// shared row) and written at dst + h * dst_stride (element strides, both
+// chunks, row h read at src + h * src_stride and written at dst + h *
+// dst_stride (element strides, both
 // below 2^24 so 24-bit multiplies address them). kBatch chunks per lane per
 // round: all loads first, then the stores, so each lane keeps kBatch 16-byte
 // reads in flight; a lane's (row, chunk) position advances by a fixed step.
@@ -138,20 +139,59 @@ __device__ __forceinline__ void pack_region(const __bf16 *src, int src_stride, u
   }
 }
 
-// One workgroup per token: the k_nope rows of every head into the first
-// d_nope bytes of each K row, the token's single rope row into the last
-// d_rope bytes of every K row (the same few cache lines re-read per head),
-// and the V rows.
+// Quantise a token's K rows whole: row h has `chunks` 8-byte output chunks,
+// the first `src_chunks` from the 16-byte chunks of src + h * src_stride,
+// the rest copied from `rope_codes` (the shared rope row, quantised once).
+// Each wave's stores cover consecutive chunks of consecutive rows, so a row
+// is written in one pass rather than as a head and a tail at different times.
+__device__ __forceinline__ void pack_k_rows(const __bf16 *src, int src_stride, uint8_t *dst, int dst_stride,
+                                            int heads, int chunks, int src_chunks, const u32x2 *rope_codes,
+                                            float scale, float inv) {
+  const int total = heads * chunks;
+  const int step_h = kPrologueThreads / chunks, step_c = kPrologueThreads % chunks;
+  int h = threadIdx.x / chunks, c = threadIdx.x % chunks;
+  for (int base = 0; base < total; base += kBatch * kPrologueThreads) {
+    bf16x8 x[kBatch];
+    uint32_t off[kBatch];
+    int rc[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool live = base + u * kPrologueThreads + static_cast<int>(threadIdx.x) < total;
+      off[u] = live ? __umul24(h, dst_stride) + c * 8 : ~0u;
+      rc[u] = c - src_chunks;
+      if (live && rc[u] < 0) x[u] = load_bf16x8(src + __umul24(h, src_stride) + c * 8);
+      h += step_h;
+      c += step_c;
+      if (c >= chunks) {
+        c -= chunks;
+        ++h;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (off[u] != ~0u)
+        *reinterpret_cast<u32x2 *>(dst + off[u]) = rc[u] < 0 ? quantize8(x[u], scale, inv) : rope_codes[rc[u]];
+  }
+}
+
+// One workgroup per token: the token's rope row is quantised once into LDS
+// (its codes are the same for every head), then every K row is written
+// whole (d_nope bytes from k_nope, d_rope bytes of rope codes), then the V
+// rows.
 __global__ __launch_bounds__(kPrologueThreads) void mla_kv_pack_kernel(const MlaPackArgs a) {
+  __shared__ u32x2 rope_codes[kMaxRopeChunks];
   const int64_t tok = blockIdx.x;
   const float k_inv = 1.0f / a.k_scale, v_inv = 1.0f / a.v_scale;   // IEEE quotients
-  uint8_t *kout = static_cast<uint8_t *>(a.k_out) + tok * a.k_out_stride_tok;
-  const int kos = static_cast<int>(a.k_out_stride_head);
-  pack_region(static_cast<const __bf16 *>(a.k_nope) + tok * a.k_nope_stride_tok,
-              static_cast<int>(a.k_nope_stride_head), kout, kos, a.num_heads, a.d_nope / 8, a.k_scale, k_inv);
-  if (a.d_rope > 0)
-    pack_region(static_cast<const __bf16 *>(a.k_rope) + tok * a.k_rope_stride_tok, 0, kout + a.d_nope, kos,
-                a.num_heads, a.d_rope / 8, a.k_scale, k_inv);
+  const int nch = a.d_nope / 8, rch = a.d_rope / 8;
+  if (rch > 0) {
+    const __bf16 *rope = static_cast<const __bf16 *>(a.k_rope) + tok * a.k_rope_stride_tok;
+    for (int i = threadIdx.x; i < rch; i += kPrologueThreads)
+      rope_codes[i] = quantize8(load_bf16x8(rope + i * 8), a.k_scale, k_inv);
+  }
+  __syncthreads();
+  pack_k_rows(static_cast<const __bf16 *>(a.k_nope) + tok * a.k_nope_stride_tok, static_cast<int>(a.k_nope_stride_head),
+              static_cast<uint8_t *>(a.k_out) + tok * a.k_out_stride_tok, static_cast<int>(a.k_out_stride_head),
+              a.num_heads, nch + rch, nch, rope_codes, a.k_scale, k_inv);
   pack_region(static_cast<const __bf16 *>(a.v) + tok * a.v_stride_tok, static_cast<int>(a.v_stride_head),
               static_cast<uint8_t *>(a.v_out) + tok * a.v_out_stride_tok, static_cast<int>(a.v_out_stride_head),
               a.num_heads, a.d_v / 8, a.v_scale, v_inv);

@@ -135,6 +135,16 @@ def test_pack_deepseek_shaped(strided):
     _check_pack(case)
 
 
+# head widths other than the MLA shape: K and V regions of different sizes
+# (the shorter one runs out first in the shared loop), a rope row whose chunk
+# count does not divide the workgroup (quantised per head), and no rope
+@pytest.mark.parametrize("d_nope,d_rope,d_v,heads", [(64, 24, 96, 5), (128, 64, 512, 3), (256, 0, 64, 2),
+                                                     (8, 8, 8, 33), (512, 40, 128, 1)])
+def test_pack_other_widths(d_nope, d_rope, d_v, heads):
+    case = inputs.pack_case(num_tokens=19, heads=heads, d_nope=d_nope, d_rope=d_rope, d_v=d_v, seed=83 + d_rope)
+    _check_pack(case)
+
+
 def test_pack_into_preallocated_strided_outputs_leaves_the_rest_alone():
     case = inputs.pack_case(num_tokens=40, heads=8, seed=82)
     kbuf = torch.full((40, 8, 256), 0x5A, dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)
