@@ -37,11 +37,18 @@ __host__ __device__ __forceinline__ int pf_heads_per_wg(int group) {
 
 // The rows workgroup blockIdx.x owns when it holds `blocks` 32-row blocks:
 // gh heads of one KV group times tq = 32 blocks / gh tokens, tiles counted
-// from the end of the request (index slow, so the longest rows of every
-// request start first), and with key splits the split it walks (slowest:
-// the workgroups running together walk the same key range of as many query
-// tiles as without splits, so each K/V tile they stream is shared as widely
-// in L2). False when the request has no tile of that index.
+// from the end of the request, and with key splits the split it walks. The
+// head group is the fastest index, so with a head-group count that is a
+// multiple of 8 every workgroup of one KV head lands on the same XCD (blocks
+// go to the XCDs in turn) and shares its L2. Without splits the query tile
+// comes next (the longest rows of every request start first). With splits
+// the split is slowest (the workgroups running together walk the same key
+// range of as many query tiles as without splits) and the request is slower
+// than the query tile: workgroups that stream the same keys are launched
+// back to back, and slots that free together take the tiles of one request
+// and split, so the workgroups sharing a K/V tile in L2 start together round
+// after round rather than drifting apart. False when the request has no
+// tile of that index.
 __device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit &u) {
   const int group = a.num_q_heads / a.num_kv_heads;
   u.gh = pf_heads_per_wg(group);
@@ -52,9 +59,14 @@ __device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit
   const int per_split = q_tiles * a.batch * head_groups;
   u.split = L / per_split;
   L %= per_split;
-  const int qt = L / (a.batch * head_groups);
-  L %= a.batch * head_groups;
-  u.b = L / head_groups;
+  int qt;
+  if (a.kv_splits > 1) {
+    qt = (L / head_groups) % q_tiles;
+    u.b = L / (head_groups * q_tiles);
+  } else {
+    qt = L / (a.batch * head_groups);
+    u.b = (L / head_groups) % a.batch;
+  }
   u.h0 = (L % head_groups) * u.gh;
   u.kvh = u.h0 / group;
   const int q_lo = a.cu_seqlens_q[u.b];
