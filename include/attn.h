@@ -94,8 +94,15 @@ typedef enum {
  *          workspace of attn_prefill_workspace_size(p) bytes (16-byte
  *          aligned) and total_q set, the keys of each query tile may be
  *          walked by several workgroups whose partials are merged by log-sum-
- *          exp; without one (or if it is too small, or o is not contiguous)
- *          the call runs unsplit. Results equal the unsplit ones up to
+ *          exp. With kv_splits = 0 (the planner chooses) a missing or too
+ *          small workspace, or an o that is not contiguous, runs the call
+ *          unsplit. A forced kv_splits > 1 is an error instead: FP8 inputs
+ *          or a non-contiguous o give ATTN_ERR_UNSUPPORTED, total_q <= 0
+ *          ATTN_ERR_INVALID_ARG, a missing or too small workspace
+ *          ATTN_ERR_WORKSPACE_TOO_SMALL and a misaligned one
+ *          ATTN_ERR_INVALID_ARG (the split count is capped at one split per
+ *          64 keys of max_seqlen_kv, so a forced count may shrink to one, which
+ *          needs no workspace). Results equal the unsplit ones up to
  *          rounding. total_q must equal cu_seqlens_q[batch]: query rows at
  *          or past a smaller total_q are not written (nor is the workspace
  *          beyond its size); with a larger one, the rows of o (and lse)
@@ -145,7 +152,8 @@ typedef struct {
  * when the plan splits the keys of each query tile into S > 1 ranges (bf16,
  * contiguous o [total_q, Hq, Dv], total_q > 0), else 0. With kv_splits = 0
  * the planner splits when the workgroups of the query tiles (counted from
- * total_q) fill at most half of the CUs' slots (toward one full round) or
+ * total_q) fill at most half of the CUs' slots (toward one full round; the
+ * CU count is the current device's, or 256 when no device is visible) or
  * leave a last round at most three quarters full (four splits), with no
  * split under 8192 keys (long keys, few query rows); each split's
  * normalised partial and LSE are then merged by attn_merge_lse's reducer.
@@ -153,7 +161,8 @@ typedef struct {
 size_t attn_prefill_workspace_size(const attn_prefill_params *p);
 
 /* Enqueue ragged prefill. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,
- * ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP. */
+ * ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL (forced key splits
+ * only) or ATTN_ERR_HIP. */
 attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -195,7 +204,8 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  *   total_kv_tokens   optional host-side sum of seq_lens (0: unknown). With
  *              it and num_splits = 0 the GQA planner sizes the splits so
  *              that every unit is resident at once (units <= (total / S_len
- *              + batch) * Hkv * q_groups fit one round of the GPU's waves),
+ *              + batch) * Hkv * q_groups fit one round of the waves the
+ *              current device's CUs hold),
  *              which on ragged batches beats a fixed split length; it only
  *              changes the plan, never the result.
  * Supported: (Dqk, Dv) in {(64,64), (128,128), (256,256)} with bf16 KV and

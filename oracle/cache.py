@@ -58,7 +58,8 @@ def quantize_e4m3fn(x: np.ndarray, scale: float = 1.0) -> np.ndarray:
     """float values -> uint8 E4M3 codes of x / scale (binary32 quotient),
     round-to-nearest-even, saturating at +-448, the sign kept (so -0 and a
     negative value that rounds to zero give 0x80). NaN gives 0x7F."""
-    y = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    with np.errstate(over="ignore"):                        # a binary32 quotient may overflow to inf: it saturates
+        y = np.asarray(x, dtype=np.float32) / np.float32(scale)
     y = y.astype(np.float64)
     mag = np.minimum(np.abs(y), E4M3_MAX)
     hi = np.searchsorted(_GRID, mag, side="left")          # first grid value >= mag

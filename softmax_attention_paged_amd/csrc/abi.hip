@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -41,6 +42,28 @@ int log2i(int64_t x) {
   return s;
 }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, asked of the runtime once per device
+// and cached (an attribute query: no synchronisation, no device memory).
+// Without a visible device (planning on a host with no GPU) the plan is made
+// for the 256 CUs of an MI355X; a failed query's error is cleared so that it
+// cannot surface as a later launch's error.
+int num_cus() {
+  static std::atomic<int> cached[attn::kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= attn::kMaxDevices) {
+    (void)hipGetLastError();
+    return attn::kDefaultCUs;
+  }
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return attn::kDefaultCUs;
+  }
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 bool is_mla_shape(const attn_decode_params *p) {
   return p->head_dim_qk == 576 && p->head_dim_v == 512;
@@ -160,6 +183,7 @@ DecodePlan plan_decode(const attn_decode_params *p) {
   }
   const int64_t base_units = (int64_t)p->batch * p->num_kv_heads * pl.q_groups;
   const int tile = pl.mla ? attn::kMlaTileTokens : attn::kGqaTileTokens;
+  const int cus = num_cus();
   int splits;
   if (p->num_splits > 0) {
     splits = p->num_splits;
@@ -176,7 +200,7 @@ DecodePlan plan_decode(const attn_decode_params *p) {
     double best = 0.0;
     splits = 1;
     for (int64_t s = 1; s <= by_len; ++s) {
-      const double cost = (double)cdiv(u * s, attn::kNumCUs) / (double)s * (1.0 + (double)s / 200.0);
+      const double cost = (double)cdiv(u * s, cus) / (double)s * (1.0 + (double)s / 200.0);
       if (s == 1 || cost < best * 0.999) {
         best = cost;
         splits = (int)s;
@@ -195,7 +219,7 @@ DecodePlan plan_decode(const attn_decode_params *p) {
       // 0.203-0.213 ms for the fixed rule below; one more split than fits
       // (a few units in a second round) costs 20-30 %.
       const bool ext = p->window_enabled || p->packed_q;
-      const int64_t slots = (int64_t)attn::kNumCUs * attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext);
+      const int64_t slots = (int64_t)cus * attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext);
       const int64_t room = slots / ((int64_t)p->num_kv_heads * pl.q_groups) - p->batch;
       const int span = window_span(p);
       if (room > 0 && span > 0) {
@@ -213,7 +237,7 @@ DecodePlan plan_decode(const attn_decode_params *p) {
       // median timings of three 64-request decodes (lengths uniform on
       // 256..8192, Hkv 8, D 128), 22 splits of 384 keys ran 5-6 % faster than
       // 16 of 512 (and than 18-20), while 23 of 352 ran 6-9 % slower.
-      const int64_t want = cdiv(44 * attn::kNumCUs, base_units > 0 ? base_units : 1);
+      const int64_t want = cdiv(44 * cus, base_units > 0 ? base_units : 1);
       const int64_t by_len = cdiv(window_span(p), 256);
       splits = (int)std::max<int64_t>(1, std::min<int64_t>({want, by_len, attn::kMaxSplits}));
     }
@@ -323,10 +347,13 @@ struct PrefillPlan {
   size_t workspace;
 };
 
+bool prefill_o_contiguous(const attn_prefill_params *p) {
+  return p->o_stride_head == p->head_dim_v && p->o_stride_tok == (int64_t)p->num_q_heads * p->head_dim_v;
+}
+
 PrefillPlan plan_prefill(const attn_prefill_params *p) {
   PrefillPlan pl{1, 0, 0};
-  const bool contiguous_o = p->o_stride_head == p->head_dim_v && p->o_stride_tok == (int64_t)p->num_q_heads * p->head_dim_v;
-  if (p->qkv_dtype != ATTN_BF16 || p->total_q <= 0 || !contiguous_o || p->max_seqlen_kv <= 0 || p->batch <= 0 ||
+  if (p->qkv_dtype != ATTN_BF16 || p->total_q <= 0 || !prefill_o_contiguous(p) || p->max_seqlen_kv <= 0 || p->batch <= 0 ||
       p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads)
     return pl;
   int splits = p->kv_splits;
@@ -334,7 +361,7 @@ PrefillPlan plan_prefill(const attn_prefill_params *p) {
     const int group = p->num_q_heads / p->num_kv_heads;
     const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
     const int64_t units = std::max<int64_t>(1, cdiv(p->total_q, kPrefillRows / gh)) * (p->num_q_heads / gh);
-    const int64_t slots = (int64_t)attn::kNumCUs * (p->head_dim_qk <= 128 ? 2 : 1);
+    const int64_t slots = (int64_t)num_cus() * (p->head_dim_qk <= 128 ? 2 : 1);
     int64_t sp = 1;
     if (2 * units <= slots) {
       while (2 * sp * units <= slots) sp *= 2;
@@ -533,7 +560,20 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
   a.o_stride_head = p->o_stride_head;
   a.lse = p->lse;
   a.kv_splits = 1;
+  if (p->kv_splits > 1) {
+    // forced key splits: anything that keeps them from running is an error
+    if (a.fp8) return fail(ATTN_ERR_UNSUPPORTED, "key splits are built for bf16 prefill only");
+    if (p->total_q <= 0) return fail(ATTN_ERR_INVALID_ARG, "key splits need total_q (the rows of q)");
+    if (!prefill_o_contiguous(p))
+      return fail(ATTN_ERR_UNSUPPORTED, "key splits need a contiguous o [total_q, Hq, Dv]");
+  }
   const PrefillPlan pl = plan_prefill(p);
+  if (pl.splits > 1 && p->kv_splits > 1) {
+    if (!p->workspace || p->workspace_bytes < pl.workspace)
+      return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "%d key splits need %zu workspace bytes, got %zu", pl.splits,
+                  pl.workspace, p->workspace ? p->workspace_bytes : (size_t)0);
+    if (!aligned16(p->workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
   if (pl.splits > 1 && p->workspace && p->workspace_bytes >= pl.workspace && aligned16(p->workspace)) {
     a.kv_splits = pl.splits;
     a.split_tokens = pl.split_tokens;

@@ -145,7 +145,8 @@ constexpr int kGqaTileTokens = 32;    // keys per wave iteration
 constexpr int kMlaRows = 128;         // folded rows of the MLA decode kernel
 constexpr int kMlaTileTokens = 32;
 constexpr int kMaxSplits = 256;
-constexpr int kNumCUs = 256;          // MI355X compute units
+constexpr int kDefaultCUs = 256;      // MI355X compute units: the plan when no device is visible
+constexpr int kMaxDevices = 64;       // device ordinals whose CU count is cached
 constexpr float kLog2eHost = 1.4426950408889634f;
 
 }  // namespace attn

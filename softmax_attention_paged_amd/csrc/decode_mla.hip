@@ -29,15 +29,20 @@
 //     is the B operand straight from the score registers; V^T is read with
 //     ds_read_b64_tr_b16;
 //   - static-anchor softmax ("Flywheel Attention", section "Static-anchor
-//     softmax" and Appendix A): each row fixes its anchor at the max of its
-//     first tile with a visible key and never moves it, so O is never rescaled (it stays in the
-//     accumulation registers, untouched by vector ALU work); after each tile
-//     the running sum is checked against 2^kAnchorLog2, which bounds every
-//     exponential taken so far. A failed check (a score far above the anchor,
-//     or an overflow) makes the whole workgroup start its split again with
-//     the failing rows' anchors raised to that tile's max; the pages replay
-//     one block from saved state instead, which would need a second copy of
-//     O. One FP32 sum of the exponentials normalises O and gives the LSE.
+//     softmax" and Appendix A): each row fixes its anchor at the max of the
+//     scores it may see in the first walked tile that holds one, with every
+//     mask applied first (so the anchor is one of the row's own scores and
+//     its sum is at least 1), and never moves it, so O is never rescaled (it
+//     stays in the accumulation registers, untouched by vector ALU work);
+//     after each tile the running sum is checked against 2^kAnchorLog2, which
+//     bounds every exponential taken so far. A failed check (a score far
+//     above the anchor, or an overflow) makes the whole workgroup walk its
+//     split again with the failing rows' anchors raised to that tile's max;
+//     after a second failure, one walk raises every anchor to its row's max
+//     over the split and the last walk, in which no exponential exceeds 1,
+//     runs unchecked. The pages replay one block from saved state instead,
+//     which would need a second copy of O. One FP32 sum of the exponentials
+//     normalises O and gives the LSE.
 // Workgroups are renumbered so that consecutive units run on the same XCD:
 // the query groups of one split then share that XCD's L2 for the latent.
 
@@ -69,7 +74,6 @@ constexpr int kXcds = 8;
 // under 2^20 keys), and O at most |V|max 2^60 (finite for fp8 codes, |c| <=
 // 448, and for bf16 latents below 2^67).
 constexpr float kAnchorLog2 = 40.0f;
-constexpr int kMaxRestarts = 8;                    // each restart raises an anchor by > 20 log2 units
 static_assert(kTileN * kChunks % (64 * kW) == 0, "whole direct loads per tile");
 static_assert(kW * 32 == kMlaRows, "rows per workgroup");
 
@@ -362,6 +366,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
   const uint32_t sink = lds_address(sink_lds + wave * 256);
   const float sum_limit = exp2f(kAnchorLog2);
 
+  // Walks: 0 checked; 1 checked, with the anchors 0 raised; on a second
+  // failure 2 rises (each anchor becomes its row's max over the split, the
+  // walk's O is dropped) and 3 runs unchecked, since no exponential exceeds 1
+  // (a split's sum is at most its 2^20 keys).
+  bool rising = false;
   for (int attempt = 0;; ++attempt) {
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) oacc[nb] = f32x16{};
@@ -417,22 +426,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
             s[i] = (j < row_end) ? s[i] : kNegInf;
           }
         }
-        if (it == 0 && attempt == 0) {        // the anchor: the max of the row's first tile
-          // A window may hide this whole tile from a row whose keys start in
-          // the next one; its scores are still real dot products of the row's
-          // query, so they bound the row's scale just as well and the anchor
-          // is taken before the window's mask.
-          float mx = kNegInf;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-          anchor = half_max(mx) * c;
-        }
         if (kExt && j0 < begin_max) {         // the window's lower bound (scalar test)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
             s[i] = (j >= row_begin) ? s[i] : kNegInf;
           }
+        }
+        // The anchor: the max of the scores the row may see, in the first
+        // tile of the walk that holds one. The masks above come first, so a
+        // key hidden by the window or the causal bound never sets it. In the
+        // first walk a row's first visible key lies in its first two tiles
+        // (the walk starts at the tile of the unit's first row's first key,
+        // and the rows of a unit start at most q_len - 1 <= 3 keys apart); a
+        // restarted walk also sets the anchors its abandoned predecessor did
+        // not reach. A rising walk takes every tile's max (its O is dropped).
+        {
+          float mx = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          const float mt = half_max(mx) * c;
+          if (it == 0 && attempt == 0) anchor = mt;
+          if (it == 1 || attempt > 0) anchor = (anchor == kNegInf) ? mt : anchor;
+          anchor = rising ? fmaxf(anchor, mt) : anchor;
         }
         const float a_use = (anchor == kNegInf) ? 0.f : anchor;
         bf16x8 pop[2];
@@ -444,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
           if (i & 1) ps1 += pe; else ps0 += pe;
         }
         lsum += half_sum(ps0 + ps1);
-        if (__ballot(!(lsum <= sum_limit) && lsum == lsum)) {
+        if (attempt < 2 && __ballot(!(lsum <= sum_limit) && lsum == lsum)) {
           // some row's sum left the budget (NaN sums, from NaN inputs, pass
           // through): raise those rows' anchors to this tile's max and start over
           float mx = kNegInf;
@@ -481,8 +497,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
     __syncthreads();
     const int again = restart;
     __syncthreads();                          // every wave has read the flag before it is cleared
-    if (!again || attempt == kMaxRestarts) break;
+    if (attempt == 2) {                       // the rising walk: every anchor is now its row's max
+      rising = false;
+      continue;
+    }
+    if (!again || attempt == 3) break;
     if (tid == 0) restart = 0;
+    rising = attempt == 1;                    // second failure
   }
 
   // ---- epilogue: each wave writes its own rows ----

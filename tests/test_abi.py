@@ -208,6 +208,37 @@ def test_prefill_validation_errors(kw, code):
     assert lib.attn_prefill(ctypes.byref(p), None) == code, lib.attn_last_error()
 
 
+def test_forced_prefill_splits_without_workspace_are_errors():
+    """A forced kv_splits > 1 never runs unsplit in silence: a missing or too
+    small workspace is ATTN_ERR_WORKSPACE_TOO_SMALL, a misaligned one
+    ATTN_ERR_INVALID_ARG, FP8 inputs or a non-contiguous o
+    ATTN_ERR_UNSUPPORTED, and total_q <= 0 ATTN_ERR_INVALID_ARG. All are
+    reported before anything is enqueued (the pointers are fake)."""
+    lib = _lib()
+    base = dict(max_seqlen_q=512, max_seqlen_kv=81920, total_q=512, kv_splits=4)
+    p = prefill_params(**base)
+    need = lib.attn_prefill_workspace_size(ctypes.byref(p))
+    assert need == 4 * 512 * 32 * 129 * 4
+    for ws, nbytes, code in ((None, 0, _ffi.ATTN_ERR_WORKSPACE_TOO_SMALL),
+                             (FAKE, need - 16, _ffi.ATTN_ERR_WORKSPACE_TOO_SMALL),
+                             (FAKE + 8, need, _ffi.ATTN_ERR_INVALID_ARG)):
+        p = prefill_params(workspace=ws, workspace_bytes=nbytes, **base)
+        assert lib.attn_prefill(ctypes.byref(p), None) == code, lib.attn_last_error()
+        assert lib.attn_last_error()
+    p = prefill_params(**dict(base, total_q=0), workspace=FAKE, workspace_bytes=need)
+    assert lib.attn_prefill(ctypes.byref(p), None) == _ffi.ATTN_ERR_INVALID_ARG
+    p = prefill_params(**base, workspace=FAKE, workspace_bytes=need, o_stride_tok=64 * 128)
+    assert lib.attn_prefill(ctypes.byref(p), None) == _ffi.ATTN_ERR_UNSUPPORTED
+    p = prefill_params(**base, workspace=FAKE, workspace_bytes=need, qkv_dtype=_ffi.ATTN_FP8_E4M3,
+                       head_dim_qk=192, head_dim_v=128, q_scale=1.0, k_scale=1.0, v_scale=1.0,
+                       q_stride_tok=32 * 192, q_stride_head=192, k_stride_tok=32 * 192, k_stride_head=192)
+    assert lib.attn_prefill(ctypes.byref(p), None) == _ffi.ATTN_ERR_UNSUPPORTED
+    # the planner's own choice (kv_splits = 0) still runs unsplit without a workspace:
+    # validation passes, and the (fake) launch is the first thing that could fail
+    p = prefill_params(**dict(base, kv_splits=0))
+    assert lib.attn_prefill_workspace_size(ctypes.byref(p)) > 0
+
+
 # ------------------------------------------------------------- planner --
 
 def test_fold_matches_tokenspeed_example_for_latent_decode():
@@ -322,8 +353,9 @@ def _latent(**kw):
 
 
 def test_packed_q_tiles_match_tokenspeed_h96_example():
-    # "H96/Sq4 uses three query tiles instead of four": folded rows need one
-    # 96-row group per token, packed rows fill 128-row tiles across tokens
+    # "TokenSpeed-MLA", packed-query paragraph: at 96 heads and 4 query
+    # tokens, packed rows fill 3 tiles of 128 across the tokens, while folded
+    # rows need 4 (one 96-row group per token)
     st, folded = plan(_latent(num_q_heads=96, q_len=4))
     assert st == 0 and (folded.fold, folded.q_groups, folded.rows_per_unit) == (1, 4, 96)
     st, packed = plan(_latent(num_q_heads=96, q_len=4, packed_q=1))

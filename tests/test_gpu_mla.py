@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import softmax_attention_paged_amd as sap
 from softmax_attention_paged_amd import inputs
 from helpers import TOL_BF16, TOL_FP8, compare, f64, oracle_decode
@@ -95,3 +96,69 @@ def test_static_anchor_restart(kv_dtype, splits):
         case.k_cache[page, j % 64, 0] = codes
     res = _check(case, splits)
     print(res)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_window_anchor_ignores_hidden_keys(kv_dtype, splits):
+    """A sliding window whose start lies 30 keys into the first walked tile:
+    those 30 keys are hidden from every row, and rows of tokens 2 and 3 see
+    no key of that tile at all. The hidden keys are planted to score at
+    least 150 log2 units above every key a row may see; the static anchor
+    must come from the row's own visible scores ("Flywheel Attention",
+    Appendix A: the anchor is one of the row's scores, so its sum is at
+    least 1), else every visible exponential underflows and the row comes
+    back empty. Queries are made positive where the planted keys are large
+    (rope columns for bf16, every column for fp8, whose planted codes are
+    the largest E4M3 value)."""
+    lens, q_len, window = [700, 444], 4, 346      # 700 - 4 - 346 = 350 = 320 + 30; 444 - 4 - 346 = 94 = 64 + 30
+    case = inputs.decode_case(batch=2, q_len=q_len, hq=64, hkv=1, d=576, dv=512, page_size=64,
+                              seq_lens=lens, seed=83, kv_dtype=kv_dtype, latent=True,
+                              scale=0.07216882, causal=True, layout="random", window_left=window)
+    cols = slice(512, 576) if kv_dtype == "bf16" else slice(0, 576)
+    case.q[..., cols] = case.q[..., cols].abs()
+    for b, lk in enumerate(lens):
+        start = lk - q_len - window                  # first key row 0 sees
+        base = start & ~31                           # first key of the walk
+        assert start - base == 30
+        for j in range(base, start):                 # hidden from every row
+            page = int(case.block_table[b, j // 64])
+            if kv_dtype == "bf16":
+                case.k_cache[page, j % 64, 0, 512:] = 48.0
+            else:
+                case.k_cache[page, j % 64, 0] = 0x7E     # E4M3 448
+    # precondition: every hidden score exceeds every visible one by >= 150 log2 units
+    kc = f64(case.k_cache) if kv_dtype == "bf16" else oracle.widen_e4m3fn(case.k_cache.numpy(), case.kv_scale)
+    qf = f64(case.q)
+    for b, lk in enumerate(lens):
+        start = lk - q_len - window
+        keys = np.stack([kc[int(case.block_table[b, j // 64]), j % 64, 0] for j in range(start & ~31, lk)])
+        s2 = qf[b].reshape(-1, 576) @ keys.T * case.scale / np.log(2.0)
+        hidden = s2[:, : start - (start & ~31)].min()
+        visible = s2[:, start - (start & ~31):].max()
+        assert hidden - visible >= 150.0, (hidden, visible)
+    print("window anchor", kv_dtype, splits, flush=True)
+    print(_check(case, splits))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_static_anchor_second_restart(kv_dtype, splits):
+    """Two planted keys for the row (token 0, head 0), the second scoring far
+    above the first: the first check fails at key 200 (anchor raised to its
+    score), the restarted walk fails again at key 240, and the pass that sets
+    every anchor to its row's max runs before the last walk. Both keys lie
+    in the first split when there are three."""
+    case = inputs.decode_case(batch=2, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
+                              seq_lens=[700, 300], seed=72, kv_dtype=kv_dtype, latent=True,
+                              scale=0.07216882, causal=True, layout="random")
+    q00 = case.q[0, 0, 0].float()
+    for j, mult in ((200, 1.0), (240, 2.0)):
+        page = int(case.block_table[0, j // 64])
+        if kv_dtype == "bf16":
+            case.k_cache[page, j % 64, 0, 512:] = (28.0 * mult * q00[512:]).to(torch.bfloat16)
+        else:
+            codes = (1.5 * mult * q00 / case.kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            case.k_cache[page, j % 64, 0] = codes.view(torch.uint8)
+    print("second restart", kv_dtype, splits, flush=True)
+    print(_check(case, splits))
