@@ -9,6 +9,8 @@ Tolerances (the bar every parity test applies):
 
 from __future__ import annotations
 
+import hashlib
+
 import numpy as np
 import torch
 
@@ -124,3 +126,32 @@ def compare(out: np.ndarray, ref: np.ndarray, lse: np.ndarray | None = None, lse
         # rows without keys are exactly zero
         assert np.all(out[~fin] == 0)
     return res
+
+
+def block_edge_rows(cu_seqlens_q, num_heads: int, block: int = 32) -> list[tuple[int, int]]:
+    """(token, head) rows at the first and the last query token of every
+    block of 32 tokens of each request, counted from the request's end (the
+    prefill's query tiles and the 32-row blocks of its waves are aligned to
+    the end of the request), for every head: the first and last row of every
+    wave, hence of every workgroup, of an unsplit or key-split launch."""
+    cu = [int(x) for x in cu_seqlens_q]
+    toks = set()
+    for b in range(len(cu) - 1):
+        lq = cu[b + 1] - cu[b]
+        for k in range(-(-lq // block)):
+            toks.add(cu[b] + lq - 1 - block * k)
+            toks.add(cu[b] + max(0, lq - block * (k + 1)))
+    return [(t, h) for t in sorted(toks) for h in range(num_heads)]
+
+
+_ORACLE_CACHE: dict = {}
+
+
+def oracle_prefill_cached(case, rows):
+    """oracle_prefill(case, rows), remembered for the process by the case's
+    name and the rows (full-size workloads checked by several tests)."""
+    key = (case.name, hashlib.sha1(np.asarray(rows, dtype=np.int64).tobytes()).hexdigest())
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = oracle_prefill(case, rows)
+    return _ORACLE_CACHE[key]

@@ -15,7 +15,7 @@ import torch
 
 import softmax_attention_paged_amd as sap
 from softmax_attention_paged_amd import inputs
-from helpers import compare, f64, oracle_prefill
+from helpers import block_edge_rows, compare, f64, oracle_prefill, oracle_prefill_cached
 
 pytestmark = pytest.mark.gpu
 
@@ -140,12 +140,20 @@ def _sampled(case, kv_splits, n_rows, seed=0):
     return compare(got, ref, np.array([float(lse[t, h]) for t, h in rows]), lref)
 
 
-def test_ragged_paged_prefill_80k_forced_two_splits_sampled():
-    # the 4-request, 80K-key chunked prefill (512/1024 queries each) with its
-    # keys split in two: every split boundary falls inside every request
+def test_ragged_paged_prefill_80k_forced_two_splits_block_edges():
+    """The 4-request, 80K-key chunked prefill (512/1024 queries each) with its
+    keys split in two (the boundary at key 40960 falls inside every
+    request's visible keys): the first and last row of every 32-row block of
+    every head (6,144 rows) against the oracle."""
     case = inputs.ragged_paged_prefill()
     print("case", case.name, flush=True)
-    print(_sampled(case, 2, 48))
+    out, lse = _run(case, 2)
+    rows = block_edge_rows(case.cu_seqlens_q.numpy(), case.q.shape[1])
+    ref, lref = oracle_prefill_cached(case, rows)
+    got = np.stack([f64(out[t, h]) for t, h in rows])
+    res = compare(got, ref, np.array([float(lse[t, h]) for t, h in rows]), lref)
+    res["rows_checked"] = len(rows)
+    print(res)
 
 
 def test_single_request_80k_planner_split_sampled():
