@@ -266,6 +266,20 @@ size_t attn_decode_workspace_size(const attn_decode_params *p);
  * or ATTN_ERR_HIP. */
 attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): attn_decode_paged with
+ * the split partials in a scratch array the library holds on each device
+ * (128 MiB, kept until the process ends) instead of a caller workspace;
+ * p->workspace and p->workspace_bytes are ignored. It allocates nothing. A
+ * plan whose partials exceed the scratch (attn_decode_workspace_size(p) >
+ * 128 MiB) returns ATTN_ERR_WORKSPACE_TOO_SMALL before anything is enqueued;
+ * pass num_splits to plan fewer splits. Every call on one device shares its
+ * scratch: calls that overlap on one device (other streams, other threads)
+ * race and must be ordered by the caller. Results equal attn_decode_paged's
+ * bit for bit (the same plan and kernels). Returns as attn_decode_paged, or
+ * ATTN_ERR_HIP when the scratch's device address cannot be obtained. */
+attn_status_t attn_decode_paged_noalloc(const attn_decode_params *p, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Merge split partials by log-sum-exp ("TokenSpeed-MLA", section "Decode
  * performance": a second kernel reduces the split-KV partial results; section

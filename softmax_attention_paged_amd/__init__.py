@@ -6,7 +6,8 @@ must be built in-tree first (python -m softmax_attention_paged_amd.build).
 """
 
 from .api import (  # noqa: F401
-    cache_append, decode_paged, decode_params, decode_plan, default_scale, merge_lse, mla_kv_pack_fp8, prefill,
+    cache_append, decode_paged, decode_paged_noalloc, decode_params, decode_plan, default_scale, merge_lse,
+    mla_kv_pack_fp8, prefill,
     prefill_workspace_size,
 )
 from ._ffi import AttnError, LIB_PATH, load  # noqa: F401

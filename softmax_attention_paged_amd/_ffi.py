@@ -105,6 +105,7 @@ EXPORTS = {
     "attn_decode_plan": (ctypes.c_int, [ctypes.POINTER(DecodeParams), ctypes.POINTER(DecodePlanInfo)]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(DecodeParams)]),
     "attn_decode_paged": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
+    "attn_decode_paged_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
     "attn_merge_lse": (ctypes.c_int, [_p, _p, _i32, _i64, _i32, _p, ctypes.c_int, _p, _p]),
     "attn_cache_append": (ctypes.c_int, [ctypes.POINTER(CacheAppendParams), _p]),
     "attn_mla_kv_pack_fp8": (ctypes.c_int, [ctypes.POINTER(MlaKvPackParams), _p]),

@@ -127,6 +127,32 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
     return (out, lse) if return_lse else out
 
 
+def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
+                         causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
+                         num_splits=0, out=None, lse=None, window_left=-1, packed_q=False,
+                         total_kv_tokens=0):
+    """decode_paged through attn_decode_paged_noalloc: the split partials go
+    to the library's static per-device scratch, so with `out` (and `lse`,
+    if wanted) given the call allocates nothing. Returns out, or (out, lse)
+    when lse is given."""
+    _need(q.is_cuda and q.dtype == _BF16 and q.is_contiguous(), "q must be a contiguous bf16 CUDA tensor")
+    _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
+    _need(block_table.stride(1) == 1 and seq_lens.is_contiguous(), "block_table rows and seq_lens must be contiguous")
+    b, q_len, hq, _ = q.shape
+    dv = head_dim_v if head_dim_v is not None else _as_4d_cache(v_cache if v_cache is not None else k_cache).shape[3]
+    if out is None:
+        out = torch.empty((b, q_len, hq, dv), dtype=_BF16, device=q.device)
+    _need(out.dtype == _BF16 and out.is_contiguous(), "out must be contiguous bf16")
+    _need(lse is None or (lse.dtype == torch.float32 and lse.is_contiguous()), "lse must be contiguous float32")
+    p = decode_params(q, k_cache, v_cache, block_table, seq_lens, max_seq_len=max_seq_len,
+                      softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
+                      k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=None,
+                      out=out, lse=lse, window_left=window_left, packed_q=packed_q,
+                      total_kv_tokens=total_kv_tokens)
+    _ffi.check(_ffi.load().attn_decode_paged_noalloc(ctypes.byref(p), _stream(q.device)), "attn_decode_paged_noalloc")
+    return (out, lse) if lse is not None else out
+
+
 # --------------------------------------------------------------------------
 # Prefill
 # --------------------------------------------------------------------------

@@ -419,19 +419,16 @@ size_t attn_decode_workspace_size(const attn_decode_params *p) {
   return plan_decode(p).workspace;
 }
 
-attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream) {
-  attn_status_t st = validate_decode(p, true);
-  if (st != ATTN_OK) return st;
-  if (p->batch == 0) return ok();
-  const DecodePlan pl = plan_decode(p);
-  if (pl.splits > 1) {
-    if (!p->workspace || p->workspace_bytes < pl.workspace)
-      return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.workspace,
-                  p->workspace ? p->workspace_bytes : (size_t)0);
-    if (!aligned16(p->workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  }
+}  // extern "C"
+
+namespace {
+
+// The split kernel and, with more than one split, the merge, for a
+// validated call whose split partials go to `workspace`.
+attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, void *workspace,
+                             hipStream_t stream) {
   const int64_t rows_total = (int64_t)p->batch * p->q_len * p->num_q_heads;
-  float *o_parts = static_cast<float *>(p->workspace);
+  float *o_parts = static_cast<float *>(workspace);
   float *lse_parts = pl.splits > 1 ? o_parts + (size_t)pl.splits * rows_total * p->head_dim_v : nullptr;
   const float scale_log2 = p->softmax_scale * attn::kLog2eHost;
   hipError_t err;
@@ -517,6 +514,70 @@ attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream)
     if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(err));
   }
   return ok();
+}
+
+// Scratch of attn_decode_paged_noalloc, for callers that cannot allocate:
+// one array per device, held by the loaded library until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device
+// array: its device address is asked for once per device and kept in
+// g_scratch (see scratch_ptr). Calls on one device share it, so calls that
+// overlap on one device (different streams) race; nothing in it needs to
+// start at zero (each split writes every partial the merge reads).
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::atomic<void *> g_scratch[attn::kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device with the device current (no allocation), or null with the
+// error recorded.
+void *scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= attn::kMaxDevices) {
+    (void)hipGetLastError();
+    fail(ATTN_ERR_HIP, "no current HIP device (or its ordinal is %d or more)", attn::kMaxDevices);
+    return nullptr;
+  }
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (err != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    fail(ATTN_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(err));
+    return nullptr;
+  }
+  g_scratch[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream) {
+  attn_status_t st = validate_decode(p, true);
+  if (st != ATTN_OK) return st;
+  if (p->batch == 0) return ok();
+  const DecodePlan pl = plan_decode(p);
+  if (pl.splits > 1) {
+    if (!p->workspace || p->workspace_bytes < pl.workspace)
+      return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.workspace,
+                  p->workspace ? p->workspace_bytes : (size_t)0);
+    if (!aligned16(p->workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  return decode_enqueue(p, pl, p->workspace, stream);
+}
+
+attn_status_t attn_decode_paged_noalloc(const attn_decode_params *p, hipStream_t stream) {
+  attn_status_t st = validate_decode(p, true);
+  if (st != ATTN_OK) return st;
+  if (p->batch == 0) return ok();
+  const DecodePlan pl = plan_decode(p);
+  if (pl.workspace > kStaticScratchBytes)
+    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "%d splits need %zu bytes of partials; the static scratch holds %zu",
+                pl.splits, pl.workspace, kStaticScratchBytes);
+  void *ws = nullptr;
+  if (pl.splits > 1 && !(ws = scratch_ptr())) return ATTN_ERR_HIP;
+  return decode_enqueue(p, pl, ws, stream);
 }
 
 attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
