@@ -49,20 +49,151 @@ def kernel_source_hash(names: list[str]) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, sources: list[str], plan: dict) -> dict | None:
-    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE,
-    WRITE_SIZE), stored under profiles/; only used while the kernel sources
-    and the launch's split plan are unchanged since the measurement."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+# Workloads whose HBM traffic is measured with rocprofv3 counters: the kernel
+# the roofline names (a substring of its symbol) and the sources it is built
+# from. A record under profiles/ is used only while those sources hash the
+# same as when the counters were taken.
+TRAFFIC_KERNELS = {
+    "qwen3_14b_decode": ("decode_gqa_wave_kernel<128, false>",
+                         ["decode_gqa.hip", "device_common.h", "attn_internal.h"]),
+    "dense_causal_prefill_d128": ("prefill_pipe_kernel<128, 0>",
+                                  ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
+    "dense_causal_prefill_d256": ("prefill_pipe_kernel<256, 0>",
+                                  ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
+    "ragged_paged_prefill_80k": ("prefill_pipe_kernel<128, 1>",
+                                 ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
+    "single_chunk_prefill_80k": ("prefill_pipe_kernel<128, 1>",
+                                 ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
+    "mla_decode_80k_bf16": ("decode_mla_kernel<false, false>",
+                            ["decode_mla.hip", "device_common.h", "attn_internal.h"]),
+    "mla_decode_80k_fp8_e4m3": ("decode_mla_kernel<true, false>",
+                                ["decode_mla.hip", "device_common.h", "attn_internal.h"]),
+    "fp8_mla_prefill_8k": ("prefill_fp8_kernel",
+                           ["prefill_fp8.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
+}
+
+
+def load_traffic(workload: str, plan: dict | None = None) -> dict | None:
+    """HBM bytes per launch of the workload's roofline kernel, measured with
+    rocprofv3 counters (FETCH_SIZE, WRITE_SIZE, each scaled by what the same
+    counter reads for a plain copy of known size), stored under profiles/ by
+    --traffic-summary; None once the kernel's sources (or, for a split
+    decode, its split plan) differ from those the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash(sources):
+    if rec.get("source_hash") != kernel_source_hash(TRAFFIC_KERNELS[workload][1]):
         return None
-    if (rec.get("num_splits"), rec.get("split_tokens")) != (plan["num_splits"], plan["split_tokens"]):
+    if plan is not None and (rec.get("num_splits"), rec.get("split_tokens")) != (plan["num_splits"],
+                                                                               plan["split_tokens"]):
         return None
     return rec
+
+
+def _counter_means(run_dir: str, kernel: str, counter: str) -> tuple[str, float, int]:
+    """Mean over the dispatches of the kernel whose symbol contains `kernel`
+    of one counter in a rocprofv3 --pmc CSV (summed over the counter's
+    instances within a dispatch); returns (symbol, mean, dispatches)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    name = None
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if kernel not in row["Kernel_Name"] or row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = (fn, row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for a kernel matching {kernel!r} under {run_dir}")
+    return name, sum(per.values()) / len(per), len(per)
+
+
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                    copy_bytes: int) -> dict:
+    """Write profiles/traffic_<workload>.json from four rocprofv3 --pmc runs
+    (the workload with FETCH_SIZE, then WRITE_SIZE; a copy of copy_bytes
+    with each): the counters in KiB per dispatch, scaled so that the copy
+    reads and writes copy_bytes."""
+    kernel, sources = TRAFFIC_KERNELS[workload]
+    name, fetch, n_f = _counter_means(fetch_dir, kernel, "FETCH_SIZE")
+    _, write, n_w = _counter_means(write_dir, kernel, "WRITE_SIZE")
+    _, cfetch, _ = _counter_means(copy_fetch_dir, "copy", "FETCH_SIZE")
+    _, cwrite, _ = _counter_means(copy_write_dir, "copy", "WRITE_SIZE")
+    fs, ws = copy_bytes / 1024.0 / cfetch, copy_bytes / 1024.0 / cwrite
+    only = "--only " + workload if workload != "qwen3_14b_decode" else "--only qwen3_14b_decode"
+    rec = {
+        "workload": workload,
+        "kernel": name,
+        "source_hash": kernel_source_hash(sources),
+        "fetch_kib_per_dispatch": round(fetch, 3),
+        "write_kib_per_dispatch": round(write, 3),
+        "dispatches": [n_f, n_w],
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cfetch, 3), "write_kib": round(cwrite, 3),
+                             "fetch_scale": round(fs, 6), "write_scale": round(ws, 6)},
+        "bytes_per_launch": int(round((fetch * fs + write * ws) * 1024)),
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py {only} --steps 3",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py {only} --steps 3",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {copy_fetch_dir} -o run -- python3 bench.py "
+            f"--copy-calibration {copy_bytes}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {copy_write_dir} -o run -- python3 bench.py "
+            f"--copy-calibration {copy_bytes}",
+            f"python3 bench.py --traffic-summary {workload} {fetch_dir} {write_dir} {copy_fetch_dir} "
+            f"{copy_write_dir} {copy_bytes}",
+        ],
+    }
+    if workload == "qwen3_14b_decode":
+        from softmax_attention_paged_amd import inputs
+        import softmax_attention_paged_amd as sap
+        case = inputs.qwen3_14b_decode()
+        p = sap.decode_params(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                              max_seq_len=case.max_seq_len, softmax_scale=case.scale,
+                              total_kv_tokens=int(case.seq_lens.sum()))
+        plan = sap.decode_plan(p)
+        rec["num_splits"], rec["split_tokens"] = plan["num_splits"], plan["split_tokens"]
+    with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
+
+
+def trace_summary(workload: str, trace_dir: str, steps: int) -> str:
+    """Write profiles/kernel_trace_<workload>.md from a rocprofv3
+    --kernel-trace --stats run of `bench.py --only <workload>`."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no kernel_stats.csv under {trace_dir}")
+    rows = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[5])
+    lines = [f"# Kernel trace: {workload}", "",
+             "Command (repository root, MI355X, rocprofv3 from ROCm 7.2):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- "
+             f"python3 bench.py --only {workload} --steps {steps}",
+             f"python3 bench.py --trace-summary {workload} {trace_dir} {steps}", "```", "",
+             "Every dispatch of the run: the workload's untimed settling calls, then its timed windows "
+             "(attention kernels), and torch's input staging and fills.", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for name, calls, avg, mn, mx, pct in rows:
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}% |")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md"), "w") as f:
+        f.write(text)
+    return text
 
 
 def time_events(fn, steps: int, stream) -> float:
@@ -260,9 +391,16 @@ def cpu_baseline(case, budget_s: float = 10.0) -> dict:
         done_req += 1
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)), "cpu_model": model,
             "sample": f"{done_req} requests, cycling through the {b_n} of the workload ({done_bytes / 1e6:.1f} MB "
-                      f"of KV), {dt:.1f} s, fp64 numpy, BLAS pool of {threads} threads"}
+                      f"of KV), {dt:.1f} s, fp64 numpy, BLAS pool of {threads} threads (the cores it used)"}
 
 
 def causal_pairs(cu_q: list[int], kv_lens: list[int], causal: bool) -> int:
@@ -278,13 +416,16 @@ def causal_pairs(cu_q: list[int], kv_lens: list[int], causal: bool) -> int:
     return tot
 
 
-def secondary_prefill(name_fn, steps: int, kv_splits: int = 0) -> dict:
+def secondary_prefill(key: str, name_fn, steps: int, kv_splits: int = 0) -> dict:
     import torch
     import softmax_attention_paged_amd as sap
     case = name_fn()
     c = case.to("cuda:0")
     tq, hq, d = case.q.shape
     flops = causal_pairs(case.cu_seqlens_q.tolist(), case.seq_lens_kv.tolist(), case.causal) * hq * 2 * (d + d)
+    # Q read, O and LSE written once; K and V of each (request, KV head) read once
+    hkv = case.k.shape[-2]
+    alg_bytes = tq * hq * (2 * d + 2 * d + 4) + int(case.seq_lens_kv.sum()) * hkv * 2 * d * 2
     out = torch.empty_like(c.q)
     kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, causal=c.causal, kv_splits=kv_splits)
     kv = dict(seq_lens_kv=c.seq_lens_kv, block_table=c.block_table) if c.paged else dict(cu_seqlens_kv=c.cu_seqlens_kv)
@@ -296,10 +437,13 @@ def secondary_prefill(name_fn, steps: int, kv_splits: int = 0) -> dict:
     ms = time_settled(fn, steps, torch.cuda.current_stream())
     tf = flops / (ms * 1e-3) / 1e12
     kernel = f"prefill_pipe_kernel<{d}, {1 if c.paged else 0}>" + (" + merge" if splits > 1 else "")
+    traffic = load_traffic(key)
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "kv_splits": splits,
             "roofline": {"bound": "mfma", "kernel": kernel,
                          "achieved": round(tf, 1),
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                         "algorithmic_bytes_per_launch": alg_bytes}}
 
 
 def secondary_mla(kv_dtype: str, steps: int) -> dict:
@@ -321,10 +465,14 @@ def secondary_mla(kv_dtype: str, steps: int) -> dict:
     flops = pairs * 2 * (dqk + 512)
     tf = flops / (ms * 1e-3) / 1e12
     peak = BF16_PEAK_TFLOPS   # the kernel runs bf16 MFMA for both KV formats
+    traffic = load_traffic(f"mla_decode_80k_{kv_dtype}")
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
             "kv_GB/s": round(case.kv_read_bytes() / (ms * 1e-3) / 1e9, 1), "num_splits": plan["num_splits"],
             "roofline": {"bound": "mfma", "kernel": "decode_mla_kernel + merge", "achieved": round(tf, 1),
-                         "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
+                         "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                         "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                         "algorithmic_bytes_per_launch": case.kv_read_bytes() + case.q.numel() * 2 +
+                         b_n * q_len * hq * (512 * 2 + 4)}}
 
 
 def secondary_prefill_fp8(steps: int) -> dict:
@@ -348,10 +496,14 @@ def secondary_prefill_fp8(steps: int) -> dict:
     qk, pv = pairs * 2 * dqk, pairs * 2 * dv
     tf = (qk + pv) / (ms * 1e-3) / 1e12
     peak = (qk + pv) / (qk / FP8_PEAK_TFLOPS + pv / BF16_PEAK_TFLOPS)
+    traffic = load_traffic("fp8_mla_prefill_8k")
+    alg_bytes = tq * hq * (dqk + 2 * dv + 4) + case.k.numel() + case.v.numel()
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
             "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel", "achieved": round(tf, 1),
                          "peak": round(peak, 1), "unit": "TFLOP/s", "frac": round(tf / peak, 4),
-                         "peak_note": "QK flops at the FP8 peak, P.V flops at the bf16 peak"}}
+                         "peak_note": "QK flops at the FP8 peak, P.V flops at the bf16 peak",
+                         "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                         "algorithmic_bytes_per_launch": alg_bytes}}
 
 
 def secondary_mla_pack(steps: int) -> dict:
@@ -432,12 +584,25 @@ def main() -> int:
                     help="override the prefill planner's key split count (1: unsplit)")
     ap.add_argument("--no-secondary", action="store_true", help="time only the main workload")
     ap.add_argument("--only", default="", metavar="WORKLOAD",
-                    help="time one secondary workload alone (for profiling): dense_causal_prefill_d128, "
+                    help="time one workload alone (for profiling): qwen3_14b_decode (the main line), "
+                         "dense_causal_prefill_d128, "
                          "dense_causal_prefill_d256, ragged_paged_prefill_80k, single_chunk_prefill_80k, mla_decode_80k_bf16, "
                          "mla_decode_80k_fp8_e4m3")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (reference for HBM counters)")
+    ap.add_argument("--traffic-summary", nargs=6, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                           "COPY_WRITE_DIR", "COPY_BYTES"),
+                    help="write profiles/traffic_<WORKLOAD>.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("WORKLOAD", "TRACE_DIR", "STEPS"),
+                    help="write profiles/kernel_trace_<WORKLOAD>.md from a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
+    if args.traffic_summary:
+        w, fd, wd, cfd, cwd, cb = args.traffic_summary
+        print(json.dumps(traffic_summary(w, fd, wd, cfd, cwd, int(cb))))
+        return 0
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary[0], args.trace_summary[1], int(args.trace_summary[2])))
+        return 0
     if args.copy_calibration:
         import torch
         src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -457,14 +622,14 @@ def main() -> int:
     from softmax_attention_paged_amd import inputs
 
     secondaries = {
-        "dense_causal_prefill_d128": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=128), steps,
-                                                                     args.prefill_kv_splits),
-        "dense_causal_prefill_d256": lambda steps: secondary_prefill(lambda: inputs.dense_causal_prefill(d=256), steps,
-                                                                     args.prefill_kv_splits),
-        "ragged_paged_prefill_80k": lambda steps: secondary_prefill(inputs.ragged_paged_prefill, steps,
-                                                                    args.prefill_kv_splits),
-        "single_chunk_prefill_80k": lambda steps: secondary_prefill(inputs.single_chunk_prefill, steps,
-                                                                    args.prefill_kv_splits),
+        "dense_causal_prefill_d128": lambda steps: secondary_prefill(
+            "dense_causal_prefill_d128", lambda: inputs.dense_causal_prefill(d=128), steps, args.prefill_kv_splits),
+        "dense_causal_prefill_d256": lambda steps: secondary_prefill(
+            "dense_causal_prefill_d256", lambda: inputs.dense_causal_prefill(d=256), steps, args.prefill_kv_splits),
+        "ragged_paged_prefill_80k": lambda steps: secondary_prefill(
+            "ragged_paged_prefill_80k", inputs.ragged_paged_prefill, steps, args.prefill_kv_splits),
+        "single_chunk_prefill_80k": lambda steps: secondary_prefill(
+            "single_chunk_prefill_80k", inputs.single_chunk_prefill, steps, args.prefill_kv_splits),
         "mla_decode_80k_bf16": lambda steps: secondary_mla("bf16", steps),
         "mla_decode_80k_fp8_e4m3": lambda steps: secondary_mla("fp8_e4m3", steps),
         "fp8_mla_prefill_8k": secondary_prefill_fp8,
@@ -472,9 +637,11 @@ def main() -> int:
         "cache_append_8k": secondary_append,
         "tiny_gqa_decode": secondary_tiny_decode,
     }
-    if args.only:
+    if args.only and args.only != "qwen3_14b_decode":
         print(json.dumps({args.only: secondaries[args.only](args.steps)}), flush=True)
         return 0
+    if args.only:                       # the main decode alone: no secondaries, no host baseline
+        args.no_secondary = args.no_cpu_baseline = True
 
     log("generating inputs ...")
     case = inputs.qwen3_14b_decode(seed=args.seed)
@@ -532,8 +699,7 @@ def main() -> int:
     split_ms = ms - merge_ms
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     achieved = alg_bytes / (split_ms * 1e-3) / 1e9
-    sources = ["decode_gqa.hip", "device_common.h", "attn_internal.h"]
-    traffic = load_traffic("decode_gqa_qwen3_14b", sources, plan)
+    traffic = load_traffic("qwen3_14b_decode", plan)
     line = {
         "metric": "prefill attn TFLOP/s (% MFMA peak); decode KV-read GB/s (% HBM peak)",
         "value": round(gbs, 2),

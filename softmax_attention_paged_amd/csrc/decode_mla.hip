@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
         // and the rows of a unit start at most q_len - 1 <= 3 keys apart); a
         // restarted walk also sets the anchors its abandoned predecessor did
         // not reach. A rising walk takes every tile's max (its O is dropped).
-        {
+        if (it < 2 || attempt > 0) {          // uniform: later tiles of the first walk skip it
           float mx = kNegInf;
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
