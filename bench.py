@@ -56,13 +56,13 @@ def kernel_source_hash(names: list[str]) -> str:
 TRAFFIC_KERNELS = {
     "qwen3_14b_decode": ("decode_gqa_wave_kernel<128, false>",
                          ["decode_gqa.hip", "device_common.h", "attn_internal.h"]),
-    "dense_causal_prefill_d128": ("prefill_pipe_kernel<128, 0>",
+    "dense_causal_prefill_d128": ("prefill_pp8_kernel<128, 0>",
                                   ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
     "dense_causal_prefill_d256": ("prefill_pipe_kernel<256, 0>",
                                   ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
-    "ragged_paged_prefill_80k": ("prefill_pipe_kernel<128, 1>",
+    "ragged_paged_prefill_80k": ("prefill_pp8_kernel<128, 1>",
                                  ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
-    "single_chunk_prefill_80k": ("prefill_pipe_kernel<128, 1>",
+    "single_chunk_prefill_80k": ("prefill_pp8_kernel<128, 1>",
                                  ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
     "mla_decode_80k_bf16": ("decode_mla_kernel<false, false>",
                             ["decode_mla.hip", "device_common.h", "attn_internal.h"]),
@@ -436,7 +436,8 @@ def secondary_prefill(key: str, name_fn, steps: int, kv_splits: int = 0) -> dict
     fn = lambda: sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, softmax_scale=c.scale, out=out, workspace=ws, **kv, **kw)
     ms = time_settled(fn, steps, torch.cuda.current_stream())
     tf = flops / (ms * 1e-3) / 1e12
-    kernel = f"prefill_pipe_kernel<{d}, {1 if c.paged else 0}>" + (" + merge" if splits > 1 else "")
+    kernel = (f"{'prefill_pp8_kernel' if d == 128 else 'prefill_pipe_kernel'}<{d}, {1 if c.paged else 0}>" +
+              (" + merge" if splits > 1 else ""))
     traffic = load_traffic(key)
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "kv_splits": splits,
             "roofline": {"bound": "mfma", "kernel": kernel,

@@ -261,7 +261,11 @@ DecodePlan plan_decode(const attn_decode_params *p) {
 }
 
 
-constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
+// Query rows per prefill workgroup and workgroups a CU holds at once, by
+// head dim: the D = 128 kernel runs eight waves (256 rows, one workgroup per
+// CU), the others four (128 rows; two workgroups per CU at D = 64).
+int prefill_rows_per_wg(int d) { return d == 128 ? 256 : 128; }
+int prefill_wgs_per_cu(int d) { return d == 64 ? 2 : 1; }
 
 // shapes_only: the checks a workspace query makes (no pointers or strides).
 attn_status_t validate_prefill(const attn_prefill_params *p, bool shapes_only = false) {
@@ -327,12 +331,14 @@ attn_status_t validate_prefill(const attn_prefill_params *p, bool shapes_only = 
 }
 
 // Key splits of a bf16 prefill: workgroups per query tile along the keys.
-// Workgroups are counted from total_q (query tiles of tq = kPrefillRows / gh
-// tokens, times the head groups) against the CUs' slots (two workgroups per
-// CU at D <= 128, one above). Measured on 80K-key paged prefills:
-//   - at most half a round (under one workgroup per CU): split by the largest
-//     power of two that keeps the launch within one round (one 512-query
-//     chunk, 128 workgroups: 1.56 -> 0.67 ms at four splits);
+// Workgroups are counted from total_q (query tiles of prefill_rows_per_wg /
+// gh tokens, times the head groups) against the CUs' slots. Measured on
+// 80K-key paged prefills (with the four-wave D = 128 kernel, 128-row
+// workgroups, two per CU: the same ratios of workgroups to slots as the
+// eight-wave kernel's 256-row workgroups, one per CU):
+//   - at most half a round (under one workgroup per slot pair): split by the
+//     largest power of two that keeps the launch within one round (one
+//     512-query chunk, 128 workgroups: 1.56 -> 0.67 ms at four splits);
 //   - more than one round with a last round at most three quarters full:
 //     four splits (768 workgroups over 512 slots: 4.67 -> 4.40 ms);
 //   - otherwise unsplit: between half and one round, or whole rounds, the
@@ -360,8 +366,9 @@ PrefillPlan plan_prefill(const attn_prefill_params *p) {
   if (splits <= 0) {
     const int group = p->num_q_heads / p->num_kv_heads;
     const int gh = (group % 4 == 0) ? 4 : (group % 2 == 0 ? 2 : 1);
-    const int64_t units = std::max<int64_t>(1, cdiv(p->total_q, kPrefillRows / gh)) * (p->num_q_heads / gh);
-    const int64_t slots = (int64_t)num_cus() * (p->head_dim_qk <= 128 ? 2 : 1);
+    const int64_t units = std::max<int64_t>(1, cdiv(p->total_q, prefill_rows_per_wg(p->head_dim_qk) / gh)) *
+                          (p->num_q_heads / gh);
+    const int64_t slots = (int64_t)num_cus() * prefill_wgs_per_cu(p->head_dim_qk);
     int64_t sp = 1;
     if (2 * units <= slots) {
       while (2 * sp * units <= slots) sp *= 2;
@@ -608,7 +615,7 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream) {
   a.head_dim = p->head_dim_qk;
   a.max_seqlen_q = p->max_seqlen_q;
   a.max_seqlen_kv = p->max_seqlen_kv;
-  a.q_tiles = (int)cdiv(p->max_seqlen_q, kPrefillRows);
+  a.q_tiles = (int)cdiv(p->max_seqlen_q, prefill_rows_per_wg(p->head_dim_qk));
   a.fp8 = p->qkv_dtype == ATTN_FP8_E4M3;
   // FP8: the dequantisation scales of q and k fold into the score scale and
   // v's into the final normalisation

@@ -32,11 +32,13 @@
 // the END of each request, so tile 0 of every request sees the most keys and
 // is launched first.
 //
-// The kernel is software-pipelined: the scores of tile j+1 are computed on
-// the matrix cores beside the softmax of tile j, with separate K and V
-// double buffers (see prefill_pipe_kernel). D = 256 runs at one wave per
-// SIMD (its Q operand and O accumulator take most of a SIMD's registers),
-// D <= 128 at two.
+// Two kernels. prefill_pp8_kernel (D = 128): eight waves in two groups
+// whose matrix and softmax phases alternate, 256 query rows per workgroup
+// sharing each K/V tile. prefill_pipe_kernel (D = 64, 256): four waves, each
+// software-pipelined in itself (the scores of tile j+1 on the matrix cores
+// beside the softmax of tile j). Both keep separate K and V double buffers;
+// D = 256 runs at one wave per SIMD (its Q operand and O accumulator take
+// most of a SIMD's registers), the others at two.
 
 #include <type_traits>
 
@@ -64,9 +66,9 @@ namespace {
 // loads are issued as inline assembly so that no LDS read in between waits
 // for them (only the barrier at the top of the next iteration does).
 
-template <int D>
+template <int D, int W = 4>
 struct PpGeom {
-  static constexpr int kW = 4;                         // waves per workgroup
+  static constexpr int kW = W;                         // waves per workgroup
   static constexpr int kWPE = D <= 128 ? 2 : 1;        // waves per SIMD the registers allow
   static constexpr int kRing = D <= 128 ? 0 : 4;       // LDS operand reads issued ahead (0: compiler order)
   static constexpr int kN = 64;                        // keys per tile
@@ -87,9 +89,9 @@ struct PpGeom {
 enum PpKv { kKvDense = 0, kKvWidePages = 1, kKvNarrowPages = 2 };
 
 // Tile row that load k of this lane fills.
-template <int D>
+template <int D, int W = 4>
 __device__ __forceinline__ int pp_row(int k, int wave, int lane) {
-  using G = PpGeom<D>;
+  using G = PpGeom<D, W>;
   return ((k * G::kW + wave) * 64 + lane) / G::kCPR;
 }
 
@@ -97,10 +99,10 @@ __device__ __forceinline__ int pp_row(int k, int wave, int lane) {
 // Load instruction k uses entry k % kLaneOffs: the swizzle depends on the
 // row modulo 16, and instructions k and k + kLaneOffs start a multiple of
 // 16 rows apart.
-template <int D>
+template <int D, int W = 4>
 __device__ __forceinline__ void pp_lane_off(int wave, int lane, int64_t stride_tok,
-                                            uint32_t (&off)[PpGeom<D>::kLaneOffs]) {
-  using G = PpGeom<D>;
+                                            uint32_t (&off)[PpGeom<D, W>::kLaneOffs]) {
+  using G = PpGeom<D, W>;
   const int r = lane / G::kCPR;
 #pragma unroll
   for (int v = 0; v < G::kLaneOffs; ++v) {
@@ -110,14 +112,15 @@ __device__ __forceinline__ void pp_lane_off(int wave, int lane, int64_t stride_t
 }
 
 // Loads of a tile that lies wholly inside the request (and, paged, inside
-// one page): `tile` is its first row, wave-uniform.
-template <int D>
+// one page): `tile` is its first row, wave-uniform. Load instructions KLO ..
+// KHI - 1 of the wave (all by default; a range of them fills a band of rows).
+template <int D, int W = 4, int KLO = 0, int KHI = PpGeom<D, W>::kLoads>
 __device__ __forceinline__ void pp_issue_whole(const __bf16 *tile, int64_t stride_tok,
-                                               const uint32_t (&lane_off)[PpGeom<D>::kLaneOffs], int wave,
+                                               const uint32_t (&lane_off)[PpGeom<D, W>::kLaneOffs], int wave,
                                                uint32_t lds_dst) {
-  using G = PpGeom<D>;
+  using G = PpGeom<D, W>;
 #pragma unroll
-  for (int k = 0; k < G::kLoads; ++k) {
+  for (int k = KLO; k < KHI; ++k) {
     const int inst = k * G::kW + wave;
     lds_dma16(tile + (int64_t)inst * G::kRowsPerInst * stride_tok, lane_off[k % G::kLaneOffs], lds_dst + inst * 1024);
   }
@@ -126,13 +129,13 @@ __device__ __forceinline__ void pp_issue_whole(const __bf16 *tile, int64_t strid
 // Loads of a tile row by row: rows at or past the request's end are
 // zero-filled with LDS stores instead, and each row finds its page itself
 // (`page` for wide pages, `pid[k]` for narrow ones).
-template <int D, int KV>
+template <int D, int KV, int W = 4, int KLO = 0, int KHI = PpGeom<D, W>::kLoads>
 __device__ __forceinline__ void pp_issue_rows(const __bf16 *src, int64_t stride_page, int64_t stride_tok, int page,
-                                              const int (&pid)[PpGeom<D>::kLoads], int j0, int lk, int pmask,
+                                              const int (&pid)[PpGeom<D, W>::kLoads], int j0, int lk, int pmask,
                                               int wave, int lane, __bf16 *dst) {
-  using G = PpGeom<D>;
+  using G = PpGeom<D, W>;
 #pragma unroll
-  for (int k = 0; k < G::kLoads; ++k) {
+  for (int k = KLO; k < KHI; ++k) {
     const int inst = k * G::kW + wave;
     const int chunk_lin = inst * 64 + lane;
     const int row = chunk_lin / G::kCPR;
@@ -151,24 +154,25 @@ __device__ __forceinline__ void pp_issue_rows(const __bf16 *src, int64_t stride_
 
 // One K or V tile: `src` is the request's first key (dense) or page 0
 // (paged) of the workgroup's KV head.
-template <int D, int KV>
+template <int D, int KV, int W = 4, int KLO = 0, int KHI = PpGeom<D, W>::kLoads>
 __device__ __forceinline__ void pp_issue(const __bf16 *src, int64_t stride_page, int64_t stride_tok,
-                                         const uint32_t (&lane_off)[PpGeom<D>::kLaneOffs], int page, const int (&pid)[PpGeom<D>::kLoads], int j0, int lk, int pmask,
+                                         const uint32_t (&lane_off)[PpGeom<D, W>::kLaneOffs], int page,
+                                         const int (&pid)[PpGeom<D, W>::kLoads], int j0, int lk, int pmask,
                                          int wave, int lane, __bf16 *dst) {
-  if (KV != kKvNarrowPages && j0 + PpGeom<D>::kN <= lk) {
+  if (KV != kKvNarrowPages && j0 + PpGeom<D, W>::kN <= lk) {
     const __bf16 *tile = (KV == kKvDense) ? src + (int64_t)j0 * stride_tok
                                           : src + (int64_t)page * stride_page + (int64_t)(j0 & pmask) * stride_tok;
-    pp_issue_whole<D>(tile, stride_tok, lane_off, wave, lds_address(dst));
+    pp_issue_whole<D, W, KLO, KHI>(tile, stride_tok, lane_off, wave, lds_address(dst));
   } else {
-    pp_issue_rows<D, KV>(src, stride_page, stride_tok, page, pid, j0, lk, pmask, wave, lane, dst);
+    pp_issue_rows<D, KV, W, KLO, KHI>(src, stride_page, stride_tok, page, pid, j0, lk, pmask, wave, lane, dst);
   }
 }
 
 // Block-table entries for the tile at key j0 (never past the request's last
 // page): one wave-uniform entry for wide pages, one per loaded row otherwise.
-template <int D, int KV>
+template <int D, int KV, int W = 4>
 __device__ __forceinline__ void pp_fetch_pages(const int32_t *bt_row, int j0, int lk, int shift, int wave, int lane,
-                                               int &page, int (&pid)[PpGeom<D>::kLoads]) {
+                                               int &page, int (&pid)[PpGeom<D, W>::kLoads]) {
   if constexpr (KV == kKvWidePages) {
     // a scalar load (the table is read-only here): waiting for it does not
     // wait for the vector-memory tile loads in flight
@@ -176,8 +180,8 @@ __device__ __forceinline__ void pp_fetch_pages(const int32_t *bt_row, int j0, in
     page = (j0 < lk) ? reinterpret_cast<const_i32 *>(reinterpret_cast<uintptr_t>(bt_row))[j0 >> shift] : 0;
   } else if constexpr (KV == kKvNarrowPages) {
 #pragma unroll
-    for (int k = 0; k < PpGeom<D>::kLoads; ++k) {
-      const int j = j0 + pp_row<D>(k, wave, lane);
+    for (int k = 0; k < PpGeom<D, W>::kLoads; ++k) {
+      const int j = j0 + pp_row<D, W>(k, wave, lane);
       pid[k] = (j < lk) ? bt_row[j >> shift] : 0;
     }
   }
@@ -528,14 +532,322 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong kernel (D = 128): eight waves of one 32-row block each, in two
+// groups of four; waves w and w + 4 run on the same SIMD. A tile step splits
+// into a matrix phase (S(j+1) = K(j+1) Q^T and O^T += V(j)^T P(j)^T: 32
+// MFMAs, operands from LDS) and a vector phase (mask, max and re-base of
+// S(j+1), P(j+1) = exp2(..), sums), and the two groups run them out of step,
+// separated by workgroup barriers: while one group's waves keep the matrix
+// cores busy, the other group's waves on the same SIMDs do their softmax
+// ("Flywheel Attention", section 3.1: the exp work of one fragment beside
+// the matrix work of another). Per tile j:
+//
+//   barrier (tile loads landed) | group 0: matrix j   group 1: vector j-1 |
+//   barrier                     | group 0: vector j   group 1: matrix j
+//
+// The waves of the matrix phase raise their issue priority. 256 query rows
+// share each K/V tile, and a CU holds one workgroup (two waves per SIMD).
+
+template <int D>
+struct P8Geom {
+  static constexpr int kW = 8;                // waves per workgroup (two groups of four)
+  static constexpr int kN = 64;               // keys per tile
+  static constexpr int kKB = D / 16;          // QK k-steps
+  static constexpr int kNB = D / 32;          // PV 32-channel blocks
+  static constexpr int kKK = kN / 16;         // PV k-steps
+  static constexpr int kTile = kN * D;        // elements of one K or V tile
+  static constexpr int kRing = 3;             // LDS operand reads in flight ahead of the MFMAs
+};
+
+template <int D, int KV>
+__global__ __launch_bounds__(64 * P8Geom<D>::kW, 1) void prefill_pp8_kernel(const PrefillArgs a) {
+  using G = P8Geom<D>;
+  using L = PpGeom<D, 4>;                     // the tile loads, spread over the four waves of group 0
+  static_assert(L::kN == G::kN, "tile size");
+  __shared__ __attribute__((aligned(16))) __bf16 lds[4 * G::kTile];   // K slot 0, K slot 1, V slot 0, V slot 1
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;                  // 0: matrix phase first; 1: vector phase first
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  PfUnit u;
+  if (!pf_unit(a, G::kW, u)) return;
+  const int blocks_per_head = G::kW / u.gh;
+  const int head = u.h0 + wave / blocks_per_head;
+  const int t = u.q_end - u.tq + (wave % blocks_per_head) * 32 + r32;   // may be < 0 at the top
+  const bool row_valid = t >= u.q_begin && t < u.q_end;
+  int bound = a.causal ? min(u.lk, max(0, u.lk - u.lq + t + 1)) : u.lk;
+  if (!row_valid) bound = 0;
+  // Sliding window ("TokenSpeed-MLA", kernel capability summary,
+  // window_left): row t sees no key before lk - lq - window_left + t.
+  const bool windowed = a.window_left >= 0;
+  const int begin = windowed ? max(0, u.lk - u.lq - a.window_left + t) : 0;
+  int jb = windowed ? max(0, u.lk - u.lq - a.window_left + u.q_begin) & ~(G::kN - 1) : 0;
+  int split_end = 0x7fffffff;
+  if (a.kv_splits > 1) {
+    jb = max(jb, u.split * a.split_tokens);
+    split_end = (u.split + 1) * a.split_tokens;
+  }
+  int wave_max = bound, valid_min = row_valid ? bound : 0x7fffffff;
+  int begin_max = row_valid ? begin : 0, begin_min = row_valid ? begin : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    wave_max = max(wave_max, __shfl_xor(wave_max, off, 64));
+    valid_min = min(valid_min, __shfl_xor(valid_min, off, 64));
+    begin_max = max(begin_max, __shfl_xor(begin_max, off, 64));
+    begin_min = min(begin_min, __shfl_xor(begin_min, off, 64));
+  }
+  wave_max = __builtin_amdgcn_readfirstlane(wave_max);
+  valid_min = __builtin_amdgcn_readfirstlane(valid_min);
+  begin_max = __builtin_amdgcn_readfirstlane(begin_max);
+  begin_min = __builtin_amdgcn_readfirstlane(begin_min);
+  const int kv_end = min(split_end, a.causal ? min(u.lk, max(0, u.lk - u.lq + u.q_end)) : u.lk);
+  const int nt = kv_end > jb ? (kv_end - jb + G::kN - 1) / G::kN : 0;       // tiles the workgroup loads
+  const int ntw = min(nt, wave_max > jb ? (wave_max - jb + G::kN - 1) / G::kN : 0);   // tiles this wave computes
+  // the wave's first tile with a key for one of its rows (0 without a
+  // window); its matrix phases start one tile earlier (that tile's keys are
+  // all below every row's window: the vector phase before it masks the
+  // stale scores whole, so it adds nothing, and it computes the scores of
+  // tile it0)
+  const int it0 = (windowed && begin_min != 0x7fffffff && begin_min > jb) ? (begin_min - jb) / G::kN : 0;
+  // (at most tile 1: the prologue holds K(0) and K(1); the tiles between
+  // it_lo and it0 - 1 are masked whole and add nothing)
+  const int it_lo = min(max(it0 - 1, 0), 1);
+
+  // Q^T operands (a negative scale negates Q, exact in bf16, so c > 0)
+  const float c = fabsf(a.scale_log2);
+  const u32x4 qsign = (a.scale_log2 < 0.f) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u} : u32x4{};
+  bf16x8 qop[G::kKB];
+  {
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (u.q_off + t) * a.q_stride_tok +
+                         (int64_t)head * a.q_stride_head;
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb)
+      qop[kb] = row_valid ? __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + h * 8)) ^ qsign)
+                          : bf16x8{};
+  }
+  int koff[G::kKB];
+  {
+    const int hf = h ^ pf_swz<D>(r32);
+#pragma unroll
+    for (int kb = 0; kb < G::kKB; ++kb) koff[kb] = r32 * D * 2 + ((2 * kb) ^ hf) * 16;
+  }
+  int voff[2][G::kNB];
+  {
+    const int s16 = lane & 15;
+    const int row0 = 4 * h + (s16 >> 2);
+    const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+    const int f0 = pf_swz<D>(row0), f1 = pf_swz<D>(row0 + 8);
+#pragma unroll
+    for (int nb = 0; nb < G::kNB; ++nb) {
+      voff[0][nb] = row0 * D * 2 + ((4 * nb + cb) ^ f0) * 16 + 8 * (s16 & 1);
+      voff[1][nb] = (row0 + 8) * D * 2 + ((4 * nb + cb) ^ f1) * 16 + 8 * (s16 & 1);
+    }
+  }
+
+  const __bf16 *ksrc = static_cast<const __bf16 *>(a.k) + (int64_t)u.kvh * a.k_stride_head;
+  const __bf16 *vsrc = static_cast<const __bf16 *>(a.v) + (int64_t)u.kvh * a.v_stride_head;
+  if constexpr (KV == kKvDense) {
+    ksrc += u.kv_off * a.k_stride_tok;
+    vsrc += u.kv_off * a.v_stride_tok;
+  }
+  const int lw = wave & 3;                    // the wave's share of the tile loads (group 0 loads)
+  uint32_t koff_g[L::kLaneOffs], voff_g[L::kLaneOffs];
+  pp_lane_off<D, 4>(lw, lane, a.k_stride_tok, koff_g);
+  pp_lane_off<D, 4>(lw, lane, a.v_stride_tok, voff_g);
+  const int32_t *bt_row = (KV != kKvDense) ? a.block_table + (int64_t)u.b * a.block_table_stride : nullptr;
+  const int pmask = (1 << a.page_shift) - 1;
+  int kpage = 0, vpage = 0;
+  int kpid[L::kLoads] = {}, vpid[L::kLoads] = {};
+  auto issue_k = [&](int j0t, int page, const int (&pid)[L::kLoads], __bf16 *dst) __attribute__((always_inline)) {
+    pp_issue<D, KV, 4>(ksrc, a.k_stride_page, a.k_stride_tok, koff_g, page, pid, j0t, u.lk, pmask, lw, lane, dst);
+  };
+  auto issue_v = [&](int j0t, int page, const int (&pid)[L::kLoads], __bf16 *dst) __attribute__((always_inline)) {
+    pp_issue<D, KV, 4>(vsrc, a.v_stride_page, a.v_stride_tok, voff_g, page, pid, j0t, u.lk, pmask, lw, lane, dst);
+  };
+  auto kslot = [&](int par) { return lds + par * G::kTile; };
+  auto vslot = [&](int par) { return lds + (2 + par) * G::kTile; };
+  if (grp == 0 && nt > 0) {
+    pp_fetch_pages<D, KV, 4>(bt_row, jb, u.lk, a.page_shift, lw, lane, kpage, kpid);
+    issue_k(jb, kpage, kpid, kslot(0));
+    issue_v(jb, kpage, kpid, vslot(0));
+    pp_fetch_pages<D, KV, 4>(bt_row, jb + G::kN, u.lk, a.page_shift, lw, lane, vpage, vpid);
+    if (nt > 1) issue_k(jb + G::kN, vpage, vpid, kslot(1));
+    pp_fetch_pages<D, KV, 4>(bt_row, jb + 2 * G::kN, u.lk, a.page_shift, lw, lane, kpage, kpid);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  f32x16 sn[2] = {f32x16{}, f32x16{}};        // scores of the next tile
+  bf16x8 pop[G::kKK];                         // P of the current tile, bf16
+  float m = kNegInf, lsum = 0.f;
+  f32x16 oacc[G::kNB];
+#pragma unroll
+  for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < G::kKK; ++kk) pop[kk] = bf16x8{};
+
+  // Matrix phase j: S(j+1) = K(j+1) Q^T from `knext`, O^T += V(j)^T P(j)^T
+  // from `vbytes`; one LDS operand read per MFMA, issued kRing ahead.
+  auto matrix_phase = [&](const char *knext, const char *vbytes) __attribute__((always_inline)) {
+    constexpr int kQK = 2 * G::kKB, kPV = G::kKK * G::kNB, kSteps = kQK + kPV, kR = G::kRing;
+    auto rd = [&](int q) __attribute__((always_inline)) -> bf16x8 {
+      if (q < kQK) return *reinterpret_cast<const bf16x8 *>(knext + koff[q % G::kKB] + (q / G::kKB) * 32 * D * 2);
+      const int v = q - kQK, kk = v / G::kNB, nb = v % G::kNB;
+      return concat(lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2),
+                    lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2));
+    };
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 ring[kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) ring[i] = rd(i);
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+#pragma unroll
+    for (int q = 0; q < kSteps; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 op = ring[q % kR];
+      if (q + kR < kSteps) ring[q % kR] = rd(q + kR);
+      if (q < kQK) {
+        sn[q / G::kKB] = mfma32x32x16(op, qop[q % G::kKB], sn[q / G::kKB]);
+      } else {
+        const int v = q - kQK;
+        oacc[v % G::kNB] = mfma32x32x16(op, pop[v / G::kNB], oacc[v % G::kNB]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Vector phase for the scores of the tile at key j0n: mask (on tiles that
+  // reach a row bound), lazy re-base of the row max (O rescaled only when it
+  // rises by more than kRebase), P = exp2(s c - m) rounded to bf16, sums.
+  auto vector_phase = [&](int j0n) __attribute__((always_inline)) {
+    if (j0n + G::kN > valid_min || j0n < begin_max) pp_mask(sn, j0n, begin, bound, h);
+    const float mt = half_max(pp_max(sn)) * c;
+    const float m_new = (mt > m + kRebase) ? mt : m;   // keep the base unless the max rose by > kRebase
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2_fast(m - m_use);          // 1 when kept; 0 from -inf
+    m = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int nb = 0; nb < G::kNB; ++nb) oacc[nb] *= alpha;
+    }
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pe = exp2_fast(__builtin_fmaf(sn[sub][i], c, -m_use));
+        pop[2 * sub + (i >> 3)][i & 7] = to_bf16(pe);
+        ps[i & 1] += pe;
+      }
+    lsum = alpha * lsum + (ps[0] + ps[1]);
+  };
+
+  // The scores of the wave's first tile (K(0) or K(1), both resident).
+  if (it_lo < ntw) {
+    const char *k0 = reinterpret_cast<const char *>(kslot(it_lo & 1));
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int kb = 0; kb < G::kKB; ++kb)
+        sn[sub] = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(k0 + koff[kb] + sub * 32 * D * 2), qop[kb], sn[sub]);
+  }
+  // Both groups run the same sequence, group 1 one phase behind:
+  //   group 0:  V(0) | B M(0) B V(1) | B M(1) B V(2) | ... | B
+  //   group 1:  B V(0) | B M(0) B V(1) | B M(1) B V(2) | ...
+  // (B a workgroup barrier, M(j) the matrix phase of tile j, V(j) the vector
+  // phase of the scores of tile j). Between two barriers one group is in a
+  // matrix phase and the other in a vector phase. Only group 0 loads tiles:
+  // at the barrier before its M(j), K(j) and V(j-1) have been read by both
+  // groups' M(j-1), and the loads it issues there (K(j+2), V(j+1)) land
+  // before the barrier before its M(j+1), which group 1's M(j+1) follows.
+  auto vec = [&](int j) __attribute__((always_inline)) {
+    if (j >= it_lo && j < ntw) vector_phase(jb + j * G::kN);
+  };
+  if (grp == 0) vec(0);
+  else {
+    __syncthreads();
+    vec(0);
+  }
+  for (int it = 0; it < nt; ++it) {
+    if (grp == 0) {
+      // this wave's loads of K(it+1) and V(it) (issued a tile ago) have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const int j0 = jb + it * G::kN;
+      if (it + 2 < nt) issue_k(j0 + 2 * G::kN, kpage, kpid, kslot(it & 1));
+      if (it + 1 < nt) issue_v(j0 + G::kN, vpage, vpid, vslot((it + 1) & 1));
+      if constexpr (KV != kKvDense) {
+        if (it + 2 < nt)
+          pp_fetch_pages<D, KV, 4>(bt_row, j0 + 2 * G::kN, u.lk, a.page_shift, lw, lane, vpage, vpid);
+        if (it + 3 < nt)
+          pp_fetch_pages<D, KV, 4>(bt_row, j0 + 3 * G::kN, u.lk, a.page_shift, lw, lane, kpage, kpid);
+      }
+    }
+    if (it >= it_lo && it < ntw)
+      matrix_phase(reinterpret_cast<const char *>(kslot((it + 1) & 1)), reinterpret_cast<const char *>(vslot(it & 1)));
+    __syncthreads();
+    vec(it + 1);
+  }
+  if (grp == 0) __syncthreads();
+
+  // ---- epilogue: O / l -> bf16; LSE2 = m + log2(l) ----
+  const float l = half_sum(lsum);
+  if (!row_valid) return;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  if (a.kv_splits > 1) {
+    const int64_t rows = (int64_t)a.total_q * a.num_q_heads;
+    const int64_t r = (u.q_off + t) * a.num_q_heads + head;
+    if (u.q_off + t >= a.total_q) return;              // total_q too small: outside the workspace
+    if (h == 0) a.lse_parts[u.split * rows + r] = (l > 0.f) ? ((m == kNegInf) ? 0.f : m) + __log2f(l) : kNegInf;
+    if (l > 0.f) {
+      float *prow = a.o_parts + (u.split * rows + r) * D;
+#pragma unroll
+      for (int nb = 0; nb < G::kNB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = oacc[nb][4 * g + i] * inv;
+          *reinterpret_cast<f32x4 *>(prow + 32 * nb + 8 * g + 4 * h) = ov;
+        }
+    }
+    return;
+  }
+  __bf16 *orow = static_cast<__bf16 *>(a.o) + (u.q_off + t) * a.o_stride_tok + (int64_t)head * a.o_stride_head;
+#pragma unroll
+  for (int nb = 0; nb < G::kNB; ++nb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 ob;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[i] = to_bf16(oacc[nb][4 * g + i] * inv);
+      *reinterpret_cast<u32x2 *>(orow + 32 * nb + 8 * g + 4 * h) = __builtin_bit_cast(u32x2, ob);
+    }
+  if (a.lse && h == 0) {
+    const float muse = (m == kNegInf) ? 0.f : m;
+    a.lse[(u.q_off + t) * a.num_q_heads + head] = (l > 0.f) ? muse + __log2f(l) : kNegInf;
+  }
+}
+
 template <int D, int KV>
 hipError_t launch_pp(const PrefillArgs &a, hipStream_t stream) {
   using G = PpGeom<D>;
+  constexpr bool kPing = D == 128;
+  constexpr int kWaves = kPing ? P8Geom<D>::kW : G::kW;
   const int gh = pf_heads_per_wg(a.num_q_heads / a.num_kv_heads);
-  const int tq = 32 * G::kW / gh;
+  const int tq = 32 * kWaves / gh;
   const int64_t q_tiles = (a.max_seqlen_q + tq - 1) / tq;
   const int64_t blocks = q_tiles * (a.kv_splits > 1 ? a.kv_splits : 1) * a.batch * (a.num_q_heads / gh);
-  hipLaunchKernelGGL((prefill_pipe_kernel<D, KV>), dim3((unsigned)blocks), dim3(64 * G::kW), 0, stream, a);
+  if constexpr (kPing)
+    hipLaunchKernelGGL((prefill_pp8_kernel<D, KV>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_pipe_kernel<D, KV>), dim3((unsigned)blocks), dim3(64 * G::kW), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.kv_splits <= 1) return err;
   MergeArgs m{};
