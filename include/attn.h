@@ -185,7 +185,15 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  *   max_seq_len host upper bound of seq_lens; plans the split count.
  *   q_len      1..4 query tokens per request; row (t, h) of a causal request
  *              sees keys j <= seq_len - q_len + t.
- *   num_splits 0 lets the planner choose; otherwise the number of KV splits.
+ *   num_splits 0 lets the planner choose; otherwise the number of KV splits
+ *              of every request. The GQA planner's choice (batch <= 512) is
+ *              key ranges: the 32-key tiles of all requests, in request
+ *              order, cut into K ranges of equal length (K = two waves per
+ *              SIMD of the current device / (Hkv * q_groups), at most 512), so
+ *              every wave walks the same number of keys ("Writing Page
+ *              Attention with PyPTO", section 1.3: equal tasks keep every core
+ *              busy to the end); a request inside one range is written
+ *              directly, the pieces of the others are merged by LSE.
  *   workspace  device scratch of at least attn_decode_workspace_size(p)
  *              bytes (may be NULL when that is 0); contents undefined after.
  *   o          bf16 [batch, q_len, Hq, Dv] contiguous.
@@ -202,11 +210,11 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  *              rows instead of 4; the last tile may be partial. Output and
  *              LSE layouts are unchanged.
  *   total_kv_tokens   optional host-side sum of seq_lens (0: unknown). With
- *              it and num_splits = 0 the GQA planner sizes the splits so
- *              that every unit is resident at once (units <= (total / S_len
- *              + batch) * Hkv * q_groups fit one round of the waves the
- *              current device's CUs hold),
- *              which on ragged batches beats a fixed split length; it only
+ *              num_splits = 0 it caps the key ranges at one per 8 tiles of
+ *              the batch (small batches); for GQA batches above 512 it sizes
+ *              per-request splits so that every unit is resident at once
+ *              (units <= (total / S_len + batch) * Hkv * q_groups fit one
+ *              round of the waves the current device's CUs hold). It only
  *              changes the plan, never the result.
  * Supported: (Dqk, Dv) in {(64,64), (128,128), (256,256)} with bf16 KV and
  * (576, 512) with Hkv == 1 and bf16 or FP8 KV; Hq % Hkv == 0; page_size a
@@ -247,10 +255,17 @@ typedef struct {
   int32_t rows_per_unit;  /* rows computed together: G * F, or the MFMA tile rows (128
                              for the latent shape, 16 otherwise) capped at G * q_len
                              with packed_q                                             */
-  int32_t num_splits;     /* S: KV splits per (request, KV head, q-group)               */
-  int32_t split_tokens;   /* keys per split (the last one of a request may be shorter)  */
+  int32_t num_splits;     /* S: KV splits per (request, KV head, q-group); 0 with key
+                             ranges                                                     */
+  int32_t split_tokens;   /* keys per split (the last one of a request may be shorter);
+                             0 with key ranges                                          */
   int64_t num_units;      /* workgroups of the split kernel                             */
-  size_t workspace_bytes; /* S * R * (Dv + 1) * 4 with R = batch * q_len * Hq; 0 if S==1 */
+  size_t workspace_bytes; /* splits: S * R * (Dv + 1) * 4 with R = batch * q_len * Hq,
+                             0 if S == 1; key ranges: (K + batch) * q_len * Hq * (Dv + 1)
+                             * 4, 0 if K == 1                                           */
+  int32_t key_ranges;     /* K > 0: the GQA plan that cuts the 32-key tiles of all
+                             requests, in request order, into K ranges of (almost) equal
+                             length, one per Hkv * q_groups waves; 0: per-request splits */
 } attn_decode_plan_info;
 
 /* Fill *info with the plan for p. Only shapes and scalars are examined (data
@@ -261,10 +276,23 @@ attn_status_t attn_decode_plan(const attn_decode_params *p, attn_decode_plan_inf
  * the shapes are invalid). Only shapes and scalars are examined. */
 size_t attn_decode_workspace_size(const attn_decode_params *p);
 
-/* Enqueue the split kernel and, when S > 1, the merge. Returns ATTN_OK,
- * ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL
- * or ATTN_ERR_HIP. */
+/* Enqueue the split kernel and, when the plan has partials (workspace_bytes
+ * > 0), the merge. Returns ATTN_OK, ATTN_ERR_INVALID_ARG,
+ * ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE_TOO_SMALL or ATTN_ERR_HIP. */
 attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream);
+
+/* The two kernels of attn_decode_paged, enqueued separately ("TokenSpeed-
+ * MLA", section "Decode performance": the split-KV kernel, then a second
+ * kernel that reduces its partials), for callers that schedule other work
+ * between them or time them apart. attn_decode_paged_split writes the rows
+ * the plan finishes in one unit to o / lse and the partials of the others
+ * to the workspace; attn_decode_paged_merge, enqueued after it with the
+ * same parameters and workspace contents, writes the remaining rows (and
+ * does nothing when the plan has no partials). Together they give
+ * attn_decode_paged's result bit for bit. Same arguments, validation and
+ * return codes as attn_decode_paged. */
+attn_status_t attn_decode_paged_split(const attn_decode_params *p, hipStream_t stream);
+attn_status_t attn_decode_paged_merge(const attn_decode_params *p, hipStream_t stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): attn_decode_paged with

@@ -70,7 +70,7 @@ class DecodePlanInfo(ctypes.Structure):
     _fields_ = [
         ("group", _i32), ("fold", _i32), ("q_groups", _i32), ("rows_per_unit", _i32),
         ("num_splits", _i32), ("split_tokens", _i32), ("num_units", _i64),
-        ("workspace_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t), ("key_ranges", _i32),
     ]
 
 
@@ -106,6 +106,8 @@ EXPORTS = {
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(DecodeParams)]),
     "attn_decode_paged": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
     "attn_decode_paged_noalloc": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
+    "attn_decode_paged_split": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
+    "attn_decode_paged_merge": (ctypes.c_int, [ctypes.POINTER(DecodeParams), _p]),
     "attn_merge_lse": (ctypes.c_int, [_p, _p, _i32, _i64, _i32, _p, ctypes.c_int, _p, _p]),
     "attn_cache_append": (ctypes.c_int, [ctypes.POINTER(CacheAppendParams), _p]),
     "attn_mla_kv_pack_fp8": (ctypes.c_int, [ctypes.POINTER(MlaKvPackParams), _p]),

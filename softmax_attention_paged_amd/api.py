@@ -90,8 +90,12 @@ def decode_plan(params: _ffi.DecodeParams) -> dict:
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                  causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
                  num_splits=0, workspace=None, out=None, return_lse=False, window_left=-1,
-                 packed_q=False, total_kv_tokens=0):
+                 packed_q=False, total_kv_tokens=0, lse=None, phase="both"):
     """Paged decode (split-KV + LSE merge). Returns out, or (out, lse).
+
+    phase "split" or "merge" enqueues only that kernel of the call
+    (attn_decode_paged_split / attn_decode_paged_merge): pass the same out,
+    lse and workspace to both.
 
     q [B, q_len, Hq, Dqk] bf16; caches [pages, page_size, Hkv, D] (or a 3-D
     latent cache, pass v_cache=None and head_dim_v=512); block_table
@@ -110,7 +114,14 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
     if out is None:
         out = torch.empty((b, q_len, hq, dv), dtype=_BF16, device=q.device)
     _need(out.dtype == _BF16 and out.is_contiguous(), "out must be contiguous bf16")
-    lse = torch.empty((b, q_len, hq), dtype=torch.float32, device=q.device) if return_lse else None
+    _need(lse is None or (lse.dtype == torch.float32 and lse.is_contiguous()), "lse must be contiguous float32")
+    if lse is not None:
+        return_lse = True
+    elif return_lse:
+        lse = torch.empty((b, q_len, hq), dtype=torch.float32, device=q.device)
+    entry = {"both": "attn_decode_paged", "split": "attn_decode_paged_split",
+             "merge": "attn_decode_paged_merge"}.get(phase)
+    _need(entry is not None, "phase must be 'both', 'split' or 'merge'")
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, max_seq_len=max_seq_len,
                       softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
                       k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=workspace,
@@ -122,7 +133,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             p.workspace, p.workspace_bytes = workspace.data_ptr(), need
-    _ffi.check(lib.attn_decode_paged(ctypes.byref(p), _stream(q.device)), "attn_decode_paged")
+    _ffi.check(getattr(lib, entry)(ctypes.byref(p), _stream(q.device)), entry)
     del k4
     return (out, lse) if return_lse else out
 

@@ -89,9 +89,21 @@ int window_span(const attn_decode_params *p) {
 struct DecodePlan {
   bool mla;
   int group, fold, q_groups, rows, splits, split_tokens;
+  int key_ranges;          // > 0: the GQA decode cuts the batch's tiles into this many ranges
   int64_t units;
   size_t workspace;
 };
+
+// Shortest key range the planner cuts (tiles of 32 keys): a range pays a
+// query load and an output write per request it touches.
+constexpr int kMinRangeTiles = 8;
+// Waves per CU the key ranges are cut for: two per SIMD. Measured on the
+// 64-request decode (lengths uniform on 256..8192, Hkv 8, D 128, three
+// resident per SIMD): 7, 7.5, 8, 8.5, 9 and 12 waves per CU ran 0.1905,
+// 0.1904, 0.1894, 0.1929, 0.1921 and 0.198 ms per call: fewer concurrent
+// streams read the paged pool more efficiently, down to the point where
+// too few requests are in flight.
+constexpr int kRangeWavesPerCU = 8;
 
 attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) {
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
@@ -207,7 +219,30 @@ DecodePlan plan_decode(const attn_decode_params *p) {
       }
     }
   } else {
-    // HBM-bound, one single-wave unit per (request, KV head, q-group, split).
+    // HBM-bound. Key ranges: the batch's tiles cut evenly over the waves
+    // the CUs hold, every wave resident from the start and streaming the
+    // same bytes. The kernels scan seq_lens on the device (up to
+    // kKeyRangeMaxBatch requests), so the plan needs no lengths; the host
+    // total, when given, only caps the range count for small batches.
+    const bool ext = p->window_enabled || p->packed_q;
+    const int span = window_span(p);
+    const int64_t req_tiles = cdiv(std::max(span, 1), tile) + 1;   // a request's tiles, window alignment included
+    if (p->batch <= attn::kKeyRangeMaxBatch && (int64_t)p->batch * req_tiles < (int64_t(1) << 30)) {
+      const int64_t per = (int64_t)p->num_kv_heads * pl.q_groups;
+      const int64_t slots = (int64_t)cus * std::min(kRangeWavesPerCU, attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext));
+      int64_t upper = (int64_t)p->batch * req_tiles;
+      if (p->total_kv_tokens > 0) upper = std::min<int64_t>(upper, cdiv(p->total_kv_tokens, tile) + p->batch);
+      const int64_t k = std::max<int64_t>(
+          1, std::min<int64_t>({slots / per, (int64_t)attn::kMaxKeyRanges, cdiv(upper, kMinRangeTiles)}));
+      pl.key_ranges = (int)k;
+      pl.splits = 0;
+      pl.split_tokens = 0;
+      pl.units = k * per;
+      const int64_t rows_req = (int64_t)p->q_len * p->num_q_heads;
+      pl.workspace = k > 1 ? (size_t)(k + p->batch) * rows_req * (p->head_dim_v + 1) * sizeof(float) : 0;
+      return pl;
+    }
+    // Otherwise one single-wave unit per (request, KV head, q-group, split).
     splits = 0;
     if (p->total_kv_tokens > 0) {
       // With the host's total of the keys: the split length L for which every
@@ -218,10 +253,8 @@ DecodePlan plan_decode(const attn_decode_params *p) {
       // uniform on 256..8192, Hkv 8, D 128): 0.194-0.204 ms against
       // 0.203-0.213 ms for the fixed rule below; one more split than fits
       // (a few units in a second round) costs 20-30 %.
-      const bool ext = p->window_enabled || p->packed_q;
       const int64_t slots = (int64_t)cus * attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext);
       const int64_t room = slots / ((int64_t)p->num_kv_heads * pl.q_groups) - p->batch;
-      const int span = window_span(p);
       if (room > 0 && span > 0) {
         const int64_t total = std::min<int64_t>(p->total_kv_tokens, (int64_t)p->batch * span);
         int64_t st = std::max<int64_t>(256, cdiv(cdiv(total, room), tile) * tile);
@@ -418,6 +451,7 @@ attn_status_t attn_decode_plan(const attn_decode_params *p, attn_decode_plan_inf
   info->split_tokens = pl.split_tokens;
   info->num_units = pl.units;
   info->workspace_bytes = pl.workspace;
+  info->key_ranges = pl.key_ranges;
   return ok();
 }
 
@@ -430,16 +464,24 @@ size_t attn_decode_workspace_size(const attn_decode_params *p) {
 
 namespace {
 
-// The split kernel and, with more than one split, the merge, for a
-// validated call whose split partials go to `workspace`.
+// Which kernels of a decode call to enqueue.
+enum DecodePhase { kPhaseSplit = 1, kPhaseMerge = 2, kPhaseBoth = 3 };
+
+// The split kernel and, when the plan has partials, the merge, for a
+// validated call whose partials go to `workspace`.
 attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, void *workspace,
-                             hipStream_t stream) {
+                             hipStream_t stream, int phase = kPhaseBoth) {
   const int64_t rows_total = (int64_t)p->batch * p->q_len * p->num_q_heads;
+  // partial slots: S per row, or key_ranges + batch per row of a request
+  const int64_t part_rows = pl.key_ranges > 0 ? (int64_t)(pl.key_ranges + p->batch) * p->q_len * p->num_q_heads
+                                              : (int64_t)pl.splits * rows_total;
   float *o_parts = static_cast<float *>(workspace);
-  float *lse_parts = pl.splits > 1 ? o_parts + (size_t)pl.splits * rows_total * p->head_dim_v : nullptr;
+  float *lse_parts = pl.workspace > 0 ? o_parts + (size_t)part_rows * p->head_dim_v : nullptr;
   const float scale_log2 = p->softmax_scale * attn::kLog2eHost;
-  hipError_t err;
-  if (pl.mla) {
+  hipError_t err = hipSuccess;
+  if (!(phase & kPhaseSplit)) {
+    // merge only
+  } else if (pl.mla) {
     attn::DecodeMlaArgs a{};
     a.q = p->q;
     a.kv_cache = p->k_cache;
@@ -497,6 +539,7 @@ attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, 
     a.packed = p->packed_q;
     a.num_splits = pl.splits;
     a.split_tokens = pl.split_tokens;
+    a.key_ranges = pl.key_ranges;
     a.scale_log2 = scale_log2;
     a.causal = p->causal;
     a.window_left = p->window_enabled ? p->window_left : -1;
@@ -507,7 +550,7 @@ attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, 
     err = attn::launch_decode_gqa(a, stream);
   }
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "split kernel launch: %s", hipGetErrorString(err));
-  if (pl.splits > 1) {
+  if ((phase & kPhaseMerge) && pl.workspace > 0) {
     attn::MergeArgs m{};
     m.o_parts = o_parts;
     m.lse_parts = lse_parts;
@@ -517,6 +560,12 @@ attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, 
     m.o = p->o;
     m.o_bf16 = 1;
     m.lse = p->lse;
+    m.key_ranges = pl.key_ranges;
+    m.seq_lens = p->seq_lens;
+    m.batch = p->batch;
+    m.q_len = p->q_len;
+    m.window_left = p->window_enabled ? p->window_left : -1;
+    m.rows_per_request = p->q_len * p->num_q_heads;
     err = attn::launch_merge(m, stream);
     if (err != hipSuccess) return fail(ATTN_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(err));
   }
@@ -560,18 +609,38 @@ void *scratch_ptr() {
 
 extern "C" {
 
-attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+attn_status_t decode_call(const attn_decode_params *p, hipStream_t stream, int phase) {
   attn_status_t st = validate_decode(p, true);
   if (st != ATTN_OK) return st;
   if (p->batch == 0) return ok();
   const DecodePlan pl = plan_decode(p);
-  if (pl.splits > 1) {
+  if (pl.workspace > 0) {
     if (!p->workspace || p->workspace_bytes < pl.workspace)
       return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", pl.workspace,
                   p->workspace ? p->workspace_bytes : (size_t)0);
     if (!aligned16(p->workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
-  return decode_enqueue(p, pl, p->workspace, stream);
+  return decode_enqueue(p, pl, p->workspace, stream, phase);
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_decode_paged(const attn_decode_params *p, hipStream_t stream) {
+  return decode_call(p, stream, kPhaseBoth);
+}
+
+attn_status_t attn_decode_paged_split(const attn_decode_params *p, hipStream_t stream) {
+  return decode_call(p, stream, kPhaseSplit);
+}
+
+attn_status_t attn_decode_paged_merge(const attn_decode_params *p, hipStream_t stream) {
+  return decode_call(p, stream, kPhaseMerge);
 }
 
 attn_status_t attn_decode_paged_noalloc(const attn_decode_params *p, hipStream_t stream) {
@@ -580,10 +649,10 @@ attn_status_t attn_decode_paged_noalloc(const attn_decode_params *p, hipStream_t
   if (p->batch == 0) return ok();
   const DecodePlan pl = plan_decode(p);
   if (pl.workspace > kStaticScratchBytes)
-    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "%d splits need %zu bytes of partials; the static scratch holds %zu",
-                pl.splits, pl.workspace, kStaticScratchBytes);
+    return fail(ATTN_ERR_WORKSPACE_TOO_SMALL, "the plan needs %zu bytes of partials; the static scratch holds %zu",
+                pl.workspace, kStaticScratchBytes);
   void *ws = nullptr;
-  if (pl.splits > 1 && !(ws = scratch_ptr())) return ATTN_ERR_HIP;
+  if (pl.workspace > 0 && !(ws = scratch_ptr())) return ATTN_ERR_HIP;
   return decode_enqueue(p, pl, ws, stream);
 }
 

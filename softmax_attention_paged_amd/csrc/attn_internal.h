@@ -24,15 +24,25 @@ struct DecodeGqaArgs {
   int32_t group, fold, q_groups, rows;
   int32_t packed;                // rows numbered t * group + g across the q_len tokens
   int32_t num_splits, split_tokens;
+  // > 0: even key ranges instead of per-request splits. The tiles of all
+  // requests, in request order, are cut into min(key_ranges, tiles) ranges
+  // of (almost) equal length, one per group of Hkv * q_groups waves; a
+  // request's piece in range g has partial slot g + b.
+  int32_t key_ranges;
   float scale_log2;              // softmax_scale * log2(e)
   int32_t causal;
   int32_t window_left;           // keys of context before the query block; -1: full history
-  // outputs: either final (num_splits == 1) or partials
+  // outputs: final (one split, or a request inside one key range) or partials
   void *o;                       // bf16 [B, q_len, Hq, D]
   float *lse;                    // optional [B, q_len, Hq]
-  float *o_parts;                // [S, R, D]
-  float *lse_parts;              // [S, R]
+  float *o_parts;                // splits: [S, R, D]; key ranges: [key_ranges + B, q_len * Hq, D]
+  float *lse_parts;              // splits: [S, R]; key ranges: [key_ranges + B, q_len * Hq]
 };
+
+// Key ranges of the GQA decode (gqa_request_tiles in device_common.h counts
+// a request's tiles).
+constexpr int kMaxKeyRanges = 512;      // pieces one row may be merged from
+constexpr int kKeyRangeMaxBatch = 512;  // requests the kernels scan (8 per lane)
 
 // MLA-shaped decode: one latent KV head, K = the 576-wide row, V its first 512.
 struct DecodeMlaArgs {
@@ -67,6 +77,13 @@ struct MergeArgs {
   void *o;                       // [R, Dv]
   int32_t o_bf16;                // 1: bf16 output, 0: fp32
   float *lse;                    // optional [R]
+  // key ranges of the GQA decode (key_ranges > 0): a row's pieces are found
+  // from seq_lens as the split kernel cut them; rows of a request that lies
+  // inside one range are final already and left alone
+  int32_t key_ranges;
+  const int32_t *seq_lens;
+  int32_t batch, q_len, window_left;
+  int32_t rows_per_request;      // q_len * Hq
 };
 
 struct PrefillArgs {

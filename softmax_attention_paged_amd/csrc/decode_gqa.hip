@@ -27,16 +27,26 @@
 //     with ds_read_b64_tr_b16. Two row sums are kept: the rounded P that
 //     multiplied V normalises O (so a constant V comes back exactly), and
 //     the unrounded FP32 P gives the log-sum-exp.
-// With one split the output is bf16 O and the base-2 LSE; otherwise FP32
-// partials (O normalised over the split, LSE of the split) that the merge
-// kernel reduces ("TokenSpeed-MLA", section "Decode performance").
+// A unit that covers its request's whole key range writes bf16 O and the
+// base-2 LSE; otherwise FP32 partials (O normalised over the unit's keys,
+// LSE of those keys) that the merge kernel reduces ("TokenSpeed-MLA",
+// section "Decode performance").
 //
-// A workgroup is one wave and one unit: it walks its split's tiles in order
-// and writes its rows itself (no cross-wave merge; a finished wave frees
-// its slot at once). Workgroups are numbered with the query group, then the
-// KV head, fastest: the units that read the per-head slices of the same
-// token rows ([page, slot, head, dim] stores a token's heads side by side)
-// are dispatched together, which keeps HBM accesses row-local.
+// Which keys a wave walks, one of two plans:
+//   - key ranges (the planner's choice up to 512 requests): the 32-key
+//     tiles of all requests, in request order, are cut into K ranges of
+//     equal length, and range g is walked by Hkv * q_groups waves (one per
+//     KV head and query group); a range that crosses request boundaries
+//     walks one piece per request. Every wave streams the same bytes, so
+//     the launch does not wait for the longest requests' last splits; K
+//     gives two waves per SIMD. The kernel finds its pieces by scanning
+//     seq_lens itself, so the host plan needs no lengths.
+//   - per-request splits (forced split counts, larger batches): one unit
+//     per (request, split).
+// A workgroup is one wave. Workgroups are numbered with the query group,
+// then the KV head, fastest: the units that read the per-head slices of the
+// same token rows ([page, slot, head, dim] stores a token's heads side by
+// side) are dispatched together, which keeps HBM accesses row-local.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -60,9 +70,10 @@ struct GqaGeom {
   static constexpr int kWPEExt = D <= 64 ? 4 : (D <= 128 ? 3 : 1);   // window / packed rows
 };
 
-// Gather one 32-key tile of K (MFMA A layout) or V (linear 16-byte chunks).
-// Keys at or past `end` read slots of an already-valid page and are masked
-// later (K) or zeroed (V); table entries at or past `end` are never read.
+// Gather one 32-key tile of K or V (linear 16-byte chunks). Keys at or past
+// `end` read slots of an already-valid page and are masked later (K) or
+// zeroed (V): skipping those loads (exec-masked) measured 5 % slower per
+// call. Table entries at or past `end` are never read.
 struct TilePages {
   int64_t p0, p1;   // physical pages of keys tok0..tok0+15 and tok0+16..tok0+31
 };
@@ -118,10 +129,11 @@ __device__ __forceinline__ void load_v(const DecodeGqaArgs &a, const __bf16 *vba
 
 // Where a unit's rows live and which keys they see.
 struct UnitRows {
-  int b, kvh, qg, split;
+  int b, kvh, qg;
   int row;          // this lane's row (lane % 16)
   bool row_valid;
   int64_t ridx;     // this lane's row in [B, q_len, Hq]
+  int rr;           // ... and within its request's q_len * Hq rows
   int c0, c1;       // keys of the split any row of the unit sees
   int first;        // first tile of the split the unit walks (tile-aligned, >= c0)
   int begin_max;    // the largest row_begin of the unit's valid rows (wave-uniform)
@@ -129,13 +141,15 @@ struct UnitRows {
   int row_end;      // ... and < row_end are visible to this lane's row
 };
 
+// The unit walks tiles [tile0, tile1) of its request (32-key tiles counted
+// from the request's base: 0, or the tile holding its window's first key).
 template <bool kExt>
-__device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int kvh, int qg, int split, int lane) {
+__device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int kvh, int qg, int tile0, int tile1,
+                                              int lane) {
   UnitRows u;
   u.b = b;
   u.kvh = kvh;
   u.qg = qg;
-  u.split = split;
   u.row = lane & 15;
   const int lk = a.seq_lens[b];
   int t_row, g_row, t_first, t_last;
@@ -173,8 +187,8 @@ __device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int
     unit_begin = max(0, lk - a.q_len - a.window_left + t_first);
     base = max(0, lk - a.q_len - a.window_left) & ~(kGqaTileTokens - 1);
   }
-  u.c0 = base + split * a.split_tokens;
-  u.c1 = min(unit_bound, u.c0 + a.split_tokens);
+  u.c0 = base + tile0 * kGqaTileTokens;
+  u.c1 = min(unit_bound, base + tile1 * kGqaTileTokens);
   u.first = u.c0 + (max(0, unit_begin - u.c0) & ~(kGqaTileTokens - 1));
   u.row_end = min(bound, u.c1);
   u.begin_max = INT32_MIN;   // no row has a lower bound: the mask branch folds away
@@ -184,7 +198,8 @@ __device__ __forceinline__ UnitRows unit_rows(const DecodeGqaArgs &a, int b, int
     for (int off = 32; off >= 1; off >>= 1) bm = max(bm, __shfl_xor(bm, off, 64));
     u.begin_max = __builtin_amdgcn_readfirstlane(bm);
   }
-  u.ridx = ((int64_t)b * a.q_len + t_row) * a.num_q_heads + h_row;
+  u.rr = t_row * a.num_q_heads + h_row;
+  u.ridx = (int64_t)b * a.q_len * a.num_q_heads + u.rr;
   return u;
 }
 
@@ -325,48 +340,38 @@ struct WaveState {
   }
 };
 
-// Rows of an empty unit: LSE -inf; with one split also O = 0.
+// Where a unit's rows go: the final bf16 O and LSE, or FP32 partial rows
+// part_base + rr of o_parts / lse_parts.
+struct UnitOut {
+  bool final_out;
+  int64_t part_base;
+};
+
+// Rows of an empty unit: LSE -inf; if final also O = 0.
 template <int D>
-__device__ __forceinline__ void write_empty(const DecodeGqaArgs &a, const UnitRows &u, int lane) {
+__device__ __forceinline__ void write_empty(const DecodeGqaArgs &a, const UnitRows &u, const UnitOut &out, int lane) {
   if (!u.row_valid) return;
   const int kg = lane >> 4;
-  const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
-  if (a.num_splits == 1) {
+  if (out.final_out) {
     __bf16 *dst = static_cast<__bf16 *>(a.o) + u.ridx * D + 4 * kg;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<u32x2 *>(dst + nb * 16) = u32x2{0u, 0u};
     if (a.lse && kg == 0) a.lse[u.ridx] = kNegInf;
   } else if (kg == 0) {
-    a.lse_parts[(int64_t)u.split * R + u.ridx] = kNegInf;
+    a.lse_parts[out.part_base + u.rr] = kNegInf;
   }
 }
 
-// One wave per workgroup and per unit: blockIdx -> (b, split, KV head, q
-// group), q group fastest, so the units that read the per-head slices of
-// the same token rows are dispatched together. The wave walks its split's
-// tiles in order and writes its rows itself: no cross-wave merge, and a
-// finished wave frees its slot at once.
-//
-// kExt adds what a sliding window or packed query rows need (the
-// lower-bound mask, the packed row mapping); it is a separate instantiation
-// so the plain kernel keeps its registers (at D = 256 it also runs at a
-// lower occupancy than the plain one).
+// One unit: walk tiles [tile0, tile1) of request b for KV head kvh and query
+// group qg, and write its rows.
 template <int D, bool kExt>
-__global__ __launch_bounds__(64, kExt ? GqaGeom<D>::kWPEExt : GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(const DecodeGqaArgs a) {
+__device__ __forceinline__ void run_unit(const DecodeGqaArgs &a, int b, int kvh, int qg, int tile0, int tile1,
+                                         const UnitOut &out, __bf16 *vlds, int lane) {
   using G = GqaGeom<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 vlds[G::kVTile];
-  const int lane = threadIdx.x;
   const int kg = lane >> 4;
-  int unit = blockIdx.x;
-  const int qg = unit % a.q_groups;
-  unit /= a.q_groups;
-  const int kvh = unit % a.num_kv_heads;
-  unit /= a.num_kv_heads;
-  const int split = unit % a.num_splits;
-  const int b = unit / a.num_splits;
-  const UnitRows u = unit_rows<kExt>(a, b, kvh, qg, split, lane);
-  if (u.first >= u.c1) {       // no key of this split is visible to the unit
-    write_empty<D>(a, u, lane);
+  const UnitRows u = unit_rows<kExt>(a, b, kvh, qg, tile0, tile1, lane);
+  if (u.first >= u.c1) {       // no key of this range is visible to the unit
+    write_empty<D>(a, u, out, lane);
     return;
   }
   WaveState<D> st;
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(64, kExt ? GqaGeom<D>::kWPEExt : GqaGeom<D>::kWPE) 
   const float inv = (st.lsum > 0.f) ? 1.f / st.lsum : 0.f;
   const float muse = (st.m == kNegInf) ? 0.f : st.m;
   const float lse2 = (st.lexact > 0.f) ? muse + __log2f(st.lexact) : kNegInf;
-  if (a.num_splits == 1) {
+  if (out.final_out) {
     __bf16 *dst = static_cast<__bf16 *>(a.o) + u.ridx * D + 4 * kg;
 #pragma unroll
     for (int nb = 0; nb < G::kNB; ++nb) {
@@ -391,17 +396,101 @@ __global__ __launch_bounds__(64, kExt ? GqaGeom<D>::kWPEExt : GqaGeom<D>::kWPE) 
     }
     if (a.lse && kg == 0) a.lse[u.ridx] = lse2;
   } else {
-    const int64_t R = (int64_t)a.batch * a.q_len * a.num_q_heads;
-    float *dst = a.o_parts + ((int64_t)split * R + u.ridx) * D + 4 * kg;
+    float *dst = a.o_parts + (out.part_base + u.rr) * D + 4 * kg;
 #pragma unroll
     for (int nb = 0; nb < G::kNB; ++nb) *reinterpret_cast<f32x4 *>(dst + nb * 16) = st.oacc[nb] * inv;
-    if (kg == 0) a.lse_parts[(int64_t)split * R + u.ridx] = lse2;
+    if (kg == 0) a.lse_parts[out.part_base + u.rr] = lse2;
+  }
+}
+
+// One wave per workgroup. Per-request splits: blockIdx -> (b, split, KV
+// head, q group), q group fastest, so the units that read the per-head
+// slices of the same token rows are dispatched together; the wave walks its
+// split's tiles in order and writes its rows itself (no cross-wave merge,
+// a finished wave frees its slot at once).
+//
+// Key ranges: blockIdx -> (range g, KV head, q group). The tiles of all
+// requests, in request order, are cut into ranges of equal length ("Writing
+// Page Attention with PyPTO", section 1.3: tasks of equal size keep every
+// core busy to the end), so every wave of the launch streams the same
+// number of bytes and the launch ends when its waves do, not when its
+// longest requests do. A range that crosses request boundaries walks one
+// piece per request; a request that lies inside one range is written
+// final, the others as partial rows g + b that the merge combines. All
+// waves of a range read the same token rows at the same time.
+//
+// kExt adds what a sliding window or packed query rows need (the
+// lower-bound mask, the packed row mapping); it is a separate instantiation
+// so the plain kernel keeps its registers (at D = 256 it also runs at a
+// lower occupancy than the plain one).
+template <int D, bool kExt>
+__global__ __launch_bounds__(64, kExt ? GqaGeom<D>::kWPEExt : GqaGeom<D>::kWPE) void decode_gqa_wave_kernel(const DecodeGqaArgs a) {
+  using G = GqaGeom<D>;
+  __shared__ __attribute__((aligned(16))) __bf16 vlds[G::kVTile];
+  const int lane = threadIdx.x;
+  int unit = blockIdx.x;
+  const int qg = unit % a.q_groups;
+  unit /= a.q_groups;
+  const int kvh = unit % a.num_kv_heads;
+  unit /= a.num_kv_heads;
+  // The wave walks pieces (b, [s0, s1)) of the tiles [t_lo, t_hi): with
+  // splits one piece, tiles [split L, split L + L) of request b; with key
+  // ranges every request its range meets.
+  const int wl = kExt ? a.window_left : -1;
+  const int64_t rows_req = (int64_t)a.q_len * a.num_q_heads;
+  const bool ranges_mode = a.key_ranges > 0;
+  int g = 0, split = 0, b = 0, p = 0, t_lo, t_hi;
+  if (!ranges_mode) {
+    split = unit % a.num_splits;
+    b = unit / a.num_splits;
+    const int st = a.split_tokens / kGqaTileTokens;
+    t_lo = split * st;
+    t_hi = t_lo + st;
+  } else {
+    g = unit;
+    const BatchTiles bt = batch_tiles(a.seq_lens, a.batch, a.q_len, wl, 0, lane);
+    const int total = __builtin_amdgcn_readfirstlane(bt.total);
+    const int ranges = min(a.key_ranges, total);
+    if (g >= ranges) return;
+    t_lo = key_range_start(g, ranges, total);
+    t_hi = key_range_start(g + 1, ranges, total);
+    // the request holding tile t_lo, and its first tile
+    int carry = 0;
+#pragma unroll
+    for (int k = 0; k < kKeyRangeMaxBatch / 64; ++k) {
+      int incl = bt.n[k];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int up = __shfl_up(incl, off, 64);
+        incl += (lane >= off) ? up : 0;
+      }
+      incl += carry;
+      const uint64_t hit = __ballot(incl > t_lo && lane + 64 * k < a.batch);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        b = 64 * k + l;
+        p = __shfl(incl - bt.n[k], l, 64);
+        break;
+      }
+      carry = __shfl(incl, 63, 64);
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    p = __builtin_amdgcn_readfirstlane(p);
+  }
+  while (p < t_hi) {
+    const int n = ranges_mode ? gqa_request_tiles(a.seq_lens[b], a.q_len, wl) : t_hi;
+    const int s0 = max(t_lo, p) - p, s1 = min(t_hi, p + n) - p;
+    const UnitOut out = ranges_mode ? UnitOut{s0 == 0 && s1 == n, (int64_t)(g + b) * rows_req}
+                                    : UnitOut{a.num_splits == 1, ((int64_t)split * a.batch + b) * rows_req};
+    run_unit<D, kExt>(a, b, kvh, qg, s0, s1, out, vlds, lane);
+    p += n;
+    ++b;
   }
 }
 
 template <int D>
 hipError_t launch_d(const DecodeGqaArgs &a, hipStream_t stream) {
-  const int64_t units = (int64_t)a.batch * a.num_splits * a.num_kv_heads * a.q_groups;
+  const int64_t units = (int64_t)(a.key_ranges > 0 ? a.key_ranges : a.batch * a.num_splits) * a.num_kv_heads * a.q_groups;
   if (a.packed || a.window_left >= 0)
     hipLaunchKernelGGL((decode_gqa_wave_kernel<D, true>), dim3((unsigned)units), dim3(64), 0, stream, a);
   else

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_internal.h"
+
 namespace attn {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -108,6 +110,51 @@ __device__ __forceinline__ float half_sum(float x) {
 template <class T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
+}
+
+// Key ranges of the GQA decode: the 32-key tiles a request's walk covers,
+// [base, seq_len) with base the tile-aligned start of its window (0 without
+// one), and at least one, so that a request without keys still belongs to a
+// range whose waves write its empty rows. The split kernel and the merge
+// both cut the batch with it.
+__device__ __forceinline__ int gqa_request_tiles(int lk, int q_len, int window_left) {
+  const int base = window_left >= 0 ? (max(0, lk - q_len - window_left) & ~31) : 0;
+  return max(1, (lk - base + 31) >> 5);
+}
+
+// Tiles of every request, lane-strided (request lane + 64 k), and their sum
+// over the batch (at most kKeyRangeMaxBatch requests); `below` sums only the
+// requests before `b`.
+struct BatchTiles {
+  int n[kKeyRangeMaxBatch / 64];
+  int total;
+  int below;
+};
+
+__device__ __forceinline__ BatchTiles batch_tiles(const int32_t *seq_lens, int batch, int q_len, int window_left,
+                                                  int b, int lane) {
+  BatchTiles t;
+  int sum = 0, below = 0;
+#pragma unroll
+  for (int k = 0; k < kKeyRangeMaxBatch / 64; ++k) {
+    const int r = lane + 64 * k;
+    t.n[k] = (r < batch) ? gqa_request_tiles(seq_lens[r], q_len, window_left) : 0;
+    sum += t.n[k];
+    below += (r < b) ? t.n[k] : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sum += __shfl_xor(sum, off, 64);
+    below += __shfl_xor(below, off, 64);
+  }
+  t.total = sum;
+  t.below = below;
+  return t;
+}
+
+// Key range g of K over T tiles: [g T / K, (g + 1) T / K).
+__device__ __forceinline__ int key_range_start(int g, int ranges, int total) {
+  return (int)((int64_t)g * total / ranges);
 }
 
 // Exact e4m3 -> bf16 of 16 codes: one hardware convert per pair of codes, at

@@ -9,13 +9,20 @@
 // FP32 partials).
 //
 // One wave per row: the lanes read the split LSEs once and reduce M and the
-// weights with wave shuffles. The row's float4 chunks are spread over the
-// lanes; when they do not fill the wave, lane groups take every G-th split
-// and are summed with shuffles at the end. A lane holding CPL chunks of a
-// row reads 16 / CPL partial rows at once, so up to 16 float4 loads per lane
-// are in flight together (a 22-split decode of 128-wide rows is read in one
-// batch: one round trip for the LSEs, one for the partials). Splits with
-// weight 0 (lse = -inf, an empty split) are never read.
+// weights with wave shuffles; the weights then go through the wave's LDS
+// row to the lanes that scale each partial. The row's float4 chunks are
+// spread over the lanes; when they do not fill the wave, lane groups take
+// every G-th split and are summed with shuffles at the end. A lane holding
+// CPL chunks of a row reads 16 / CPL partial rows at once, so up to 16
+// float4 loads per lane are in flight together (a 22-split decode of
+// 128-wide rows is read in one batch: one round trip for the LSEs, one for
+// the partials). Splits with weight 0 (lse = -inf, an empty split) are
+// never read.
+//
+// The GQA decode's key ranges: a row's pieces are the ranges its request
+// meets, found from seq_lens as the split kernel cut them (one round trip);
+// their first batch of partial rows is read together with their LSEs (one
+// more), since only a causal row's last piece can be empty.
 
 #include "attn_internal.h"
 #include "device_common.h"
@@ -26,21 +33,68 @@ namespace {
 constexpr int kMergeWaves = 4;
 constexpr int kLoadsInFlight = 16;     // float4 loads per lane issued together
 
-// CPL: float4 chunks per lane (1, 2 or 4; head_dim_v <= 1024).
-template <int CPL>
+// CPL: float4 chunks per lane (1, 2 or 4; head_dim_v <= 1024). kRanges:
+// the pieces of the GQA decode's key ranges (partial i of row r of request
+// b at slot (g_first + b + i) * q_len * Hq + r, found from seq_lens as the
+// split kernel cut the batch); otherwise splits (partial i of row r at
+// i * num_rows + r).
+template <int CPL, bool kRanges>
 __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
   constexpr int kBatch = kLoadsInFlight / CPL;   // partial rows read together
+  constexpr int kMax = kRanges ? kMaxKeyRanges : kMaxSplits;
   const int lane = threadIdx.x & 63;
   const int64_t rowi = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   if (rowi >= a.num_rows) return;
 
+  int count = a.num_splits;
+  int64_t base = rowi, stride = a.num_rows;
+  if constexpr (kRanges) {
+    const int b = (int)(rowi / a.rows_per_request);
+    const int rr = (int)(rowi % a.rows_per_request);
+    const BatchTiles bt = batch_tiles(a.seq_lens, a.batch, a.q_len, a.window_left, b, lane);
+    const int ranges = min(a.key_ranges, bt.total);
+    const int n = gqa_request_tiles(a.seq_lens[b], a.q_len, a.window_left);
+    // the ranges holding the request's first and last tile
+    const int g_first = (int)(((int64_t)(bt.below + 1) * ranges - 1) / bt.total);
+    const int g_last = (int)(((int64_t)(bt.below + n) * ranges - 1) / bt.total);
+    if (g_first == g_last) return;            // inside one range: written final by the split kernel
+    count = g_last - g_first + 1;
+    base = (int64_t)(g_first + b) * a.rows_per_request + rr;
+    stride = a.rows_per_request;
+  }
+
+  // lane layout: G groups of 64 / G lanes; group g sums splits g, g + G, ...
+  const int nchunks = a.head_dim_v >> 2;
+  const int G = nchunks >= 64 ? 1 : (nchunks >= 32 ? 2 : 4);
+  const int glanes = 64 / G;
+  const int g = lane / glanes, gl = lane % glanes;
+
+  // Key ranges: every piece but a causal row's empty last one holds a
+  // partial, so the first batch of partial rows is read together with the
+  // LSEs (one round trip instead of two); an empty piece's stale row is
+  // selected away by its zero weight below.
+  f32x4 first[kRanges ? kBatch : 1][CPL];
+  if constexpr (kRanges) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = u * G + g;
+      const float *src = a.o_parts + (base + sp * stride) * a.head_dim_v;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int c = gl + glanes * k;
+        first[u][k] = (sp < count && c < nchunks) ? *reinterpret_cast<const f32x4 *>(src + 4 * c)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+
   // split weights: lane holds splits lane, lane + 64, ...
-  float lse_r[kMaxSplits / 64];
+  float lse_r[kMax / 64];
   float mmax = kNegInf;
 #pragma unroll
-  for (int j = 0; j < kMaxSplits / 64; ++j) {
+  for (int j = 0; j < kMax / 64; ++j) {
     const int s = lane + 64 * j;
-    lse_r[j] = (s < a.num_splits) ? a.lse_parts[(int64_t)s * a.num_rows + rowi] : kNegInf;
+    lse_r[j] = (s < count) ? a.lse_parts[base + s * stride] : kNegInf;
     mmax = fmaxf(mmax, lse_r[j]);
   }
 #pragma unroll
@@ -48,42 +102,53 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(const MergeArgs a) {
   const float muse = (mmax == kNegInf) ? 0.f : mmax;
   float wsum = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxSplits / 64; ++j) {
+  for (int j = 0; j < kMax / 64; ++j) {
     lse_r[j] = exp2_fast(lse_r[j] - muse);   // weight; 0 for empty splits
     wsum += lse_r[j];
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += wave_shfl_xor(wsum, off);
 
-  // lane layout: G groups of 64 / G lanes; group g sums splits g, g + G, ...
-  const int nchunks = a.head_dim_v >> 2;
-  const int G = nchunks >= 64 ? 1 : (nchunks >= 32 ? 2 : 4);
-  const int glanes = 64 / G;
-  const int g = lane / glanes, gl = lane % glanes;
   f32x4 acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = 0; s0 < a.num_splits; s0 += kBatch * G) {
+  // The weights go to the wave's LDS row, where each lane group reads those
+  // of its splits (LDS operations of one wave execute in order).
+  __shared__ float wts[kMergeWaves][kMax];
+  float *wrow = wts[threadIdx.x >> 6];
+#pragma unroll
+  for (int j = 0; j < kMax / 64; ++j) wrow[lane + 64 * j] = lse_r[j];
+  asm volatile("" ::: "memory");
+  // the weight of split sg + g of this lane's group
+  auto weight = [&](int sg) { return (sg + g < count) ? wrow[sg + g] : 0.f; };
+  int s_begin = 0;
+  if constexpr (kRanges) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float wu = weight(u * G);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[k][e] += (wu != 0.f) ? wu * first[u][k][e] : 0.f;
+    }
+    s_begin = kBatch * G;
+  }
+  for (int s0 = s_begin; s0 < count; s0 += kBatch * G) {
     float w[kBatch];
     f32x4 v[kBatch][CPL];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int sg = s0 + u * G;            // this batch slot's split for group 0; group g adds g
-      float wu = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {         // the weight of split sg + g, from its lane
-        const int sq = sg + q;
-        const float wq = (sq < a.num_splits) ? __shfl(lse_r[(sq >> 6) & (kMaxSplits / 64 - 1)], sq & 63, 64) : 0.f;
-        if (q == g) wu = wq;
-      }
+      const float wu = weight(sg);
       w[u] = wu;
       const int s = sg + g;
-      const float *src = a.o_parts + ((int64_t)s * a.num_rows + rowi) * a.head_dim_v;
+      const float *src = a.o_parts + (base + s * stride) * a.head_dim_v;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int c = gl + glanes * k;
-        v[u][k] = (wu != 0.f && c < nchunks) ? *reinterpret_cast<const f32x4 *>(src + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[u][k] = (wu != 0.f && c < nchunks) ? *reinterpret_cast<const f32x4 *>(src + 4 * c)
+                                             : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
@@ -128,12 +193,20 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
   const int glanes = 64 / (nchunks >= 64 ? 1 : (nchunks >= 32 ? 2 : 4));
   const int cpl = (nchunks + glanes - 1) / glanes;
   const dim3 grid((unsigned)blocks), block(64 * kMergeWaves);
-  if (cpl <= 1)
-    hipLaunchKernelGGL(merge_lse_kernel<1>, grid, block, 0, stream, a);
-  else if (cpl == 2)
-    hipLaunchKernelGGL(merge_lse_kernel<2>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_lse_kernel<4>, grid, block, 0, stream, a);
+  if (a.key_ranges > 0) {
+    if (cpl <= 1)
+      hipLaunchKernelGGL((merge_lse_kernel<1, true>), grid, block, 0, stream, a);
+    else if (cpl == 2)
+      hipLaunchKernelGGL((merge_lse_kernel<2, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((merge_lse_kernel<4, true>), grid, block, 0, stream, a);
+  } else if (cpl <= 1) {
+    hipLaunchKernelGGL((merge_lse_kernel<1, false>), grid, block, 0, stream, a);
+  } else if (cpl == 2) {
+    hipLaunchKernelGGL((merge_lse_kernel<2, false>), grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((merge_lse_kernel<4, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

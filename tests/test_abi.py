@@ -83,7 +83,7 @@ def test_ctypes_mirrors_match_the_c_compiler_layout(tmp_path):
 def test_struct_sizes_match_c_layout():
     # ctypes mirrors must match the C layout (checked against offsets the C
     # compiler would use: pointers and int64 are 8-aligned, int32/float 4).
-    assert ctypes.sizeof(_ffi.DecodePlanInfo) == 40
+    assert ctypes.sizeof(_ffi.DecodePlanInfo) == 48
     assert _ffi.DecodeParams.workspace.offset % 8 == 0
     assert _ffi.PrefillParams.lse.offset % 8 == 0
 
@@ -281,20 +281,20 @@ def test_latent_planner_fills_whole_rounds(batch, splits):
 
 
 @pytest.mark.parametrize("batch,max_len,total,hkv,d", [
-    (64, 8192, 256194, 8, 128), (64, 8192, 64 * 8192, 8, 128), (8, 65536, 300000, 8, 128),
-    (17, 513, 2000, 2, 64), (200, 4096, 400000, 8, 256), (64, 8192, 1000, 8, 128)])
-def test_gqa_planner_with_total_keys_fits_one_round(batch, max_len, total, hkv, d):
-    # a request walking n keys has at most n / L + 1 units per KV head, so the
-    # plan must keep (total / L + batch) * Hkv within the resident waves
-    # (12 per CU at D 128, 16 at D 64, 8 at D 256), unless even one split per
-    # request does not fit
+    (600, 8192, 2_500_000, 8, 128), (600, 4096, 600 * 4096, 8, 128), (700, 513, 2000 * 4, 2, 64),
+    (520, 4096, 400000, 8, 256), (600, 8192, 1000, 8, 128)])
+def test_gqa_split_planner_with_total_keys_fits_one_round(batch, max_len, total, hkv, d):
+    # above 512 requests the GQA plan splits each request: a request walking
+    # n keys has at most n / L + 1 units per KV head, so the plan must keep
+    # (total / L + batch) * Hkv within the resident waves (12 per CU at D 128,
+    # 16 at D 64, 8 at D 256), unless even one split per request does not fit
     p = decode_params(num_q_heads=hkv * 4, num_kv_heads=hkv, head_dim_qk=d, head_dim_v=d, q_len=1, batch=batch,
                       max_seq_len=max_len, page_size=128, num_pages=(max_len // 128 + 1) * batch,
                       block_table_stride=max_len // 128 + 1, k_stride_page=128 * hkv * d, k_stride_tok=hkv * d,
                       k_stride_head=d, v_stride_page=128 * hkv * d, v_stride_tok=hkv * d, v_stride_head=d)
     p.total_kv_tokens = total
     st, info = plan(p)
-    assert st == 0
+    assert st == 0 and info.key_ranges == 0
     L = info.split_tokens
     assert L % 32 == 0 and info.num_splits * L >= max_len and (info.num_splits - 1) * L < max_len
     slots = 256 * {64: 16, 128: 12, 256: 8}[d]
@@ -303,6 +303,34 @@ def test_gqa_planner_with_total_keys_fits_one_round(batch, max_len, total, hkv, 
         assert L >= 256 or info.num_splits == 1
     p.total_kv_tokens = -1
     assert plan(p)[0] == _ffi.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("batch,max_len,total,hkv,d,q_len", [
+    (64, 8192, 256194, 8, 128, 1), (64, 8192, 0, 8, 128, 1), (8, 65536, 300000, 8, 128, 1),
+    (17, 513, 2000, 2, 64, 1), (200, 4096, 400000, 8, 256, 1), (64, 8192, 1000, 8, 128, 1),
+    (512, 100, 0, 1, 64, 1), (3, 64, 0, 2, 128, 4), (1, 1, 0, 8, 128, 1)])
+def test_gqa_key_range_plan(batch, max_len, total, hkv, d, q_len):
+    # up to 512 requests the GQA plan cuts the batch's 32-key tiles into K
+    # equal ranges: K = 8 waves per CU / (Hkv q_groups), at most 512, and
+    # at most one per 8 tiles of the batch (bounded by max_seq_len, or by the
+    # host total when given); partial slots K + batch per row of a request
+    hq = hkv * 4
+    p = decode_params(num_q_heads=hq, num_kv_heads=hkv, head_dim_qk=d, head_dim_v=d, q_len=q_len, batch=batch,
+                      max_seq_len=max_len, page_size=128, num_pages=(max_len // 128 + 1) * batch,
+                      block_table_stride=max_len // 128 + 1, k_stride_page=128 * hkv * d, k_stride_tok=hkv * d,
+                      k_stride_head=d, v_stride_page=128 * hkv * d, v_stride_tok=hkv * d, v_stride_head=d)
+    p.total_kv_tokens = total
+    st, info = plan(p)
+    assert st == 0
+    slots = 256 * 8                  # two waves per SIMD stream the key ranges
+    upper = batch * (-(-max(max_len, 1) // 32) + 1)
+    if total:
+        upper = min(upper, -(-total // 32) + batch)
+    k = max(1, min(slots // (hkv * info.q_groups), 512, -(-upper // 8)))
+    assert info.key_ranges == k
+    assert info.num_splits == 0 and info.split_tokens == 0
+    assert info.num_units == k * hkv * info.q_groups
+    assert info.workspace_bytes == (0 if k == 1 else (k + batch) * q_len * hq * (d + 1) * 4)
 
 
 def test_gqa_plan_folds_heads_and_tokens_into_16_rows():
@@ -316,14 +344,15 @@ def test_gqa_plan_folds_heads_and_tokens_into_16_rows():
 
 
 def test_split_plan_is_nonempty_and_tile_aligned():
+    # per-request splits (above 512 requests): whole tiles, every split non-empty
     for max_len in (1, 31, 100, 1000, 8192, 81920):
         pages = -(-max_len // 16)
-        st, info = plan(decode_params(max_seq_len=max_len, num_pages=pages, block_table_stride=pages))
-        assert st == 0
+        st, info = plan(decode_params(batch=513, max_seq_len=max_len, num_pages=pages, block_table_stride=pages))
+        assert st == 0 and info.key_ranges == 0
         assert info.split_tokens % 32 == 0
         assert (info.num_splits - 1) * info.split_tokens < max(max_len, 1) <= info.num_splits * info.split_tokens
-        assert info.num_units == 2 * 2 * info.num_splits
-        assert info.workspace_bytes == (0 if info.num_splits == 1 else info.num_splits * 16 * 129 * 4)
+        assert info.num_units == 513 * 2 * info.num_splits
+        assert info.workspace_bytes == (0 if info.num_splits == 1 else info.num_splits * 513 * 8 * 129 * 4)
 
 
 def test_qwen3_14b_decode_plan():
@@ -334,7 +363,9 @@ def test_qwen3_14b_decode_plan():
     st, info = plan(p)
     assert st == 0
     assert (info.group, info.fold, info.rows_per_unit) == (5, 1, 5)
-    assert info.num_units == 64 * 8 * info.num_splits and info.num_splits > 1
+    # 2048 streaming waves (256 CUs x 8) over 8 KV heads: 256 key ranges
+    assert info.key_ranges == 256 and info.num_units == 2048
+    assert info.workspace_bytes == (256 + 64) * 40 * 129 * 4
 
 
 def test_packed_q_must_be_a_flag():
@@ -381,9 +412,14 @@ def test_window_plans_splits_over_the_window():
     assert st == st2 == 0
     assert full.num_splits > 1
     assert win.num_splits == 1 and win.split_tokens >= 100 + 4 and win.split_tokens % 32 == 0
-    st, g = plan(decode_params(max_seq_len=256, num_pages=16, block_table_stride=16, window_enabled=1,
+    st, g = plan(decode_params(batch=513, max_seq_len=256, num_pages=16, block_table_stride=16, window_enabled=1,
                                window_left=1000))
     assert st == 0 and g.num_splits * g.split_tokens >= 256     # a window wider than the history
+    # key ranges: the tile bound per request follows the window (100 + 4 + 31
+    # keys: 5 tiles + 1 of alignment), so K is capped at one per 8 of them
+    st, kr = plan(decode_params(batch=4, max_seq_len=8192, num_pages=512, block_table_stride=512, q_len=4,
+                                window_enabled=1, window_left=100))
+    assert st == 0 and kr.key_ranges == -(-4 * (-(-(100 + 4 + 31) // 32) + 1) // 8)
 
 
 

@@ -176,6 +176,104 @@ def test_qwen3_14b_decode_every_row_full_size(hint):
     print(res)
 
 
+# ------------------------------------------------------------- key ranges --
+
+def _lens(rng, n, lo, hi, zeros=0.0):
+    return [0 if rng.random() < zeros else int(rng.integers(lo, hi + 1)) for _ in range(n)]
+
+
+_KR = np.random.default_rng(5)
+_KEY_RANGE_CASES = {
+    # one request cut into 33 pieces (K = 257 tiles / 8)
+    "one_long_request": dict(batch=1, q_len=1, hq=8, hkv=2, d=128, page_size=16, seq_lens=[8191]),
+    # 300 short requests, a fifth of them empty: ranges of ~3 tiles hold
+    # several whole requests each (written final) and cut others
+    "many_short_with_empty": dict(batch=300, q_len=1, hq=8, hkv=2, d=64, page_size=16,
+                                  seq_lens=_lens(_KR, 300, 1, 40, zeros=0.2)),
+    # two query groups per KV head (G 8, F 2), causal: the last tile of a
+    # request is empty for the first query group's rows
+    "causal_q4_two_groups": dict(batch=5, q_len=4, hq=16, hkv=2, d=128, page_size=16, causal=True,
+                                 seq_lens=[1, 2, 3000, 33, 1500]),
+    # the largest batch the kernels scan, and one past it (per-request splits)
+    "batch_512": dict(batch=512, q_len=1, hq=4, hkv=1, d=64, page_size=16, seq_lens=_lens(_KR, 512, 0, 100)),
+    "batch_513_splits": dict(batch=513, q_len=1, hq=4, hkv=1, d=64, page_size=16,
+                             seq_lens=_lens(_KR, 513, 0, 100)),
+    "d256_ragged": dict(batch=9, q_len=1, hq=16, hkv=4, d=256, page_size=64,
+                        seq_lens=[0, 4096, 17, 2000, 31, 32, 33, 700, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(_KEY_RANGE_CASES))
+def test_key_ranges_match_oracle(name):
+    kw = dict(_KEY_RANGE_CASES[name])
+    d = kw.pop("d")
+    case = inputs.decode_case(dv=d, d=d, seed=300 + len(name), layout="noncontiguous", **kw)
+    c = case.to(DEV)
+    plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                             max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal))
+    print(name, "key ranges", plan["key_ranges"], "splits", plan["num_splits"], flush=True)
+    assert (plan["key_ranges"] > 0) == (kw["batch"] <= 512)
+    res = _check(case)
+    res["rows_checked"] = int(np.prod(case.q.shape[:3]))
+    print(res)
+
+
+def test_key_ranges_constant_v_and_single_key():
+    # the exact-value invariants through the key-range plan: constant V comes
+    # back bitwise (requests cut into pieces included), a single key's O is its
+    # V row bitwise
+    lens = [1, 50, 5000]
+    case = inputs.decode_case(batch=3, q_len=1, hq=8, hkv=2, d=128, dv=128, page_size=16,
+                              seq_lens=lens, seed=27, q_mult=4.0)
+    vc = case.v_cache.clone()
+    bt = case.block_table
+    const = torch.randn(3, 2, 128).to(torch.bfloat16)
+    for b, n in enumerate(lens):
+        for j in range(n):
+            vc[int(bt[b, j // 16]), j % 16] = const[b]
+    case.v_cache = vc
+    c = case.to(DEV)
+    plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                             max_seq_len=c.max_seq_len, softmax_scale=c.scale))
+    assert plan["key_ranges"] > 1
+    out, lse = _run(case)
+    for b in range(3):
+        for h in range(8):
+            assert torch.equal(out[b, 0, h].view(torch.int16), const[b, h // 4].view(torch.int16))
+    p0 = int(bt[0, 0])
+    for h in range(8):
+        assert torch.equal(out[0, 0, h].view(torch.int16), vc[p0, 0, h // 4].view(torch.int16))
+
+
+@pytest.mark.parametrize("plan", ["key_ranges", "splits", "latent"])
+def test_split_and_merge_phases_equal_the_whole_call(plan):
+    # attn_decode_paged_split then attn_decode_paged_merge, with the same
+    # out, lse and workspace, give attn_decode_paged's result bit for bit
+    if plan == "latent":
+        case = inputs.decode_case(batch=3, q_len=2, hq=32, hkv=1, d=576, dv=512, page_size=64, latent=True,
+                                  seq_lens=[3000, 1, 900], seed=28, scale=0.07216882)
+    else:
+        case = inputs.decode_case(batch=6, q_len=1, hq=40, hkv=8, d=128, dv=128, page_size=128,
+                                  seq_lens=[4000, 0, 300, 8000, 77, 2500], seed=29)
+    c = case.to(DEV)
+    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale, head_dim_v=c.head_dim_v,
+              num_splits=3 if plan != "key_ranges" else 0)
+    args = (c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens)
+    p = sap.decode_params(*args, **kw)
+    info = sap.decode_plan(p)
+    assert (info["key_ranges"] > 0) == (plan == "key_ranges") and info["workspace_bytes"] > 0
+    ws = torch.empty(info["workspace_bytes"], dtype=torch.uint8, device=DEV)
+    ref, lref = sap.decode_paged(*args, workspace=ws, return_lse=True, **kw)
+    out = torch.full_like(ref, float("nan"))
+    lse = torch.full_like(lref, float("nan"))
+    ws.fill_(0xFF)                                   # the split phase must write what the merge reads
+    sap.decode_paged(*args, workspace=ws, out=out, lse=lse, phase="split", **kw)
+    sap.decode_paged(*args, workspace=ws, out=out, lse=lse, phase="merge", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lref.view(torch.int32))
+
+
 # ------------------------------------------------------------------ merge --
 
 @pytest.mark.parametrize("s,r,dv", [(1, 5, 128), (3, 100, 128), (16, 2560, 128), (7, 33, 512), (64, 10, 64)])

@@ -45,7 +45,7 @@ def _check(case, tol=TOL_BF16, **kw):
 @pytest.mark.gpu
 def test_noalloc_gqa_decode_two_calls_second_smaller():
     # first: the Qwen3-14B-shaped decode planned with the host's total of keys
-    # (10 splits: 13 MB of partials); second: a smaller decode (3 splits)
+    # (256 key ranges: 6.6 MB of partials); second: a smaller decode (3 splits)
     big = inputs.qwen3_14b_decode()
     print("call 1", big.name, flush=True)
     print(_check(big, total_kv_tokens=int(big.seq_lens.sum())))
