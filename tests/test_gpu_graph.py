@@ -38,12 +38,17 @@ def _capture(fn):
     return graph
 
 
-def test_decode_graph_replays_match_eager():
+@pytest.mark.parametrize("num_splits", [3, 0])
+def test_decode_graph_replays_match_eager(num_splits):
+    # 3: per-request splits and the merge kernel; 0: key ranges, merged in
+    # the split kernel through arrival counters that every replay (same
+    # captured epoch) must find reset by the previous one
     case = inputs.decode_case(batch=6, q_len=2, hq=8, hkv=2, d=128, dv=128, page_size=16,
                               seq_lens=[1, 40, 300, 511, 777, 64], seed=901, causal=True)
     c = case.to(DEV)
-    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=True, num_splits=3)
+    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=True, num_splits=num_splits)
     plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, **kw))
+    assert (plan["key_ranges"] > 1) == (num_splits == 0)
     ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=DEV)
     out = torch.empty((6, 2, 8, 128), dtype=torch.bfloat16, device=DEV)
     q = c.q.clone()
