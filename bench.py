@@ -64,10 +64,12 @@ TRAFFIC_KERNELS = {
                                  ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
     "single_chunk_prefill_80k": ("prefill_pp8_kernel<128, 1>",
                                  ["prefill.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
-    "mla_decode_80k_bf16": ("decode_mla_kernel<false, false>",
+    "mla_decode_80k_bf16": ("decode_mla_kernel<false, false, false>",
                             ["decode_mla.hip", "device_common.h", "attn_internal.h"]),
-    "mla_decode_80k_fp8_e4m3": ("decode_mla_kernel<true, false>",
+    "mla_decode_80k_fp8_e4m3": ("decode_mla_kernel<true, false, false>",
                                 ["decode_mla.hip", "device_common.h", "attn_internal.h"]),
+    "mla_decode_80k_fp8_q": ("decode_mla_kernel<true, true, false>",
+                             ["decode_mla.hip", "device_common.h", "attn_internal.h"]),
     "fp8_mla_prefill_8k": ("prefill_fp8_kernel",
                            ["prefill_fp8.hip", "prefill_unit.h", "device_common.h", "attn_internal.h"]),
 }
@@ -448,15 +450,19 @@ def secondary_prefill(key: str, name_fn, steps: int, kv_splits: int = 0) -> dict
                          "algorithmic_bytes_per_launch": alg_bytes}}
 
 
-def secondary_mla(kv_dtype: str, steps: int) -> dict:
+def secondary_mla(kv_dtype: str, steps: int, q_dtype: str = "bf16") -> dict:
+    """The 80K MLA-shaped decode. bf16 q runs both products on the bf16
+    MFMA; with fp8 q (and fp8 KV) QK runs on the FP8 MFMA and P.V on bf16,
+    so the roof is the two peaks blended by each part's flops."""
     import torch
     import softmax_attention_paged_amd as sap
     from softmax_attention_paged_amd import inputs
-    case = inputs.mla_decode(kv_dtype=kv_dtype)
+    case = inputs.mla_decode(kv_dtype=kv_dtype, q_dtype=q_dtype)
     c = case.to("cuda:0")
     b_n, q_len, hq, dqk = case.q.shape
     kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal, head_dim_v=512,
-              kv_dtype=None if kv_dtype == "bf16" else kv_dtype, k_scale=c.kv_scale, v_scale=c.kv_scale)
+              kv_dtype=None if kv_dtype == "bf16" else kv_dtype, k_scale=c.kv_scale, v_scale=c.kv_scale,
+              q_scale=None if q_dtype == "bf16" else c.q_scale)
     plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, None, c.block_table, c.seq_lens, **kw))
     ws = torch.empty(plan["workspace_bytes"] + 16, dtype=torch.uint8, device=c.q.device)
     out = torch.empty((b_n, q_len, hq, 512), dtype=torch.bfloat16, device=c.q.device)
@@ -464,17 +470,21 @@ def secondary_mla(kv_dtype: str, steps: int) -> dict:
     ms = time_settled(fn, steps, torch.cuda.current_stream())
     lens = case.seq_lens.tolist()
     pairs = hq * sum(min(lk, max(0, lk - q_len + t + 1)) if case.causal else lk for lk in lens for t in range(q_len))
-    flops = pairs * 2 * (dqk + 512)
+    qk, pv = pairs * 2 * dqk, pairs * 2 * 512
+    flops = qk + pv
     tf = flops / (ms * 1e-3) / 1e12
-    peak = BF16_PEAK_TFLOPS   # the kernel runs bf16 MFMA for both KV formats
-    traffic = load_traffic(f"mla_decode_80k_{kv_dtype}")
+    if q_dtype == "bf16":
+        peak = BF16_PEAK_TFLOPS   # bf16 MFMA for both products (fp8 KV is widened to bf16)
+    else:
+        peak = flops / (qk / FP8_PEAK_TFLOPS + pv / BF16_PEAK_TFLOPS)
+    traffic = load_traffic(f"mla_decode_80k_{kv_dtype}" if q_dtype == "bf16" else "mla_decode_80k_fp8_q")
     return {"workload": case.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
             "kv_GB/s": round(case.kv_read_bytes() / (ms * 1e-3) / 1e9, 1), "num_splits": plan["num_splits"],
             "roofline": {"bound": "mfma", "kernel": "decode_mla_kernel + merge", "achieved": round(tf, 1),
                          "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
                          "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                         "algorithmic_bytes_per_launch": case.kv_read_bytes() + case.q.numel() * 2 +
-                         b_n * q_len * hq * (512 * 2 + 4)}}
+                         "algorithmic_bytes_per_launch": case.kv_read_bytes() +
+                         case.q.numel() * case.q.element_size() + b_n * q_len * hq * (512 * 2 + 4)}}
 
 
 def secondary_prefill_fp8(steps: int) -> dict:
@@ -589,7 +599,7 @@ def main() -> int:
                     help="time one workload alone (for profiling): qwen3_14b_decode (the main line), "
                          "dense_causal_prefill_d128, "
                          "dense_causal_prefill_d256, ragged_paged_prefill_80k, single_chunk_prefill_80k, mla_decode_80k_bf16, "
-                         "mla_decode_80k_fp8_e4m3")
+                         "mla_decode_80k_fp8_e4m3, mla_decode_80k_fp8_q")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (reference for HBM counters)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -634,6 +644,7 @@ def main() -> int:
             "single_chunk_prefill_80k", inputs.single_chunk_prefill, steps, args.prefill_kv_splits),
         "mla_decode_80k_bf16": lambda steps: secondary_mla("bf16", steps),
         "mla_decode_80k_fp8_e4m3": lambda steps: secondary_mla("fp8_e4m3", steps),
+        "mla_decode_80k_fp8_q": lambda steps: secondary_mla("fp8_e4m3", steps, "fp8_e4m3"),
         "fp8_mla_prefill_8k": secondary_prefill_fp8,
         "mla_kv_pack_fp8_8k": secondary_mla_pack,
         "cache_append_8k": secondary_append,

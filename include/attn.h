@@ -170,7 +170,13 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  * sections "Decode performance" and "Key Optimization ... Group q_seqlen and
  * num_heads into BMM1 M"; "Writing Page Attention with PyPTO", sections 1-9).
  *
- *   q          bf16 [batch, q_len, Hq, Dqk] contiguous.
+ *   q          [batch, q_len, Hq, Dqk] contiguous, in q_dtype: bf16 (0, a
+ *              zeroed struct), or ATTN_FP8_E4M3 codes with the per-tensor
+ *              dequantisation scale q_scale (value = code * q_scale), for an
+ *              MLA-shaped FP8 cache only: the FP8 decode path whose query and
+ *              latent cache are both FP8 ("TokenSpeed-MLA", MLA Decode in the
+ *              kernel capability summary); its QK product runs on the FP8
+ *              matrix instruction. q_scale is ignored for bf16 q.
  *   k_cache    [num_pages, page_size, Hkv, Dqk] in kv_dtype, strides k_stride_*.
  *   v_cache    [num_pages, page_size, Hkv, >= Dv] in kv_dtype, strides
  *              v_stride_*; V is the first Dv entries of each row. For an
@@ -243,6 +249,8 @@ typedef struct {
   int32_t window_left;      /* keys of context when window_enabled */
   int32_t packed_q;         /* 0: folded rows; 1: continuous token * G + head rows */
   int64_t total_kv_tokens;  /* planner hint: host sum of seq_lens, 0 = unknown */
+  attn_dtype_t q_dtype;     /* ATTN_BF16 (0) or ATTN_FP8_E4M3 (MLA-shaped FP8 cache only) */
+  float q_scale;            /* fp8 q: value = code * q_scale */
 } attn_decode_params;
 
 /* How attn_decode_paged will decompose a call (host-only; no device access). */

@@ -203,13 +203,15 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                       scale: float, causal: bool, head_dim_v: int,
                       rows: list[tuple[int, int, int]], kv_format: str = "f64",
                       kv_scale: float = 1.0, q_format: str = "f64",
-                      window_left: int = -1) -> tuple[np.ndarray, np.ndarray]:
+                      window_left: int = -1, q_scale: float = 1.0) -> tuple[np.ndarray, np.ndarray]:
     """Decode attention for selected (batch, query token, query head) rows.
 
     q: [B, q_len, Hq, Dqk] float64; k_cache: [P, ps, Hkv, Dqk];
     v_cache: [P, ps, Hkv, >=Dv] (V is its first head_dim_v entries); caches
     hold values (kv_format "f64") or raw storage ("bf16", "e4m3fn" with
-    kv_scale), widened after gathering; q likewise ("f64" or "bf16" bits);
+    kv_scale), widened after gathering; q likewise ("f64", "bf16" bits, or
+    "e4m3fn" codes times q_scale: the FP8 decode path of "TokenSpeed-MLA",
+    whose FP8 inputs are the query and the latent cache);
     block_table: [B, max_pages] ints; seq_lens: [B] ints.
     Returns o [len(rows), Dv] and lse2 [len(rows)].
     """
@@ -226,7 +228,7 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         k = widen(gather_paged_rows(k_cache, block_table[b], lk, page_size, g), kv_format, kv_scale)
         v = widen(gather_paged_rows(v_cache, block_table[b], lk, page_size, g, head_dim_v),
                   kv_format, kv_scale)
-        qr = widen(np.stack([q[rows[n][0], rows[n][1], rows[n][2]] for n in members]), q_format)
+        qr = widen(np.stack([q[rows[n][0], rows[n][1], rows[n][2]] for n in members]), q_format, q_scale)
         t = np.array([rows[n][1] for n in members], dtype=np.int64)
         bound = causal_key_bound(t, q_len, lk) if causal else np.full(len(members), lk)
         start = window_key_start(t, q_len, lk, window_left)
@@ -237,14 +239,15 @@ def decode_paged_rows(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
 
 
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, page_size, scale,
-                 causal, head_dim_v, kv_format="f64", kv_scale=1.0, q_format="f64", window_left=-1):
+                 causal, head_dim_v, kv_format="f64", kv_scale=1.0, q_format="f64", window_left=-1,
+                 q_scale=1.0):
     """Decode attention for every row: returns o [B, q_len, Hq, Dv] and
     lse2 [B, q_len, Hq]."""
     b_n, q_len, hq, _ = q.shape
     rows = [(b, t, h) for b in range(b_n) for t in range(q_len) for h in range(hq)]
     o, lse2 = decode_paged_rows(q, k_cache, v_cache, block_table, seq_lens, page_size,
                                 scale, causal, head_dim_v, rows, kv_format, kv_scale, q_format,
-                                window_left)
+                                window_left, q_scale)
     return o.reshape(b_n, q_len, hq, head_dim_v), lse2.reshape(b_n, q_len, hq)
 
 

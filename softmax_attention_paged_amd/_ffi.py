@@ -62,7 +62,7 @@ class DecodeParams(ctypes.Structure):
         ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
         ("o", _p), ("lse", _p),
         ("window_enabled", _i32), ("window_left", _i32), ("packed_q", _i32),
-        ("total_kv_tokens", _i64),
+        ("total_kv_tokens", _i64), ("q_dtype", ctypes.c_int), ("q_scale", ctypes.c_float),
     ]
 
 

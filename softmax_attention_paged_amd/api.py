@@ -53,8 +53,9 @@ def _as_4d_cache(cache: torch.Tensor) -> torch.Tensor:
 def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                   causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
                   num_splits=0, workspace=None, out=None, lse=None, window_left=-1,
-                  packed_q=False, total_kv_tokens=0) -> _ffi.DecodeParams:
-    """Fill the C parameter struct from tensors (no device access)."""
+                  packed_q=False, total_kv_tokens=0, q_scale=None) -> _ffi.DecodeParams:
+    """Fill the C parameter struct from tensors (no device access). A uint8
+    (or float8_e4m3fn) q holds E4M3 codes with dequantisation scale q_scale."""
     k4 = _as_4d_cache(k_cache)
     v4 = _as_4d_cache(v_cache if v_cache is not None else k_cache)
     b, q_len, hq, dqk = q.shape
@@ -78,7 +79,16 @@ def decode_params(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, so
     p.window_enabled, p.window_left = int(window_left >= 0), max(int(window_left), 0)
     p.packed_q = int(bool(packed_q))
     p.total_kv_tokens = int(total_kv_tokens)
+    if _is_fp8_codes(q):
+        _need(q_scale is not None, "fp8 q needs q_scale")
+        p.q_dtype, p.q_scale = _ffi.ATTN_FP8_E4M3, float(q_scale)
+    else:
+        p.q_dtype, p.q_scale = _ffi.ATTN_BF16, 1.0
     return p
+
+
+def _is_fp8_codes(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
 
 
 def decode_plan(params: _ffi.DecodeParams) -> dict:
@@ -90,7 +100,7 @@ def decode_plan(params: _ffi.DecodeParams) -> dict:
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                  causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
                  num_splits=0, workspace=None, out=None, return_lse=False, window_left=-1,
-                 packed_q=False, total_kv_tokens=0, lse=None, phase="both"):
+                 packed_q=False, total_kv_tokens=0, lse=None, phase="both", q_scale=None):
     """Paged decode (split-KV + LSE merge). Returns out, or (out, lse).
 
     phase "split" or "merge" enqueues only that kernel of the call
@@ -105,7 +115,8 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
     host's sum of seq_lens, 0 if unknown) lets the planner size the splits
     so every unit is resident at once.
     """
-    _need(q.is_cuda and q.dtype == _BF16 and q.is_contiguous(), "q must be a contiguous bf16 CUDA tensor")
+    _need(q.is_cuda and (q.dtype == _BF16 or _is_fp8_codes(q)) and q.is_contiguous(),
+          "q must be a contiguous bf16 (or fp8 code) CUDA tensor")
     _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
     _need(block_table.stride(1) == 1 and seq_lens.is_contiguous(), "block_table rows and seq_lens must be contiguous")
     b, q_len, hq, _ = q.shape
@@ -126,7 +137,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
                       softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
                       k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=workspace,
                       out=out, lse=lse, window_left=window_left, packed_q=packed_q,
-                      total_kv_tokens=total_kv_tokens)
+                      total_kv_tokens=total_kv_tokens, q_scale=q_scale)
     lib = _ffi.load()
     if workspace is None:
         need = lib.attn_decode_workspace_size(ctypes.byref(p))
@@ -141,12 +152,13 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
 def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, softmax_scale,
                          causal=False, head_dim_v=None, kv_dtype=None, k_scale=1.0, v_scale=1.0,
                          num_splits=0, out=None, lse=None, window_left=-1, packed_q=False,
-                         total_kv_tokens=0):
+                         total_kv_tokens=0, q_scale=None):
     """decode_paged through attn_decode_paged_noalloc: the split partials go
     to the library's static per-device scratch, so with `out` (and `lse`,
     if wanted) given the call allocates nothing. Returns out, or (out, lse)
     when lse is given."""
-    _need(q.is_cuda and q.dtype == _BF16 and q.is_contiguous(), "q must be a contiguous bf16 CUDA tensor")
+    _need(q.is_cuda and (q.dtype == _BF16 or _is_fp8_codes(q)) and q.is_contiguous(),
+          "q must be a contiguous bf16 (or fp8 code) CUDA tensor")
     _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "block_table/seq_lens must be int32")
     _need(block_table.stride(1) == 1 and seq_lens.is_contiguous(), "block_table rows and seq_lens must be contiguous")
     b, q_len, hq, _ = q.shape
@@ -159,7 +171,7 @@ def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_
                       softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
                       k_scale=k_scale, v_scale=v_scale, num_splits=num_splits, workspace=None,
                       out=out, lse=lse, window_left=window_left, packed_q=packed_q,
-                      total_kv_tokens=total_kv_tokens)
+                      total_kv_tokens=total_kv_tokens, q_scale=q_scale)
     _ffi.check(_ffi.load().attn_decode_paged_noalloc(ctypes.byref(p), _stream(q.device)), "attn_decode_paged_noalloc")
     return (out, lse) if lse is not None else out
 

@@ -158,6 +158,14 @@ attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) 
   }
   if (p->kv_dtype == ATTN_BF16 && (p->k_scale != 1.f || p->v_scale != 1.f))
     return fail(ATTN_ERR_INVALID_ARG, "k_scale and v_scale must be 1.0 for bf16 KV");
+  if (p->q_dtype != ATTN_BF16 && p->q_dtype != ATTN_FP8_E4M3)
+    return fail(ATTN_ERR_INVALID_ARG, "q_dtype must be ATTN_BF16 or ATTN_FP8_E4M3");
+  if (p->q_dtype == ATTN_FP8_E4M3) {
+    if (!mla || p->kv_dtype != ATTN_FP8_E4M3)
+      return fail(ATTN_ERR_UNSUPPORTED, "fp8 q is supported with an MLA-shaped fp8 cache only");
+    if (!(p->q_scale > 0.f) || !std::isfinite(p->q_scale))
+      return fail(ATTN_ERR_INVALID_ARG, "fp8 q needs a finite positive q_scale");
+  }
 
   if (p->batch == 0 || !check_pointers) return ok();
   if (!p->q || !p->k_cache || !p->v_cache || !p->seq_lens || !p->block_table || !p->o)
@@ -488,6 +496,7 @@ attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, 
     a.kv_stride_page = p->k_stride_page;
     a.kv_stride_tok = p->k_stride_tok;
     a.kv_fp8 = p->kv_dtype == ATTN_FP8_E4M3;
+    a.q_fp8 = p->q_dtype == ATTN_FP8_E4M3;
     // FP8 codes are used as stored: k_scale folds into the score scale,
     // v_scale into the output normalisation.
     a.kv_scale = a.kv_fp8 ? p->v_scale : 1.0f;
@@ -504,7 +513,7 @@ attn_status_t decode_enqueue(const attn_decode_params *p, const DecodePlan &pl, 
     a.packed = p->packed_q;
     a.num_splits = pl.splits;
     a.split_tokens = pl.split_tokens;
-    a.scale_log2 = a.kv_fp8 ? scale_log2 * p->k_scale : scale_log2;
+    a.scale_log2 = (a.kv_fp8 ? scale_log2 * p->k_scale : scale_log2) * (a.q_fp8 ? p->q_scale : 1.f);
     a.causal = p->causal;
     a.window_left = p->window_enabled ? p->window_left : -1;
     a.o = p->o;

@@ -50,6 +50,7 @@ struct DecodeMlaArgs {
   const void *kv_cache;          // bf16 or fp8 codes [pages, ps, 1, 576]
   int64_t kv_stride_page, kv_stride_tok;
   int32_t kv_fp8;
+  int32_t q_fp8;                 // E4M3 q codes (kv_fp8 too); q_scale folds into scale_log2
   float kv_scale;
   const int32_t *seq_lens;
   const int32_t *block_table;

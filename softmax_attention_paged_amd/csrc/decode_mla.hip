@@ -202,13 +202,62 @@ __device__ __forceinline__ void mla_store_fp8(char *dst, int tid, const u32x4 (&
   }
 }
 
+// FP8 q: the codes also stay in LDS as the K operand of the FP8 matrix
+// instruction (576-byte rows; the 16-byte chunks of row r XOR-swizzled by
+// (r >> 2) & 3, which puts rows r, r + 4, r + 8, r + 12 of an operand read
+// on different banks and keeps each chunk in its aligned group of four),
+// and only the 512 V columns are widened to the bf16 tile.
+constexpr int kK8RowB = kDk;                         // bytes of a code row
+constexpr int kK8TileB = kTileN * kK8RowB;           // bytes of a code tile
+constexpr int kKB8 = kDk / 64;                       // FP8 QK k-steps of 64 codes
+constexpr int kKB8Reg = 6;                           // k-steps whose q codes stay in registers
+constexpr int kQ8RowB = (kKB8 - kKB8Reg) * 64 + 16;  // LDS bytes per row of the other q codes (padded)
+__device__ __forceinline__ int k8_swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void mla_store_fp8q(char *vdst, char *kdst, int tid, const u32x4 (&stage)[kF8PerThread]) {
+#pragma unroll
+  for (int c = 0; c < kF8PerThread; ++c) {
+    const int idx = c * kThreads + tid;
+    if (idx >= kF8Chunks) continue;
+    const int row = idx / (kDk / 16), c8 = idx % (kDk / 16);
+    *reinterpret_cast<u32x4 *>(kdst + row * kK8RowB + (c8 ^ k8_swz(row)) * 16) = stage[c];
+    if (c8 < kDv / 16) {
+      bf16x8 lo, hi;
+      fp8x16_to_bf16(stage[c], lo, hi);
+      char *r = vdst + row * kRowB;
+      store_bf16x8_lds(r + ((2 * c8) ^ mla_swz(row)) * 16, lo);
+      store_bf16x8_lds(r + ((2 * c8 + 1) ^ mla_swz(row)) * 16, hi);
+    }
+  }
+}
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  // format selectors 0, 0: both operands E4M3; zero scale operands give the
+  // unscaled instruction
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
+  i32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = static_cast<int>(lo[i]);
+    r[4 + i] = static_cast<int>(hi[i]);
+  }
+  return r;
+}
+
 // kExt adds what a sliding window or packed query rows need (the packed row
 // mapping, the window's start and lower-bound mask); the plain kernel keeps
-// those registers free.
-template <bool FP8, bool kExt>
+// those registers free. QF8 (with FP8): E4M3 q, QK on the FP8 instruction.
+template <bool FP8, bool QF8, bool kExt>
 __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMlaArgs a) {
+  static_assert(!QF8 || FP8, "fp8 q comes with an fp8 cache");
   __shared__ __attribute__((aligned(16))) char tiles[2 * kTileB];
-  __shared__ __attribute__((aligned(16))) char qlds[kMlaRows * kQRowB];
+  __shared__ __attribute__((aligned(16))) char qlds[QF8 ? kMlaRows * kQ8RowB : kMlaRows * kQRowB];
+  __shared__ __attribute__((aligned(16))) char ktiles8[QF8 ? 2 * kK8TileB : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -301,7 +350,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
   const float c = fabsf(a.scale_log2);
   const u32x4 qsign = (a.scale_log2 < 0.f) ? u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u} : u32x4{};
   bf16x8 qop[kKBReg];
-  {
+  // FP8 q: codes 64 kb + 32 half .. + 31 of row r; k-steps past kKB8Reg
+  // wait in the row's LDS copy
+  i32x8 qop8[QF8 ? kKB8Reg : 1];
+  if constexpr (QF8) {
+    const unsigned s8 = (a.scale_log2 < 0.f) ? 0x80808080u : 0u;   // a sign flip of every code is exact
+    const u32x4 sg = u32x4{s8, s8, s8, s8};
+    const uint8_t *qrow = static_cast<const uint8_t *>(a.q) + ridx * kDk;
+    char *qdst = qlds + r * kQ8RowB;
+#pragma unroll
+    for (int kb = 0; kb < kKB8; ++kb) {
+      u32x4 lo = u32x4{0u, 0u, 0u, 0u}, hi = lo;
+      if (row_valid) {
+        lo = *reinterpret_cast<const u32x4 *>(qrow + 64 * kb + 32 * half) ^ sg;
+        hi = *reinterpret_cast<const u32x4 *>(qrow + 64 * kb + 32 * half + 16) ^ sg;
+      }
+      if (kb < kKB8Reg) {
+        qop8[kb < kKB8Reg ? kb : 0] = cat8(lo, hi);
+      } else {
+        *reinterpret_cast<u32x4 *>(qdst + (kb - kKB8Reg) * 64 + 32 * half) = lo;
+        *reinterpret_cast<u32x4 *>(qdst + (kb - kKB8Reg) * 64 + 32 * half + 16) = hi;
+      }
+    }
+  } else {
     const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + ridx * kDk;
 #pragma unroll
     for (int kb = 0; kb < kKBReg; ++kb)
@@ -377,7 +448,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
     lsum = 0.f;
     mla_issue<FP8>(x, map, first, c1, wave, lane, tid, tiles, stage);
     if (x.wide && first + 2 * kTileN <= c1) mla_prefetch<FP8>(x, first + kTileN, tid, sink);
-    if constexpr (FP8) mla_store_fp8(tiles, tid, stage);
+    if constexpr (QF8) mla_store_fp8q(tiles, ktiles8, tid, stage);
+    else if constexpr (FP8) mla_store_fp8(tiles, tid, stage);
     for (int it = 0; it < ntiles; ++it) {
       const int j0 = first + it * kTileN;
       const int p = it & 1;
@@ -396,7 +468,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
         // Operands come from LDS kRing MFMAs ahead of use (one wave per SIMD:
         // no other wave hides the LDS latency); the fences keep that order.
         f32x16 s = f32x16{};
-        {
+        if constexpr (QF8) {
+          // 9 FP8 k-steps of 64 codes: chunks 4 kb + 2 half (+1) of key row r32
+          const char *krow = ktiles8 + p * kK8TileB + r32 * kK8RowB;
+          const int sw = k8_swz(r32);
+          auto kread8 = [&](int kb) {
+            return cat8(*reinterpret_cast<const u32x4 *>(krow + ((4 * kb + 2 * half) ^ sw) * 16),
+                        *reinterpret_cast<const u32x4 *>(krow + ((4 * kb + 2 * half + 1) ^ sw) * 16));
+          };
+          const char *q8src = qlds + r * kQ8RowB + 32 * half;
+          auto qread8 = [&](int kb) {
+            return (kb < kKB8Reg) ? qop8[kb < kKB8Reg ? kb : 0]
+                                  : cat8(*reinterpret_cast<const u32x4 *>(q8src + (kb - kKB8Reg) * 64),
+                                         *reinterpret_cast<const u32x4 *>(q8src + (kb - kKB8Reg) * 64 + 16));
+          };
+          i32x8 kr8[kRing], qr8[kRing];
+#pragma unroll
+          for (int i = 0; i < kRing; ++i) {
+            kr8[i] = kread8(i);
+            qr8[i] = qread8(i);
+          }
+#pragma unroll
+          for (int kb = 0; kb < kKB8; ++kb) {
+            __builtin_amdgcn_sched_barrier(0);
+            s = mfma_f8(kr8[kb % kRing], qr8[kb % kRing], s);
+            if (kb + kRing < kKB8) {
+              kr8[kb % kRing] = kread8(kb + kRing);
+              qr8[kb % kRing] = qread8(kb + kRing);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
           auto kread = [&](int kb) { return *reinterpret_cast<const bf16x8 *>(tile + koff[kb & 3] + (kb >> 2) * 128); };
           auto qread = [&](int kb) {
             return (kb < kKBReg) ? qop[kb < kKBReg ? kb : 0]
@@ -489,7 +591,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mla_kernel(const DecodeMla
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      if constexpr (FP8) {
+      if constexpr (QF8) {
+        if (it + 1 < ntiles) mla_store_fp8q(tiles + (p ^ 1) * kTileB, ktiles8 + (p ^ 1) * kK8TileB, tid, stage);
+      } else if constexpr (FP8) {
         if (it + 1 < ntiles) mla_store_fp8(tiles + (p ^ 1) * kTileB, tid, stage);
       }
     }
@@ -545,12 +649,15 @@ hipError_t launch_decode_mla(const DecodeMlaArgs &a, hipStream_t stream) {
   const int64_t units = (int64_t)a.batch * a.num_splits * a.q_groups;
   const bool ext = a.packed || a.window_left >= 0;
   const dim3 grid((unsigned)units), block(kThreads);
-  if (a.kv_fp8) {
-    if (ext) hipLaunchKernelGGL((decode_mla_kernel<true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_mla_kernel<true, false>), grid, block, 0, stream, a);
+  if (a.kv_fp8 && a.q_fp8) {
+    if (ext) hipLaunchKernelGGL((decode_mla_kernel<true, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mla_kernel<true, true, false>), grid, block, 0, stream, a);
+  } else if (a.kv_fp8) {
+    if (ext) hipLaunchKernelGGL((decode_mla_kernel<true, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mla_kernel<true, false, false>), grid, block, 0, stream, a);
   } else {
-    if (ext) hipLaunchKernelGGL((decode_mla_kernel<false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_mla_kernel<false, false>), grid, block, 0, stream, a);
+    if (ext) hipLaunchKernelGGL((decode_mla_kernel<false, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_mla_kernel<false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -180,6 +180,8 @@ class DecodeCase:
     seed: int
     window_left: int = -1           # sliding window of context keys; -1: full history
     packed_q: bool = False          # continuous (token * H + head) row packing
+    q_dtype: str = "bf16"           # "bf16", or "fp8_e4m3": q holds uint8 codes
+    q_scale: float = 1.0            # dequantisation scale of fp8 q
 
     @property
     def latent(self) -> bool:
@@ -205,7 +207,7 @@ def decode_case(*, batch: int, q_len: int, hq: int, hkv: int, d: int, dv: int, p
                 pool_pages: int | None = None, max_pages: int | None = None, kv_dtype: str = "bf16",
                 latent: bool = False, scale: float | None = None, causal: bool = False,
                 q_mult: float = 1.0, shared_prefix_pages: int = 0, name: str = "",
-                window_left: int = -1, packed_q: bool = False) -> DecodeCase:
+                window_left: int = -1, packed_q: bool = False, q_dtype: str = "bf16") -> DecodeCase:
     s_layout, s_q, s_k, s_v = _streams(seed)
     rng = np.random.Generator(np.random.PCG64(s_layout))
     if seq_lens is None:
@@ -214,7 +216,14 @@ def decode_case(*, batch: int, q_len: int, hq: int, hkv: int, d: int, dv: int, p
     seq_lens = [int(n) for n in seq_lens]
     assert len(seq_lens) == batch
     lay = make_layout(rng, seq_lens, page_size, layout, pool_pages, max_pages, shared_prefix_pages)
-    q = _normal_bf16(s_q, (batch, q_len, hq, d), q_mult)
+    if q_dtype == "bf16":
+        q, q_scale = _normal_bf16(s_q, (batch, q_len, hq, d), q_mult), 1.0
+    elif q_dtype == "fp8_e4m3":
+        if kv_dtype != "fp8_e4m3":
+            raise ValueError("fp8 q is generated with an fp8 latent cache only")
+        q, q_scale = _fp8_codes(_normal_f32(s_q, (batch, q_len, hq, d), q_mult))
+    else:
+        raise ValueError(q_dtype)
     total = sum(seq_lens)
     shared_tokens = shared_prefix_pages * page_size
 
@@ -242,7 +251,7 @@ def decode_case(*, batch: int, q_len: int, hq: int, hkv: int, d: int, dv: int, p
                       seq_lens=torch.tensor(seq_lens, dtype=torch.int32), page_size=page_size,
                       head_dim_v=dv, scale=float(scale), causal=causal, kv_dtype=kv_dtype,
                       kv_scale=kv_scale, max_seq_len=max(seq_lens, default=0), seed=seed,
-                      window_left=window_left, packed_q=packed_q)
+                      window_left=window_left, packed_q=packed_q, q_dtype=q_dtype, q_scale=q_scale)
 
 
 # --------------------------------------------------------------------------
@@ -349,15 +358,16 @@ def single_chunk_prefill(seed: int = 6) -> PrefillCase:
                         page_size=64, name="single_chunk_prefill_q512_kv80k_h32kv8_d128_ps64")
 
 
-def mla_decode(kv_dtype: str = "bf16", seed: int = 5, causal: bool = True) -> DecodeCase:
+def mla_decode(kv_dtype: str = "bf16", seed: int = 5, causal: bool = True, q_dtype: str = "bf16") -> DecodeCase:
     """MLA-shaped split-KV decode: batch 8, 4 query tokens, 64 heads folded
     with 2 tokens into 128 rows, one latent KV head of width 576 (K = all 576,
-    V = the first 512), kv_len 81920, page_size 64, bf16 or fp8 e4m3 KV,
-    scale 0.07216882."""
+    V = the first 512), kv_len 81920, page_size 64, bf16 or fp8 e4m3 KV (and
+    with fp8 KV optionally fp8 e4m3 q), scale 0.07216882."""
+    qtag = "" if q_dtype == "bf16" else "_q" + q_dtype
     return decode_case(batch=8, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
                        seq_lens=[81920] * 8, seed=seed, kv_dtype=kv_dtype, latent=True,
-                       scale=0.07216882, causal=causal,
-                       name=f"mla_decode_b8_q4_h64_kv80k_d576-512_ps64_{kv_dtype}")
+                       scale=0.07216882, causal=causal, q_dtype=q_dtype,
+                       name=f"mla_decode_b8_q4_h64_kv80k_d576-512_ps64_{kv_dtype}{qtag}")
 
 
 @dataclasses.dataclass

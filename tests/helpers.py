@@ -53,11 +53,13 @@ def oracle_decode(case, rows=None):
     bt = case.block_table.numpy()
     sl = case.seq_lens.numpy()
     w = getattr(case, "window_left", -1)
+    qfmt = "bf16" if getattr(case, "q_dtype", "bf16") == "bf16" else "e4m3fn"
+    qs = getattr(case, "q_scale", 1.0)
     if rows is None:
         return oracle.decode_paged(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal, case.head_dim_v,
-                                   fmt, case.kv_scale, "bf16", w)
+                                   fmt, case.kv_scale, qfmt, w, qs)
     return oracle.decode_paged_rows(q, kc, vc, bt, sl, case.page_size, case.scale, case.causal,
-                                    case.head_dim_v, rows, fmt, case.kv_scale, "bf16", w)
+                                    case.head_dim_v, rows, fmt, case.kv_scale, qfmt, w, qs)
 
 
 def oracle_prefill(case, rows=None):

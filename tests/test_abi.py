@@ -137,6 +137,8 @@ def plan(p):
     (dict(num_q_heads=68, num_kv_heads=2), _ffi.ATTN_ERR_UNSUPPORTED),
     (dict(window_enabled=2), _ffi.ATTN_ERR_INVALID_ARG),
     (dict(window_enabled=1, window_left=-3), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(q_dtype=7), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(q_dtype=_ffi.ATTN_FP8_E4M3, q_scale=1.0), _ffi.ATTN_ERR_UNSUPPORTED),    # fp8 q needs an fp8 latent cache
 ])
 def test_decode_validation_errors(kw, code):
     lib = _lib()
@@ -500,3 +502,21 @@ def test_mla_pack_zero_tokens_and_no_rope_are_accepted():
     lib = _lib()
     assert lib.attn_mla_kv_pack_fp8(ctypes.byref(pack_params()), None) == _ffi.ATTN_OK
     assert lib.attn_mla_kv_pack_fp8(ctypes.byref(pack_params(d_rope=0, k_rope=None)), None) == _ffi.ATTN_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), _ffi.ATTN_OK),
+    (dict(q_scale=0.0), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(q_scale=float("inf")), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(kv_dtype=_ffi.ATTN_BF16, k_scale=1.0, v_scale=1.0), _ffi.ATTN_ERR_UNSUPPORTED),
+])
+def test_fp8_query_needs_an_fp8_latent_cache_and_a_scale(kw, code):
+    # host-side plan only (no pointers read): the FP8 query path is the MLA
+    # shape with an FP8 cache and a finite positive q_scale
+    d = dict(num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, q_len=4, v_cache=FAKE,
+             k_stride_page=64 * 576, k_stride_tok=576, k_stride_head=576, v_stride_page=64 * 576, v_stride_tok=576,
+             v_stride_head=576, page_size=64, num_pages=64, max_seq_len=4096, block_table_stride=64,
+             kv_dtype=_ffi.ATTN_FP8_E4M3, k_scale=0.5, v_scale=0.5, q_dtype=_ffi.ATTN_FP8_E4M3, q_scale=0.25)
+    d.update(kw)
+    st, _ = plan(decode_params(**d))
+    assert st == code, (st, _lib().attn_last_error())

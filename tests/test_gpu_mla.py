@@ -15,13 +15,29 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
+# KV dtype, with "+q" for the FP8 path whose query is FP8 too
+DTYPES = ["bf16", "fp8_e4m3", "fp8_e4m3+q"]
+
+
+def _dt(name):
+    return dict(kv_dtype=name.split("+")[0], q_dtype="fp8_e4m3" if name.endswith("+q") else "bf16")
+
+
+def _qvalues(case):
+    """The query's values as float64 (bf16 bits, or E4M3 codes times q_scale)."""
+    if case.q_dtype == "bf16":
+        return f64(case.q)
+    return oracle.widen_e4m3fn(case.q.numpy(), case.q_scale)
+
+
 def _run(case, num_splits=0):
     c = case.to(DEV)
     out, lse = sap.decode_paged(c.q, c.k_cache, None, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
                                 softmax_scale=c.scale, causal=c.causal, head_dim_v=512,
                                 kv_dtype=None if c.kv_dtype == "bf16" else c.kv_dtype,
                                 k_scale=c.kv_scale, v_scale=c.kv_scale, num_splits=num_splits, return_lse=True,
-                                window_left=c.window_left, packed_q=c.packed_q)
+                                window_left=c.window_left, packed_q=c.packed_q,
+                                q_scale=None if c.q_dtype == "bf16" else c.q_scale)
     torch.cuda.synchronize()
     return out.cpu(), lse.cpu()
 
@@ -32,46 +48,46 @@ def _check(case, num_splits=0):
     return compare(f64(out), ref, lse.numpy(), lref, TOL_BF16 if case.kv_dtype == "bf16" else TOL_FP8)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("hq,q_len", [(64, 4), (16, 4), (128, 1), (8, 3), (32, 2)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_latent_decode_small(kv_dtype, hq, q_len, causal):
     case = inputs.decode_case(batch=3, q_len=q_len, hq=hq, hkv=1, d=576, dv=512, page_size=16,
-                              seq_lens=[3, 37, 300], seed=hq + q_len, kv_dtype=kv_dtype, latent=True,
-                              scale=0.07216882, causal=causal, layout="noncontiguous")
+                              seq_lens=[3, 37, 300], seed=hq + q_len, latent=True,
+                              scale=0.07216882, causal=causal, layout="noncontiguous", **_dt(kv_dtype))
     print(kv_dtype, hq, q_len, causal, flush=True)
     for splits in (0, 1, 3):
         print(_check(case, splits))
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 def test_latent_layouts_bitwise(kv_dtype):
     outs = []
     for layout in ("identity", "random", "reverse"):
         case = inputs.decode_case(batch=2, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
-                                  seq_lens=[1000, 129], seed=61, kv_dtype=kv_dtype, latent=True,
-                                  scale=0.07216882, causal=True, layout=layout)
+                                  seq_lens=[1000, 129], seed=61, latent=True,
+                                  scale=0.07216882, causal=True, layout=layout, **_dt(kv_dtype))
         outs.append(_run(case, num_splits=2))
     for o, l in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("causal", [True, False])
 def test_mla_decode_80k_every_row(kv_dtype, causal):
     """The MLA-shaped workload at full size (batch 8, 4 tokens, 64 heads,
     kv_len 81920), planned as the benchmark plans it: every one of its 2,048
     (request, token, head) rows against the oracle."""
-    case = inputs.mla_decode(kv_dtype=kv_dtype, causal=causal)
+    case = inputs.mla_decode(causal=causal, **_dt(kv_dtype))
     print("case", case.name, flush=True)
     out, lse = _run(case)
     ref, lref = oracle_decode(case)
-    res = compare(f64(out), ref, lse.numpy(), lref, TOL_BF16 if kv_dtype == "bf16" else TOL_FP8)
+    res = compare(f64(out), ref, lse.numpy(), lref, TOL_BF16 if case.kv_dtype == "bf16" else TOL_FP8)
     res["rows_checked"] = int(np.prod(lref.shape))
     print(res)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("splits", [0, 3])
 def test_static_anchor_restart(kv_dtype, splits):
     """One latent row gives the row (token 0, head 0) a score of about 150-175
@@ -82,12 +98,12 @@ def test_static_anchor_restart(kv_dtype, splits):
     keep their usual size); fp8: the whole row is 3 x the query, clamped to
     the e4m3 range."""
     case = inputs.decode_case(batch=2, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
-                              seq_lens=[700, 300], seed=71, kv_dtype=kv_dtype, latent=True,
-                              scale=0.07216882, causal=True, layout="random")
+                              seq_lens=[700, 300], seed=71, latent=True,
+                              scale=0.07216882, causal=True, layout="random", **_dt(kv_dtype))
     j = 500                                            # logical key of request 0
     page = int(case.block_table[0, j // 64])
-    q00 = case.q[0, 0, 0].float()
-    if kv_dtype == "bf16":
+    q00 = torch.from_numpy(_qvalues(case)[0, 0, 0]).float()
+    if case.kv_dtype == "bf16":
         case.k_cache[page, j % 64, 0, 512:] = (28.0 * q00[512:]).to(torch.bfloat16)
     else:
         codes = (3.0 * q00 / case.kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
@@ -96,7 +112,7 @@ def test_static_anchor_restart(kv_dtype, splits):
     print(res)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("splits", [1, 3])
 def test_window_anchor_ignores_hidden_keys(kv_dtype, splits):
     """A sliding window whose start lies 30 keys into the first walked tile:
@@ -111,10 +127,14 @@ def test_window_anchor_ignores_hidden_keys(kv_dtype, splits):
     the largest E4M3 value)."""
     lens, q_len, window = [700, 444], 4, 346      # 700 - 4 - 346 = 350 = 320 + 30; 444 - 4 - 346 = 94 = 64 + 30
     case = inputs.decode_case(batch=2, q_len=q_len, hq=64, hkv=1, d=576, dv=512, page_size=64,
-                              seq_lens=lens, seed=83, kv_dtype=kv_dtype, latent=True,
-                              scale=0.07216882, causal=True, layout="random", window_left=window)
+                              seq_lens=lens, seed=83, latent=True,
+                              scale=0.07216882, causal=True, layout="random", window_left=window, **_dt(kv_dtype))
+    kv_dtype = case.kv_dtype
     cols = slice(512, 576) if kv_dtype == "bf16" else slice(0, 576)
-    case.q[..., cols] = case.q[..., cols].abs()
+    if case.q_dtype == "bf16":
+        case.q[..., cols] = case.q[..., cols].abs()
+    else:
+        case.q[..., cols] = case.q[..., cols] & 0x7F        # E4M3 codes: clear the sign bit
     for b, lk in enumerate(lens):
         start = lk - q_len - window                  # first key row 0 sees
         base = start & ~31                           # first key of the walk
@@ -127,7 +147,7 @@ def test_window_anchor_ignores_hidden_keys(kv_dtype, splits):
                 case.k_cache[page, j % 64, 0] = 0x7E     # E4M3 448
     # precondition: every hidden score exceeds every visible one by >= 150 log2 units
     kc = f64(case.k_cache) if kv_dtype == "bf16" else oracle.widen_e4m3fn(case.k_cache.numpy(), case.kv_scale)
-    qf = f64(case.q)
+    qf = _qvalues(case)
     for b, lk in enumerate(lens):
         start = lk - q_len - window
         keys = np.stack([kc[int(case.block_table[b, j // 64]), j % 64, 0] for j in range(start & ~31, lk)])
@@ -139,7 +159,7 @@ def test_window_anchor_ignores_hidden_keys(kv_dtype, splits):
     print(_check(case, splits))
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv_dtype", DTYPES)
 @pytest.mark.parametrize("splits", [1, 3])
 def test_static_anchor_second_restart(kv_dtype, splits):
     """Two planted keys for the row (token 0, head 0), the second scoring far
@@ -148,12 +168,12 @@ def test_static_anchor_second_restart(kv_dtype, splits):
     every anchor to its row's max runs before the last walk. Both keys lie
     in the first split when there are three."""
     case = inputs.decode_case(batch=2, q_len=4, hq=64, hkv=1, d=576, dv=512, page_size=64,
-                              seq_lens=[700, 300], seed=72, kv_dtype=kv_dtype, latent=True,
-                              scale=0.07216882, causal=True, layout="random")
-    q00 = case.q[0, 0, 0].float()
+                              seq_lens=[700, 300], seed=72, latent=True,
+                              scale=0.07216882, causal=True, layout="random", **_dt(kv_dtype))
+    q00 = torch.from_numpy(_qvalues(case)[0, 0, 0]).float()
     for j, mult in ((200, 1.0), (240, 2.0)):
         page = int(case.block_table[0, j // 64])
-        if kv_dtype == "bf16":
+        if case.kv_dtype == "bf16":
             case.k_cache[page, j % 64, 0, 512:] = (28.0 * mult * q00[512:]).to(torch.bfloat16)
         else:
             codes = (1.5 * mult * q00 / case.kv_scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)

@@ -508,3 +508,47 @@ def test_fp8_prefill_sampled_rows_equal_full():
     orow, lrow = oracle.prefill_dense_fp8_rows(q, k, v, 0.03, 0.02, 0.5, cu_q, cu_k, 0.09, True, rows, window_left=9)
     for n, (t, hh) in enumerate(rows):
         assert np.allclose(orow[n], o[t, hh], atol=1e-12) and abs(lrow[n] - l[t, hh]) < 1e-12
+
+
+# ------------------------------------------------- FP8 query, latent decode --
+
+def test_fp8_query_latent_decode_matches_sdpa_on_torch_decoded_values():
+    # the FP8 decode path: E4M3 query codes and an E4M3 latent cache (K the
+    # 576-wide row, V its first 512), each with its own scale; one query
+    # token, non-causal, against torch's own decoding of the codes and SDPA
+    r = _rng(94)
+    h, ps, lens = 4, 16, [5, 40, 1]
+    q = _e4m3_codes(r, (3, 1, h, 576))
+    logical = [_e4m3_codes(r, (n, 576)) for n in lens]
+    pages = sum(-(-n // ps) for n in lens)
+    perm = r.permutation(pages)
+    cache = np.zeros((pages, ps, 1, 576), dtype=np.uint8)
+    bt = np.full((3, 3), -1, dtype=np.int64)
+    used = 0
+    for b, n in enumerate(lens):
+        for j in range(-(-n // ps)):
+            bt[b, j] = perm[used]
+            rows = logical[b][j * ps:(j + 1) * ps]
+            cache[perm[used], :len(rows), 0] = rows
+            used += 1
+    qs, kvs, scale = 0.021, 0.017, 0.0417
+    o, lse2 = oracle.decode_paged(q, cache, cache, bt, np.array(lens), ps, scale, False, 512, "e4m3fn", kvs,
+                                  "e4m3fn", q_scale=qs)
+    for b, n in enumerate(lens):
+        kv = _torch_values(logical[b], kvs)
+        for hh in range(h):
+            qv = _torch_values(q[b, 0, hh][None], qs)
+            ref = _sdpa(qv, kv, kv[:, :512], scale, False)[0]
+            assert np.max(np.abs(o[b, 0, hh] - ref)) < 1e-10
+            want = logsumexp(scale * (qv @ kv.T)[0]) / math.log(2.0)
+            assert abs(lse2[b, 0, hh] - want) < 1e-10
+
+
+def test_fp8_query_scale_enters_as_a_product_with_the_softmax_scale():
+    r = _rng(95)
+    q = _e4m3_codes(r, (1, 2, 2, 576))
+    cache = _e4m3_codes(r, (2, 16, 1, 576))
+    bt, lens = np.array([[1, 0]]), np.array([20])
+    a = oracle.decode_paged(q, cache, cache, bt, lens, 16, 0.05, True, 512, "e4m3fn", 0.01, "e4m3fn", q_scale=0.03)
+    b = oracle.decode_paged(q, cache, cache, bt, lens, 16, 0.1, True, 512, "e4m3fn", 0.01, "e4m3fn", q_scale=0.015)
+    assert np.allclose(a[0], b[0], atol=1e-12) and np.allclose(a[1], b[1], atol=1e-12)
