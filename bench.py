@@ -199,6 +199,67 @@ def trace_summary(workload: str, trace_dir: str, steps: int) -> str:
     return text
 
 
+COUNTER_PASSES = [
+    "MfmaUtil",
+    "VALUBusy",
+    "SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_LDS SQ_INSTS_LDS "
+    "SQ_INSTS_VALU SQ_WAIT_ANY",
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS_LOAD_BANDWIDTH GRBM_GUI_ACTIVE",
+]
+
+
+def counter_summary(workload: str, run_dir: str) -> str:
+    """Write profiles/counters_<workload>.md from the four rocprofv3 --pmc
+    passes (run_dir/p1 .. p4, one counter block each) of `bench.py --only
+    <workload> --steps 3`: means over the dispatches of the workload's
+    roofline kernel."""
+    import csv
+    import glob
+    kernel = TRAFFIC_KERNELS[workload][0]
+    agg: dict[str, list[float]] = {}
+    name = None
+    for i in range(1, len(COUNTER_PASSES) + 1):
+        files = glob.glob(os.path.join(run_dir, f"p{i}", "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter_collection.csv under {run_dir}/p{i}")
+        per: dict[tuple[str, str], float] = {}
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                name = r["Kernel_Name"]
+                key = (r.get("Dispatch_Id", r.get("Correlation_Id", "")), r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, c), v in per.items():
+            agg.setdefault(c, []).append(v)
+    m = {c: sum(v) / len(v) for c, v in agg.items()}
+    n = len(agg.get("SQ_INSTS_MFMA", []))
+    mf = m["SQ_INSTS_MFMA"]
+    row = (f"| {workload} | `{name.split('(attn')[0].replace('void ', '').split('::')[-1]}` | {n} | "
+           f"{m['MfmaUtil']:.1f} | {m['VALUBusy']:.1f} | {mf:.3g} | {m['SQ_VALU_MFMA_BUSY_CYCLES'] / mf:.1f} | "
+           f"{m['SQ_INSTS_VALU'] / mf:.2f} | {m['SQ_INSTS_LDS'] / mf:.2f} | "
+           f"{100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.0f}% | "
+           f"{100 * m['SQ_LDS_BANK_CONFLICT'] / max(m['SQ_LDS_IDX_ACTIVE'], 1):.1f}% |")
+    lines = [f"# MFMA, VALU and LDS counters: {workload}", "", "Commands (repository root, MI355X, rocprofv3 "
+             "from ROCm 7.2; one counter block per run, as rocprofv3 collects no counters over several passes):",
+             "", "```"]
+    for i, c in enumerate(COUNTER_PASSES, 1):
+        lines.append(f"rocprofv3 --pmc {c} --output-format csv -d {run_dir}/p{i} -o run -- "
+                     f"python3 bench.py --only {workload} --steps 3")
+    lines += [f"python3 bench.py --counter-summary {workload} {run_dir}", "```", "",
+              "Means over the dispatches of the kernel in the run (settling calls, warm-up and timed calls). "
+              "MfmaUtil and VALUBusy are rocprofv3's derived metrics (percent of active cycles); per-MFMA columns "
+              "divide by SQ_INSTS_MFMA; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES; conflicts = SQ_LDS_BANK_CONFLICT / "
+              "SQ_LDS_IDX_ACTIVE.", "",
+              "| workload | kernel | dispatches | MfmaUtil % | VALUBusy % | MFMA instr./dispatch | busy cycles/MFMA | "
+              "vector instr./MFMA | LDS instr./MFMA | wave cycles waiting | LDS bank conflicts |",
+              "|---|---|---|---|---|---|---|---|---|---|---|", row]
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md"), "w") as f:
+        f.write(text)
+    return text
+
+
 def time_events(fn, steps: int, stream) -> float:
     """Average milliseconds per call of fn, HIP events on `stream`."""
     import torch
@@ -600,6 +661,8 @@ def main() -> int:
                          "dense_causal_prefill_d128, "
                          "dense_causal_prefill_d256, ragged_paged_prefill_80k, single_chunk_prefill_80k, mla_decode_80k_bf16, "
                          "mla_decode_80k_fp8_e4m3, mla_decode_80k_fp8_q")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("WORKLOAD", "RUN_DIR"),
+                    help="write profiles/counters_<workload>.md from four rocprofv3 --pmc passes under RUN_DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 3 device-to-device copies of BYTES (reference for HBM counters)")
     ap.add_argument("--traffic-summary", nargs=6, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -614,6 +677,9 @@ def main() -> int:
         return 0
     if args.trace_summary:
         print(trace_summary(args.trace_summary[0], args.trace_summary[1], int(args.trace_summary[2])))
+        return 0
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary[0], args.counter_summary[1]))
         return 0
     if args.copy_calibration:
         import torch
