@@ -84,5 +84,44 @@ __device__ __forceinline__ bool pf_unit(const PrefillArgs &a, int blocks, PfUnit
   return u.q_end > 0;
 }
 
+// pf_unit for launches whose per-head K/V fits one XCD's L2 (the FP8 MLA
+// prefill: 2.5 MB per head at 8K keys): each XCD walks its own heads HB at a
+// time, all query tiles of those heads (longest first) before the next HB,
+// so the workgroups running on an XCD share the K/V of HB heads instead of
+// one or two tiles of every head (blocks go to the XCDs in turn, so block i
+// runs on XCD i % 8). Falls back to pf_unit when the heads or blocks do not
+// divide evenly, or with key splits.
+template <int HB>
+__device__ __forceinline__ bool pf_unit_xcd_heads(const PrefillArgs &a, int blocks, PfUnit &u) {
+  constexpr int kXcds = 8;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  u.gh = pf_heads_per_wg(group);
+  u.tq = 32 * (blocks / u.gh);
+  const int head_groups = a.num_q_heads / u.gh;
+  const int q_tiles = (a.max_seqlen_q + u.tq - 1) / u.tq;
+  if (a.kv_splits > 1 || head_groups % (kXcds * HB) != 0) return pf_unit(a, blocks, u);
+  const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+  const int per_round = HB * q_tiles * a.batch;          // blocks of one XCD's round of HB heads
+  const int round = k / per_round, r = k % per_round;
+  const int qt = r / (HB * a.batch), rest = r % (HB * a.batch);
+  u.b = rest / HB;
+  u.split = 0;
+  u.h0 = ((round * kXcds + x) * HB + rest % HB) * u.gh;
+  u.kvh = u.h0 / group;
+  const int q_lo = a.cu_seqlens_q[u.b];
+  u.lq = a.cu_seqlens_q[u.b + 1] - q_lo;
+  u.q_off = q_lo;
+  if (a.block_table) {
+    u.lk = a.seq_lens_kv[u.b];
+    u.kv_off = 0;
+  } else {
+    u.kv_off = a.cu_seqlens_kv[u.b];
+    u.lk = a.cu_seqlens_kv[u.b + 1] - (int)u.kv_off;
+  }
+  u.q_end = u.lq - qt * u.tq;
+  u.q_begin = max(0, u.q_end - u.tq);
+  return u.q_end > 0;
+}
+
 }  // namespace
 }  // namespace attn
