@@ -38,6 +38,7 @@ MUTATIONS = [
     ("widen_e4m3fn(v_codes, v_scale), cu_seqlens_q", "widen_e4m3fn(v_codes, k_scale), cu_seqlens_q"),  # FP8 V scale
     ("return prefill_dense(widen_e4m3fn(q_codes, q_scale), widen_e4m3fn(k_codes, k_scale),",
      "return prefill_dense(widen_e4m3fn(q_codes, 1.0), widen_e4m3fn(k_codes, k_scale),"),  # FP8 q scale dropped
+    ("for n in members]), q_format, q_scale)", "for n in members]), q_format)"),   # decode q scale dropped
     ("rows.append(cache[physical, :take, head, :width])",
      "rows.append(cache[physical, :page_size, head, :width][:take])"),             # harmless: must survive
 ]
