@@ -82,7 +82,22 @@ struct PpGeom {
   // distinct per-lane offsets: instruction k starts at row (k kW + wave) kRowsPerInst
   // and the swizzle repeats every 16 rows
   static constexpr int kLaneOffs = (kW * kRowsPerInst >= 16) ? 1 : 16 / (kW * kRowsPerInst);
+  // Distinct LDS operand offsets per lane: the row swizzle permutes 16-byte
+  // chunks within aligned groups of 16 (256 bytes), so K k-steps kb and
+  // kb + 8 (and V channel blocks nb and nb + 4) differ by exactly 256 bytes.
+  static constexpr int kKOffs = kKB > 8 ? 8 : kKB;
+  static constexpr int kVOffs = kNB > 4 ? 4 : kNB;
 };
+
+// LDS byte offsets of K k-step kb and of V channel block nb for this lane.
+template <int D>
+__device__ __forceinline__ int pp_koff(const int (&koff)[PpGeom<D>::kKOffs], int kb) {
+  return koff[kb % PpGeom<D>::kKOffs] + (kb / PpGeom<D>::kKOffs) * 256;
+}
+template <int D>
+__device__ __forceinline__ int pp_voff(const int (&voff)[PpGeom<D>::kVOffs], int nb) {
+  return voff[nb % PpGeom<D>::kVOffs] + (nb / PpGeom<D>::kVOffs) * 256;
+}
 
 // How K/V rows are addressed: dense, paged with pages of at least one tile
 // (a tile then lies inside one page), or paged with smaller pages.
@@ -190,14 +205,15 @@ __device__ __forceinline__ void pp_fetch_pages(const int32_t *bt_row, int j0, in
 // S^T for the 64 keys of a resident K tile: two 32-key blocks, 16 scores of
 // this lane's row each.
 template <int D>
-__device__ __forceinline__ void pp_scores(const char *kbytes, const int (&koff)[PpGeom<D>::kKB],
+__device__ __forceinline__ void pp_scores(const char *kbytes, const int (&koff)[PpGeom<D>::kKOffs],
                                           const bf16x8 (&qop)[PpGeom<D>::kKB], f32x16 (&s)[2]) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     s[sub] = f32x16{};
 #pragma unroll
     for (int kb = 0; kb < PpGeom<D>::kKB; ++kb)
-      s[sub] = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(kbytes + koff[kb] + sub * 32 * D * 2), qop[kb], s[sub]);
+      s[sub] = mfma32x32x16(*reinterpret_cast<const bf16x8 *>(kbytes + pp_koff<D>(koff, kb) + sub * 32 * D * 2),
+                            qop[kb], s[sub]);
   }
 }
 
@@ -226,7 +242,7 @@ __device__ __forceinline__ void pp_mask(f32x16 (&s)[2], int j0, int begin, int b
 template <int D>
 __device__ __forceinline__ void pp_step(f32x16 (&s)[2], float &mx, float m_use, float c, float alpha, float &lsum,
                                         f32x16 (&oacc)[PpGeom<D>::kNB], const char *knext, const char *vbytes,
-                                        const int (&koff)[PpGeom<D>::kKB], const int (&voff)[2][PpGeom<D>::kNB],
+                                        const int (&koff)[PpGeom<D>::kKOffs], const int (&voff)[2][PpGeom<D>::kVOffs],
                                         const bf16x8 (&qop)[PpGeom<D>::kKB]) {
   using G = PpGeom<D>;
   if constexpr (G::kRing == 0) {
@@ -246,8 +262,8 @@ __device__ __forceinline__ void pp_step(f32x16 (&s)[2], float &mx, float m_use, 
     for (int kk = 0; kk < G::kKK; ++kk)
 #pragma unroll
       for (int nb = 0; nb < G::kNB; ++nb) {
-        const bf16x4 lo = lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2);
-        const bf16x4 hi = lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2);
+        const bf16x4 lo = lds_read_tr16(vbytes + pp_voff<D>(voff[0], nb) + kk * 16 * D * 2);
+        const bf16x4 hi = lds_read_tr16(vbytes + pp_voff<D>(voff[1], nb) + kk * 16 * D * 2);
         oacc[nb] = mfma32x32x16(concat(lo, hi), pop[kk], oacc[nb]);
       }
     lsum = alpha * lsum + (ps[0] + ps[1]);
@@ -267,10 +283,10 @@ __device__ __forceinline__ void pp_step(f32x16 (&s)[2], float &mx, float m_use, 
     constexpr int kMaxPer = 32 / kPV;
     auto rd = [&](int t) -> bf16x8 {
       if (t < kQK)
-        return *reinterpret_cast<const bf16x8 *>(knext + koff[t % G::kKB] + (t / G::kKB) * 32 * D * 2);
+        return *reinterpret_cast<const bf16x8 *>(knext + pp_koff<D>(koff, t % G::kKB) + (t / G::kKB) * 32 * D * 2);
       const int u = t - kQK, kk = u / G::kNB, nb = u % G::kNB;
-      return concat(lds_read_tr16(vbytes + voff[0][nb] + kk * 16 * D * 2),
-                    lds_read_tr16(vbytes + voff[1][nb] + kk * 16 * D * 2));
+      return concat(lds_read_tr16(vbytes + pp_voff<D>(voff[0], nb) + kk * 16 * D * 2),
+                    lds_read_tr16(vbytes + pp_voff<D>(voff[1], nb) + kk * 16 * D * 2));
     };
     bf16x8 ring[kR];
 #pragma unroll
@@ -372,20 +388,20 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
       qop[kb] = row_valid ? __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, load_bf16x8(qrow + kb * 16 + h * 8)) ^ qsign)
                           : bf16x8{};
   }
-  int koff[G::kKB];
+  int koff[G::kKOffs];
   {
     const int hf = h ^ pf_swz<D>(r32);
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) koff[kb] = r32 * D * 2 + ((2 * kb) ^ hf) * 16;
+    for (int kb = 0; kb < G::kKOffs; ++kb) koff[kb] = r32 * D * 2 + ((2 * kb) ^ hf) * 16;
   }
-  int voff[2][G::kNB];
+  int voff[2][G::kVOffs];
   {
     const int s16 = lane & 15;
     const int row0 = 4 * h + (s16 >> 2);
     const int cb = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
     const int f0 = pf_swz<D>(row0), f1 = pf_swz<D>(row0 + 8);
 #pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) {
+    for (int nb = 0; nb < G::kVOffs; ++nb) {
       voff[0][nb] = row0 * D * 2 + ((4 * nb + cb) ^ f0) * 16 + 8 * (s16 & 1);
       voff[1][nb] = (row0 + 8) * D * 2 + ((4 * nb + cb) ^ f1) * 16 + 8 * (s16 & 1);
     }
@@ -445,9 +461,9 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
   auto tile_step = [&](int it, auto par_c) {
     constexpr int par = decltype(par_c)::value;
 #pragma unroll
-    for (int kb = 0; kb < G::kKB; ++kb) asm volatile("" : "+v"(koff[kb]));
+    for (int kb = 0; kb < G::kKOffs; ++kb) asm volatile("" : "+v"(koff[kb]));
 #pragma unroll
-    for (int nb = 0; nb < G::kNB; ++nb) asm volatile("" : "+v"(voff[0][nb]), "+v"(voff[1][nb]));
+    for (int nb = 0; nb < G::kVOffs; ++nb) asm volatile("" : "+v"(voff[0][nb]), "+v"(voff[1][nb]));
     // K(it+1) and V(it) have landed for every wave, and every wave is done
     // with K(it) and V(it-1), whose slots take K(it+2) and V(it+1).
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -464,6 +480,8 @@ __global__ __launch_bounds__(64 * PpGeom<D>::kW, PpGeom<D>::kWPE) void prefill_p
     // mask clears the stale scores, the step adds nothing and computes the
     // scores of tile it0. (0 <= it0 < ntw when ntw > 0: a valid row's first
     // key lies below its bound; one unsigned compare tests it0 - 1 <= it < ntw.)
+    // Stepping every wave through every tile instead (masked whole) ran 3-4 %
+    // slower at D = 256.
     if ((unsigned)(it + 1 - it0) < (unsigned)(ntw + 1 - it0)) {
       if (j0 + G::kN > valid_min || j0 < begin_max) {
         pp_mask(s, j0, begin, bound, h);
