@@ -33,7 +33,7 @@ def _shape(seed):
                 seed=2000 + seed, causal=causal, layout="random"), rng
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_decode_with_and_without_the_total_hint(seed):
     kw, rng = _shape(seed)
     case = inputs.decode_case(**kw)
@@ -48,7 +48,8 @@ def test_random_decode_with_and_without_the_total_hint(seed):
                               softmax_scale=c.scale, causal=c.causal, total_kv_tokens=total)
         plan = sap.decode_plan(p)
         print(f"seed {seed} b{b} q{q_len} hq{hq}/{kw['hkv']} d{kw['d']} page {kw['page_size']} max "
-              f"{max(kw['seq_lens'])} total {total}: {plan['num_splits']} x {plan['split_tokens']}", flush=True)
+              f"{max(kw['seq_lens'])} total {total}: {plan['num_splits']} x {plan['split_tokens']}, "
+              f"{plan['key_ranges']} key ranges", flush=True)
         out, lse = sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
                                     softmax_scale=c.scale, causal=c.causal, return_lse=True, total_kv_tokens=total)
         out, lse = out.cpu(), lse.cpu()

@@ -36,7 +36,7 @@ def _case(seed):
     return case, splits
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_prefill(seed):
     case, splits = _case(seed)
     c = case.to(DEV)
