@@ -180,3 +180,30 @@ def test_static_anchor_second_restart(kv_dtype, splits):
             case.k_cache[page, j % 64, 0] = codes.view(torch.uint8)
     print("second restart", kv_dtype, splits, flush=True)
     print(_check(case, splits))
+
+
+def _random_mla_shape(seed):
+    rng = np.random.default_rng(3000 + seed)
+    batch = int(rng.integers(1, 9))
+    q_len = int(rng.integers(1, 5))
+    hq = int(rng.choice([8, 16, 32, 64, 128]))
+    max_len = int(rng.choice([40, 700, 3000, 12000]))
+    lens = rng.integers(0, max_len + 1, size=batch).tolist()
+    lens[int(rng.integers(batch))] = max_len              # one request at the bound
+    return dict(batch=batch, q_len=q_len, hq=hq, hkv=1, d=576, dv=512, page_size=int(rng.choice([16, 64, 128])),
+                seq_lens=lens, seed=4000 + seed, latent=True, scale=0.07216882, causal=bool(rng.integers(2)),
+                layout="random", **_dt(DTYPES[seed % len(DTYPES)]))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_latent_decode(seed):
+    """Seeded random batches, lengths, query tokens, head counts (folded
+    tokens F = 1, 2 or 4 per 128-row unit), page sizes and causality, in all
+    three dtypes, planned and with forced splits, every row against the
+    oracle."""
+    kw = _random_mla_shape(seed)
+    case = inputs.decode_case(**kw)
+    print(f"seed {seed}: b{kw['batch']} q{kw['q_len']} hq{kw['hq']} page {kw['page_size']} max "
+          f"{max(kw['seq_lens'])} causal {kw['causal']} {kw['kv_dtype']}/{kw['q_dtype']}", flush=True)
+    for splits in (0, 2):
+        print(_check(case, splits))
