@@ -183,7 +183,7 @@ def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_
 def _prefill_params(q, k, v, cu_seqlens_q, out, lse, max_seqlen_q, max_seqlen_kv, softmax_scale, causal,
                     cu_seqlens_kv, seq_lens_kv, block_table, window_left, q_scale, k_scale, v_scale, kv_splits):
     fp8 = q.dtype == torch.float8_e4m3fn
-    _need(q.is_cuda and q.dtype in (_BF16, torch.float8_e4m3fn) and q.stride(2) == 1,
+    _need(q.is_cuda and q.dtype in (_BF16, torch.float8_e4m3fn) and (q.stride(2) == 1 or q.numel() == 0),
           "q must be bf16 or float8_e4m3fn CUDA with contiguous channels")
     _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k and v must share one dtype")
     _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous(), "cu_seqlens_q must be contiguous int32")

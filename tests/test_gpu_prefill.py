@@ -95,6 +95,16 @@ def test_constant_v_and_single_key():
         assert abs(float(lse[0, h]) - s / np.log(2.0)) < 1e-3
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_batch_without_queries(paged):
+    # every request has keys but no query token: nothing to compute, an
+    # empty result, no error (dense and paged)
+    case = inputs.prefill_case(q_lens=[0, 0, 0], kv_lens=[5, 300, 0], hq=4, hkv=2, d=128, seed=17, causal=True,
+                               paged=paged, page_size=16)
+    out, lse = _run(case)
+    assert tuple(out.shape) == (0, 4, 128) and tuple(lse.shape) == (0, 4)
+
+
 def test_negative_scale():
     case = inputs.prefill_case(q_lens=[33, 70], kv_lens=[100, 70], hq=4, hkv=2, d=128, seed=53, causal=True,
                                scale=-0.09)

@@ -82,3 +82,22 @@ def test_fp8_mla_prefill_8k_sampled():
     got = np.stack([f64(out[t, hh]) for t, hh in rows])
     glse = np.array([float(lse[t, hh]) for t, hh in rows])
     print(compare(got, ref, glse, lref, TOL_BF16))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_fp8_prefill(seed):
+    """Seeded random ragged batches: request count, query and key lengths
+    (chunks over histories, empty and one-token requests), head groups,
+    causality and windows, every row against the oracle."""
+    rng = np.random.default_rng(5000 + seed)
+    batch = int(rng.integers(1, 7))
+    q_lens = [int(x) for x in rng.integers(0, 700, size=batch)]
+    kv_lens = [q + int(rng.integers(0, 900)) for q in q_lens]
+    q_lens[int(rng.integers(batch))] = int(rng.choice([0, 1]))
+    hq, hkv = [(4, 4), (8, 2), (16, 16), (6, 3)][int(rng.integers(4))]
+    causal = bool(rng.integers(2))
+    window = int(rng.choice([-1, -1, 0, 100, 700]))
+    case = inputs.fp8_prefill_case(q_lens=q_lens, kv_lens=kv_lens, hq=hq, hkv=hkv, seed=6000 + seed, causal=causal,
+                                   window_left=window)
+    print(f"seed {seed}: q {q_lens} kv {kv_lens} h {hq}/{hkv} causal {causal} window {window}", _check(case),
+          flush=True)
