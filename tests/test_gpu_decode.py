@@ -295,3 +295,33 @@ def test_merge_lse_matches_oracle(s, r, dv):
     ob, _ = sap.merge_lse(o_parts.to(DEV), lse_parts.to(DEV), out_dtype=torch.bfloat16)
     compare(f64(ob.cpu()), ref)
     print(res)
+
+
+@pytest.mark.parametrize("latent", [False, True])
+def test_no_request_has_keys(latent):
+    # every request empty: O = 0 and LSE = -inf exactly, planned and forced
+    # split (a one-page pool, as a cache that has not been written yet)
+    kw = dict(batch=3, q_len=2, page_size=16, seq_lens=[0, 0, 0], seed=23, pool_pages=1, max_pages=1)
+    if latent:
+        case = inputs.decode_case(hq=64, hkv=1, d=576, dv=512, latent=True, scale=0.07216882, **kw)
+    else:
+        case = inputs.decode_case(hq=8, hkv=2, d=128, dv=128, **kw)
+    for splits in (0, 2):
+        c = case.to(DEV)
+        out, lse = sap.decode_paged(c.q, c.k_cache, None if latent else c.v_cache, c.block_table, c.seq_lens,
+                                    max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal,
+                                    head_dim_v=c.head_dim_v, num_splits=splits, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu().float(), torch.zeros(out.shape))
+        assert bool(torch.all(lse.cpu() == float("-inf")))
+
+
+def test_empty_batch():
+    # batch 0: nothing to compute, empty outputs, no error
+    q = torch.empty((0, 1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((1, 16, 2, 128), dtype=torch.bfloat16, device=DEV)
+    bt = torch.zeros((0, 1), dtype=torch.int32, device=DEV)
+    sl = torch.zeros((0,), dtype=torch.int32, device=DEV)
+    out, lse = sap.decode_paged(q, k, k.clone(), bt, sl, max_seq_len=16, softmax_scale=0.1, return_lse=True)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 1, 8, 128) and tuple(lse.shape) == (0, 1, 8)
