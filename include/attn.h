@@ -81,6 +81,9 @@ typedef enum {
  *   cu_seqlens_q   int32 [batch + 1], request b owns query rows
  *                  cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1.
  *   max_seqlen_q, max_seqlen_kv   host upper bounds of the per-request lengths.
+ *                  With max_seqlen_kv == 0 no row sees a key (O = 0, LSE =
+ *                  -inf) and k, v (and, paged, the pages) may be empty/NULL;
+ *                  with max_seqlen_q == 0 the call does nothing.
  *   causal         0 or 1 (bottom-right aligned).
  *   o      bf16 [total_q, Hq, Dv], strides o_stride_tok / o_stride_head.
  *   lse    optional float32 [total_q, Hq] contiguous, base 2; NULL to skip.

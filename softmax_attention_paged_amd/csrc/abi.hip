@@ -342,31 +342,38 @@ attn_status_t validate_prefill(const attn_prefill_params *p, bool shapes_only = 
   if (p->window_enabled && p->window_left < 0)
     return fail(ATTN_ERR_INVALID_ARG, "window_left %d < 0", p->window_left);
   const bool paged = p->block_table != nullptr;
+  // No request has a key (max_seqlen_kv == 0): every row is empty (O = 0,
+  // LSE = -inf) and K/V are never read, so they may be empty and NULL.
+  const bool any_keys = p->max_seqlen_kv > 0;
   if (paged) {
     if (!pow2(p->page_size) || p->page_size < 16)
       return fail(ATTN_ERR_UNSUPPORTED, "page_size %d is not a power of two >= 16", p->page_size);
-    if (p->num_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", p->num_pages);
+    if (any_keys && p->num_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", p->num_pages);
     if ((int64_t)p->max_seqlen_kv > (int64_t)p->num_pages * p->page_size)
       return fail(ATTN_ERR_INVALID_ARG, "max_seqlen_kv exceeds num_pages * page_size");
     if (p->block_table_stride < cdiv(p->max_seqlen_kv, p->page_size))
       return fail(ATTN_ERR_INVALID_ARG, "block_table_stride %d < pages of max_seqlen_kv", p->block_table_stride);
   }
   if (shapes_only || p->batch == 0 || p->max_seqlen_q == 0) return ok();
-  if (!p->q || !p->k || !p->v || !p->cu_seqlens_q || !p->o)
+  if (!p->q || !p->cu_seqlens_q || !p->o || (any_keys && (!p->k || !p->v)))
     return fail(ATTN_ERR_INVALID_ARG, "a required pointer (q, k, v, cu_seqlens_q, o) is NULL");
   if (paged ? !p->seq_lens_kv : !p->cu_seqlens_kv)
     return fail(ATTN_ERR_INVALID_ARG, paged ? "paged mode needs seq_lens_kv" : "dense mode needs cu_seqlens_kv");
-  if (!aligned16(p->q) || !aligned16(p->k) || !aligned16(p->v) || !aligned16(p->o))
+  if (!aligned16(p->q) || !aligned16(p->o) || (any_keys && (!aligned16(p->k) || !aligned16(p->v))))
     return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
   // every stride a multiple of 16 bytes (elements of 2 bytes, or of 1 byte for FP8 inputs)
   const int64_t in_bytes = fp8 ? 1 : 2;
-  const int64_t strides[] = {p->q_stride_tok * in_bytes, p->q_stride_head * in_bytes, p->k_stride_tok * in_bytes,
-                             p->k_stride_head * in_bytes, p->v_stride_tok * in_bytes, p->v_stride_head * in_bytes,
-                             p->o_stride_tok * 2, p->o_stride_head * 2,
-                             paged ? p->k_stride_page * in_bytes : 16, paged ? p->v_stride_page * in_bytes : 16};
+  const int64_t kv_strides[] = {p->k_stride_tok * in_bytes, p->k_stride_head * in_bytes, p->v_stride_tok * in_bytes,
+                                p->v_stride_head * in_bytes, paged ? p->k_stride_page * in_bytes : 16,
+                                paged ? p->v_stride_page * in_bytes : 16};
+  const int64_t strides[] = {p->q_stride_tok * in_bytes, p->q_stride_head * in_bytes, p->o_stride_tok * 2,
+                             p->o_stride_head * 2};
   for (int64_t st : strides)
     if (st < 0 || st % 16) return fail(ATTN_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
-  if (p->q_stride_tok < 1 || p->k_stride_tok < 1 || p->v_stride_tok < 1 || p->o_stride_tok < 1)
+  if (any_keys)
+    for (int64_t st : kv_strides)
+      if (st < 0 || st % 16) return fail(ATTN_ERR_INVALID_ARG, "strides must be non-negative multiples of 16 bytes");
+  if (p->q_stride_tok < 1 || p->o_stride_tok < 1 || (any_keys && (p->k_stride_tok < 1 || p->v_stride_tok < 1)))
     return fail(ATTN_ERR_INVALID_ARG, "token strides must be positive");
   return ok();
 }

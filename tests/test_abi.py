@@ -203,6 +203,12 @@ def prefill_params(**kw):
      _ffi.ATTN_ERR_INVALID_ARG),
     (dict(q_stride_head=100), _ffi.ATTN_ERR_INVALID_ARG),
     (dict(causal=3), _ffi.ATTN_ERR_INVALID_ARG),
+    # K/V may be empty only when no request has a key (max_seqlen_kv == 0)
+    (dict(k=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(v_stride_tok=0), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(k_stride_head=100), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(block_table=FAKE, seq_lens_kv=FAKE, page_size=64, num_pages=0, block_table_stride=1000),
+     _ffi.ATTN_ERR_INVALID_ARG),
 ])
 def test_prefill_validation_errors(kw, code):
     lib = _lib()

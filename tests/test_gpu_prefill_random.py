@@ -49,3 +49,27 @@ def test_random_prefill(seed):
     out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, **kv, **kw)
     ref, lref = oracle_prefill(case)
     print(compare(f64(out.cpu()), ref, lse.cpu().numpy(), lref))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefill_short_histories(seed):
+    """Key lengths drawn apart from the query lengths: requests with fewer
+    keys than queries (bottom-right causal rows that see no key: O = 0, LSE =
+    -inf) and requests with no keys at all, causal or not, dense or paged."""
+    rng = np.random.default_rng(7000 + seed)
+    batch = int(rng.integers(1, 6))
+    q_lens = rng.integers(1, 300, size=batch).tolist()
+    kv_lens = rng.integers(0, 400, size=batch).tolist()
+    kv_lens[int(rng.integers(batch))] = 0
+    hkv, group = int(rng.choice([1, 2])), int(rng.choice([1, 4]))
+    case = inputs.prefill_case(q_lens=q_lens, kv_lens=kv_lens, hq=hkv * group, hkv=hkv, d=int(rng.choice([64, 128])),
+                               seed=8000 + seed, causal=bool(rng.integers(2)), paged=bool(rng.integers(2)),
+                               page_size=16, name=f"short-{seed}")
+    c = case.to(DEV)
+    kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale, causal=c.causal,
+              return_lse=True, kv_splits=int(rng.choice([0, 2])))
+    kv = dict(seq_lens_kv=c.seq_lens_kv, block_table=c.block_table) if c.paged else dict(cu_seqlens_kv=c.cu_seqlens_kv)
+    print(f"seed {seed}: q {q_lens} kv {kv_lens} causal {c.causal} paged {c.paged}", flush=True)
+    out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, **kv, **kw)
+    ref, lref = oracle_prefill(case)
+    print(compare(f64(out.cpu()), ref, lse.cpu().numpy(), lref))
