@@ -191,7 +191,9 @@ attn_status_t attn_prefill(const attn_prefill_params *p, hipStream_t stream);
  *              for bf16. An MLA-shaped FP8 cache needs k_scale == v_scale.
  *   seq_lens   int32 [batch]: keys of each request (0 allowed).
  *   block_table int32, row b at block_table + b * block_table_stride.
- *   max_seq_len host upper bound of seq_lens; plans the split count.
+ *   max_seq_len host upper bound of seq_lens; plans the split count. With
+ *              max_seq_len == 0 no row sees a key (O = 0, LSE = -inf) and the
+ *              caches and block_table may be empty/NULL (num_pages 0).
  *   q_len      1..4 query tokens per request; row (t, h) of a causal request
  *              sees keys j <= seq_len - q_len + t.
  *   num_splits 0 lets the planner choose; otherwise the number of KV splits

@@ -116,8 +116,12 @@ attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) 
                 p->num_q_heads, p->num_kv_heads);
   if (!pow2(p->page_size) || p->page_size < 16)
     return fail(ATTN_ERR_UNSUPPORTED, "page_size %d is not a power of two >= 16", p->page_size);
-  if (p->num_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", p->num_pages);
   if (p->max_seq_len < 0) return fail(ATTN_ERR_INVALID_ARG, "max_seq_len %d < 0", p->max_seq_len);
+  // No request has a key (max_seq_len == 0): every row is empty (O = 0, LSE
+  // = -inf) and neither the caches nor the block table are read, so they may
+  // be empty and NULL.
+  const bool any_keys = p->max_seq_len > 0;
+  if (any_keys && p->num_pages < 1) return fail(ATTN_ERR_INVALID_ARG, "num_pages %d < 1", p->num_pages);
   if ((int64_t)p->max_seq_len > (int64_t)p->num_pages * p->page_size)
     return fail(ATTN_ERR_INVALID_ARG, "max_seq_len %d exceeds num_pages * page_size", p->max_seq_len);
   if (p->block_table_stride < cdiv(p->max_seq_len, p->page_size))
@@ -168,9 +172,11 @@ attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) 
   }
 
   if (p->batch == 0 || !check_pointers) return ok();
-  if (!p->q || !p->k_cache || !p->v_cache || !p->seq_lens || !p->block_table || !p->o)
+  if (!p->q || !p->seq_lens || !p->o || (any_keys && (!p->k_cache || !p->v_cache || !p->block_table)))
     return fail(ATTN_ERR_INVALID_ARG, "a required pointer (q, k_cache, v_cache, seq_lens, block_table, o) is NULL");
-  if (!aligned16(p->q) || !aligned16(p->k_cache) || !aligned16(p->v_cache) || !aligned16(p->o))
+  if (!aligned16(p->q) || !aligned16(p->o)) return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
+  if (!any_keys) return ok();
+  if (!aligned16(p->k_cache) || !aligned16(p->v_cache))
     return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
   const int esz = (p->kv_dtype == ATTN_FP8_E4M3) ? 1 : 2;
   const int64_t strides[6] = {p->k_stride_page, p->k_stride_tok, p->k_stride_head,

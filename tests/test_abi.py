@@ -139,6 +139,11 @@ def plan(p):
     (dict(window_enabled=1, window_left=-3), _ffi.ATTN_ERR_INVALID_ARG),
     (dict(q_dtype=7), _ffi.ATTN_ERR_INVALID_ARG),
     (dict(q_dtype=_ffi.ATTN_FP8_E4M3, q_scale=1.0), _ffi.ATTN_ERR_UNSUPPORTED),    # fp8 q needs an fp8 latent cache
+    # the caches and the block table may be empty only when no request has a key
+    (dict(k_cache=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(block_table=None), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(num_pages=0), _ffi.ATTN_ERR_INVALID_ARG),
+    (dict(v_cache=FAKE + 8), _ffi.ATTN_ERR_INVALID_ARG),
 ])
 def test_decode_validation_errors(kw, code):
     lib = _lib()

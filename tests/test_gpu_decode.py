@@ -297,11 +297,13 @@ def test_merge_lse_matches_oracle(s, r, dv):
     print(res)
 
 
+@pytest.mark.parametrize("pool", [1, 0])
 @pytest.mark.parametrize("latent", [False, True])
-def test_no_request_has_keys(latent):
+def test_no_request_has_keys(latent, pool):
     # every request empty: O = 0 and LSE = -inf exactly, planned and forced
-    # split (a one-page pool, as a cache that has not been written yet)
-    kw = dict(batch=3, q_len=2, page_size=16, seq_lens=[0, 0, 0], seed=23, pool_pages=1, max_pages=1)
+    # split (a one-page pool, as a cache that has not been written yet, or
+    # an empty cache)
+    kw = dict(batch=3, q_len=2, page_size=16, seq_lens=[0, 0, 0], seed=23, pool_pages=pool, max_pages=1)
     if latent:
         case = inputs.decode_case(hq=64, hkv=1, d=576, dv=512, latent=True, scale=0.07216882, **kw)
     else:
