@@ -327,3 +327,11 @@ def test_empty_batch():
     out, lse = sap.decode_paged(q, k, k.clone(), bt, sl, max_seq_len=16, softmax_scale=0.1, return_lse=True)
     torch.cuda.synchronize()
     assert tuple(out.shape) == (0, 1, 8, 128) and tuple(lse.shape) == (0, 1, 8)
+
+
+def test_merge_lse_without_rows():
+    o_parts = torch.empty((3, 0, 128), dtype=torch.float32, device=DEV)
+    lse_parts = torch.empty((3, 0), dtype=torch.float32, device=DEV)
+    o, lse = sap.merge_lse(o_parts, lse_parts)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (0, 128) and tuple(lse.shape) == (0,)

@@ -173,3 +173,12 @@ def test_quantiser_on_every_bf16_value(scale):
     rope = torch.from_numpy(pats[: t * 64].view(np.int16).reshape(t, 64)).view(torch.bfloat16)
     case = inputs.PackCase(name="all-bf16", k_nope=nope, k_rope=rope, v=v, k_scale=scale, v_scale=scale, seed=0)
     _check_pack(case)
+
+
+def test_pack_zero_tokens_is_a_no_op():
+    k_nope = torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV)
+    k_rope = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV)
+    k_out, v_out = sap.mla_kv_pack_fp8(k_nope, k_rope, v, k_scale=0.5, v_scale=0.25)
+    torch.cuda.synchronize()
+    assert tuple(k_out.shape) == (0, 4, 192) and tuple(v_out.shape) == (0, 4, 128)
