@@ -126,3 +126,35 @@ def test_prefill_window_paged(page_size, window):
                                layout="noncontiguous", window_left=window)
     print("prefill window paged", page_size, window, flush=True)
     _prefill(case)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_decode_window_and_packing(seed):
+    """Seeded random GQA and latent decodes with windows (from 0 to wider
+    than the history), packed or folded query rows, 1-4 query tokens, causal
+    or not, planned or with forced splits."""
+    import numpy as np
+    rng = np.random.default_rng(9000 + seed)
+    latent = bool(rng.integers(2))
+    batch = int(rng.integers(1, 12))
+    q_len = int(rng.integers(1, 5))
+    max_len = int(rng.choice([50, 600, 4000]))
+    lens = rng.integers(0, max_len + 1, size=batch).tolist()
+    window = int(rng.choice([0, 1, 31, 77, 300, 5000]))
+    packed = bool(rng.integers(2))
+    causal = bool(rng.integers(2))
+    if latent:
+        hq = int(rng.choice([16, 32, 96, 128]))
+        case = inputs.decode_case(batch=batch, q_len=q_len, hq=hq, hkv=1, d=576, dv=512, page_size=64,
+                                  seq_lens=lens, seed=9500 + seed, latent=True, scale=0.07216882, causal=causal,
+                                  window_left=window, packed_q=packed, layout="random")
+    else:
+        hkv = int(rng.choice([1, 2, 4]))
+        hq = hkv * int(rng.choice([1, 3, 5, 8]))
+        d = int(rng.choice([64, 128]))
+        case = inputs.decode_case(batch=batch, q_len=q_len, hq=hq, hkv=hkv, d=d, dv=d,
+                                  page_size=int(rng.choice([16, 128])), seq_lens=lens, seed=9500 + seed,
+                                  causal=causal, window_left=window, packed_q=packed, layout="random")
+    splits = int(rng.choice([0, 0, 3]))
+    print(f"seed {seed}: latent {latent} b{batch} q{q_len} hq{hq} window {window} packed {packed} causal {causal} "
+          f"splits {splits}", _decode(case, splits), flush=True)
