@@ -97,3 +97,45 @@ def test_split_prefill_graph_replays_match_eager():
         if i == 0:
             ref, _ = oracle_prefill(case)
             print(compare(f64(got), ref))
+
+
+def test_concurrent_calls_on_two_streams_with_their_own_workspaces():
+    """The library keeps no state between calls: two key-range decodes with
+    split partials, each on its own stream and workspace and running at the
+    same time, give the same bits as each run alone."""
+    cases = [inputs.decode_case(batch=24, q_len=1, hq=16, hkv=4, d=128, dv=128, page_size=64,
+                                seq_len_range=(100, 6000), seed=s, layout="random") for s in (41, 42)]
+    devs = [c.to("cuda") for c in cases]
+
+    def call(c, ws, out, lse):
+        tokens = int(c.seq_lens.sum())
+        sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
+                         softmax_scale=c.scale, workspace=ws, out=out, lse=lse, total_kv_tokens=tokens)
+
+    bufs = []
+    for c in devs:
+        plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
+                                                 max_seq_len=c.max_seq_len, softmax_scale=c.scale,
+                                                 total_kv_tokens=int(c.seq_lens.sum())))
+        assert plan["key_ranges"] > 1 and plan["workspace_bytes"] > 0
+        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+        out = torch.empty((c.q.shape[0], 1, 16, 128), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((c.q.shape[0], 1, 16), dtype=torch.float32, device="cuda")
+        bufs.append((ws, out, lse))
+    alone = []
+    for c, (ws, out, lse) in zip(devs, bufs):
+        call(c, ws, out, lse)
+        torch.cuda.synchronize()
+        alone.append((out.clone(), lse.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(5):
+        for c, (ws, out, lse), st in zip(devs, bufs, streams):
+            with torch.cuda.stream(st):
+                call(c, ws, out, lse)
+        torch.cuda.synchronize()
+        for (out, lse), (o0, l0) in zip([(b[1], b[2]) for b in bufs], alone):
+            assert torch.equal(out.view(torch.int16), o0.view(torch.int16)) and torch.equal(lse, l0)
+    for c, case, (o0, l0) in zip(devs, cases, alone):
+        ref, lref = oracle_decode(case)
+        print(compare(f64(o0.cpu()), ref, l0.cpu().numpy(), lref))
