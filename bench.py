@@ -305,6 +305,7 @@ def ceilings_lib():
     lib = ctypes.CDLL(path)
     lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_mfma_bf16_varied.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -329,7 +330,9 @@ class Evictor:
 
 def measured_peaks() -> dict:
     """Ceilings measured on this GPU, as secondary denominators: a 1 GiB
-    streaming read and a bf16 32x32x16 MFMA loop (the ceiling kernels), and
+    streaming read and a bf16 32x32x16 MFMA loop (the ceiling kernels; the
+    loop once with fixed operands and once with operands that change every
+    instruction, as a real contraction's do), and
     for context a 1 GiB torch copy (bytes read + written) and a bf16 8192^3
     GEMM through torch.matmul (hipBLASLt)."""
     import torch
@@ -349,10 +352,15 @@ def measured_peaks() -> dict:
         if lib.ceil_mfma_bf16(sink.data_ptr(), iters, blocks, stream.cuda_stream) != 0:
             raise RuntimeError("ceil_mfma_bf16 failed")
 
-    for f in (read, mfma):
+    def mfma_varied():
+        if lib.ceil_mfma_bf16_varied(sink.data_ptr(), iters, blocks, stream.cuda_stream) != 0:
+            raise RuntimeError("ceil_mfma_bf16_varied failed")
+
+    for f in (read, mfma, mfma_varied):
         f()
     read_ms = time_events(read, 10, stream)
     mfma_ms = time_events(mfma, 5, stream)
+    varied_ms = time_events(mfma_varied, 5, stream)
     y = torch.empty_like(x)
     y.copy_(x)
     copy_ms = time_events(lambda: y.copy_(x), 10, stream)
@@ -369,6 +377,7 @@ def measured_peaks() -> dict:
     mfma_flops = blocks * 4 * iters * 4 * 32768
     return {"stream_read_GBs": round((1 << 30) / (read_ms * 1e-3) / 1e9, 1),
             "mfma_bf16_loop_TFLOPs": round(mfma_flops / (mfma_ms * 1e-3) / 1e12, 1),
+            "mfma_bf16_loop_varied_operands_TFLOPs": round(mfma_flops / (varied_ms * 1e-3) / 1e12, 1),
             "torch_copy_GBs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
             "hipblaslt_bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
 

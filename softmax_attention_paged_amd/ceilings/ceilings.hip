@@ -15,6 +15,14 @@
 //     each wave of `blocks` workgroups of four waves runs 4 * iters
 //     independent-chain MFMAs (32768 flops each); sink holds blocks * 4
 //     floats. Returns 0, -1 on bad arguments, or the HIP error code.
+//   int ceil_mfma_bf16_varied(float *sink, int iters, int blocks, hipStream_t stream);
+//     the same loop with every MFMA taking other operands: each lane holds
+//     eight A and eight B operands of pseudo-random bf16 values (random
+//     signs and mantissas, magnitudes in [0.25, 4)) and the four chains
+//     cycle through them, so the matrix cores' inputs change every
+//     instruction as they do in a real contraction (the loop above feeds the
+//     same two operands to every MFMA). iters must be a positive multiple
+//     of 8; otherwise the same arguments and returns.
 
 #include <hip/hip_runtime.h>
 
@@ -41,6 +49,8 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *__re
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+__device__ __forceinline__ bool lane_is_zero() { return (threadIdx.x & 63) == 0; }
+
 __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float *sink, int iters) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
@@ -62,6 +72,45 @@ __global__ __launch_bounds__(kThreads) void mfma_loop_kernel(float *sink, int it
   if (lane == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+// bf16 bits of a pseudo-random value: sign and mantissa from the hash,
+// exponent so that |value| lies in [0.25, 4).
+__device__ __forceinline__ unsigned short varied_bits(unsigned x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  const unsigned exp = 125u + (x >> 7) % 4u;           // 2^-2 .. 2^1
+  return static_cast<unsigned short>((x & 0x8000u) | (exp << 7) | (x & 0x7fu));
+}
+
+__global__ __launch_bounds__(kThreads) void mfma_varied_kernel(float *sink, int iters) {
+  constexpr int kOps = 8;
+  const unsigned seed = (blockIdx.x * kThreads + threadIdx.x) * 131u;
+  bf16x8 a[kOps], b[kOps];
+#pragma unroll
+  for (int r = 0; r < kOps; ++r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[r][e] = __builtin_bit_cast(__bf16, varied_bits(seed + 16u * r + e));
+      b[r][e] = __builtin_bit_cast(__bf16, varied_bits(~(seed + 16u * r + e)));
+    }
+  f32x16 c0{}, c1{}, c2{}, c3{};
+  for (int i = 0; i < iters; i += kOps) {
+#pragma unroll
+    for (int r = 0; r < kOps; ++r) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[r], b[(r + 1) % kOps], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(r + 2) % kOps], b[(r + 3) % kOps], c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(r + 4) % kOps], b[(r + 5) % kOps], c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(r + 6) % kOps], b[(r + 7) % kOps], c3, 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  if (lane_is_zero()) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,6 +127,12 @@ int ceil_stream_read(const void *src, size_t bytes, unsigned *sink, int blocks, 
 int ceil_mfma_bf16(float *sink, int iters, int blocks, hipStream_t stream) {
   if (!sink || iters < 1 || blocks < 1) return -1;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(kThreads), 0, stream, sink, iters);
+  return static_cast<int>(hipGetLastError());
+}
+
+int ceil_mfma_bf16_varied(float *sink, int iters, int blocks, hipStream_t stream) {
+  if (!sink || iters < 8 || iters % 8 || blocks < 1) return -1;
+  hipLaunchKernelGGL(mfma_varied_kernel, dim3(blocks), dim3(kThreads), 0, stream, sink, iters);
   return static_cast<int>(hipGetLastError());
 }
 

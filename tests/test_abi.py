@@ -48,6 +48,11 @@ def test_ceiling_kernels_library_loads_and_rejects_bad_arguments():
     assert lib.ceil_stream_read(None, 16384, FAKE, 64, None) == -1
     assert lib.ceil_mfma_bf16(FAKE, 0, 8, None) == -1
     assert lib.ceil_mfma_bf16(None, 8, 8, None) == -1
+    lib.ceil_mfma_bf16_varied.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert lib.ceil_mfma_bf16_varied(FAKE, 12, 8, None) == -1       # not a multiple of 8
+    assert lib.ceil_mfma_bf16_varied(FAKE, 0, 8, None) == -1
+    assert lib.ceil_mfma_bf16_varied(None, 8, 8, None) == -1
+    assert lib.ceil_mfma_bf16_varied(FAKE, 8, 0, None) == -1
 
 
 def test_ctypes_mirrors_match_the_c_compiler_layout(tmp_path):
