@@ -64,8 +64,10 @@ struct GqaGeom {
   static constexpr int kChunksPerRow = D / 8;                   // 16-byte chunks per V row
   static constexpr int kVChunks = kTile * kChunksPerRow / 64;   // 16-byte chunks per lane per V tile
   // waves per SIMD the registers are budgeted for: three (twelve streaming
-  // waves per CU) is the best measured for the paged read; D = 128 fits in
-  // 149 VGPRs (167 with a window or packed rows), D = 256 fits two
+  // waves per CU) is the best measured for the per-request split plan, and
+  // the key-range plan launches two; D = 128 fits in 157 VGPRs (168 with a
+  // window or packed rows), D = 256 fits two (with a few registers spilled
+  // outside the tile loop, reloaded once per piece)
   static constexpr int kWPE = D <= 64 ? 4 : (D <= 128 ? 3 : 2);
   static constexpr int kWPEExt = D <= 64 ? 4 : (D <= 128 ? 3 : 1);   // window / packed rows
 };
