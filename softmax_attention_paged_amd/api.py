@@ -31,6 +31,40 @@ def _need(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+def _rows_contiguous(t: torch.Tensor) -> bool:
+    """Channels (the last dimension) adjacent in memory; an empty tensor has
+    no rows to read."""
+    return t.numel() == 0 or t.stride(-1) == 1
+
+
+def _check_out(t: torch.Tensor, shape: tuple, dtypes: tuple, dev: torch.device, name: str) -> None:
+    """A caller-provided output: the kernels write exactly `shape` elements
+    of one of `dtypes`, rows contiguous, on q's device."""
+    _need(t.device == dev, f"{name} must be on {dev}")
+    _need(t.dtype in dtypes, f"{name} must be {' or '.join(str(d) for d in dtypes)}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_decode_inputs(q, k_cache, v_cache, block_table, seq_lens, dv) -> None:
+    """Tensor metadata the C ABI cannot see: devices, ranks and the sizes the
+    kernels index with."""
+    k4 = _as_4d_cache(k_cache)
+    _need(k4.dim() == 4, "k_cache must be [pages, page_size, Hkv, D] or a latent [pages, page_size, D]")
+    for t, name in ((k_cache, "k_cache"), (block_table, "block_table"), (seq_lens, "seq_lens")):
+        _need(t.device == q.device, f"{name} must be on {q.device}")
+    _need(k4.shape[3] == q.shape[3] and _rows_contiguous(k4), "k_cache rows must hold the query's head_dim, contiguous")
+    if v_cache is not None:
+        v4 = _as_4d_cache(v_cache)
+        _need(v_cache.device == q.device, f"v_cache must be on {q.device}")
+        _need(v4.dim() == 4 and tuple(v4.shape[:3]) == tuple(k4.shape[:3]), "v_cache must match k_cache's pages, rows and heads")
+        _need(v4.shape[3] >= dv and _rows_contiguous(v4), "v_cache rows must hold head_dim_v channels, contiguous")
+    else:
+        _need(dv <= k4.shape[3], "a latent cache's V (its first head_dim_v channels) cannot exceed its rows")
+    b = q.shape[0]
+    _need(block_table.dim() == 2 and block_table.shape[0] >= b, "block_table must be [B, max_pages]")
+    _need(seq_lens.dim() == 1 and seq_lens.numel() >= b, "seq_lens must hold B lengths")
+
+
 def _kv_code(cache: torch.Tensor, kv_dtype: str | None) -> int:
     if cache.dtype == _BF16:
         return _ffi.ATTN_BF16
@@ -122,10 +156,16 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_len, sof
     b, q_len, hq, _ = q.shape
     k4 = _as_4d_cache(k_cache)
     dv = head_dim_v if head_dim_v is not None else _as_4d_cache(v_cache if v_cache is not None else k_cache).shape[3]
+    _check_decode_inputs(q, k_cache, v_cache, block_table, seq_lens, dv)
     if out is None:
         out = torch.empty((b, q_len, hq, dv), dtype=_BF16, device=q.device)
-    _need(out.dtype == _BF16 and out.is_contiguous(), "out must be contiguous bf16")
+    _check_out(out, (b, q_len, hq, dv), (_BF16,), q.device, "out")
+    _need(out.is_contiguous(), "out must be contiguous bf16")
+    if lse is not None:
+        _check_out(lse, (b, q_len, hq), (torch.float32,), q.device, "lse")
     _need(lse is None or (lse.dtype == torch.float32 and lse.is_contiguous()), "lse must be contiguous float32")
+    _need(workspace is None or (workspace.device == q.device and workspace.is_contiguous()),
+          f"workspace must be a contiguous tensor on {q.device}")
     if lse is not None:
         return_lse = True
     elif return_lse:
@@ -163,9 +203,13 @@ def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, max_seq_
     _need(block_table.stride(1) == 1 and seq_lens.is_contiguous(), "block_table rows and seq_lens must be contiguous")
     b, q_len, hq, _ = q.shape
     dv = head_dim_v if head_dim_v is not None else _as_4d_cache(v_cache if v_cache is not None else k_cache).shape[3]
+    _check_decode_inputs(q, k_cache, v_cache, block_table, seq_lens, dv)
     if out is None:
         out = torch.empty((b, q_len, hq, dv), dtype=_BF16, device=q.device)
-    _need(out.dtype == _BF16 and out.is_contiguous(), "out must be contiguous bf16")
+    _check_out(out, (b, q_len, hq, dv), (_BF16,), q.device, "out")
+    _need(out.is_contiguous(), "out must be contiguous bf16")
+    if lse is not None:
+        _check_out(lse, (b, q_len, hq), (torch.float32,), q.device, "lse")
     _need(lse is None or (lse.dtype == torch.float32 and lse.is_contiguous()), "lse must be contiguous float32")
     p = decode_params(q, k_cache, v_cache, block_table, seq_lens, max_seq_len=max_seq_len,
                       softmax_scale=softmax_scale, causal=causal, head_dim_v=dv, kv_dtype=kv_dtype,
@@ -190,6 +234,13 @@ def _prefill_params(q, k, v, cu_seqlens_q, out, lse, max_seqlen_q, max_seqlen_kv
     paged = block_table is not None
     tq, hq, dqk = q.shape
     dv = v.shape[-1]
+    _need(k.dim() == (4 if paged else 3) and v.dim() == k.dim(),
+          "k and v must be [pages, page_size, Hkv, D] (paged) or [Tk, Hkv, D] (dense)")
+    for t, name in ((k, "k"), (v, "v"), (cu_seqlens_q, "cu_seqlens_q")):
+        _need(t.device == q.device, f"{name} must be on {q.device}")
+    _need(tuple(v.shape[:-1]) == tuple(k.shape[:-1]), "k and v must match in all but their channels")
+    _need(k.shape[-1] == dqk and _rows_contiguous(k) and _rows_contiguous(v),
+          "k rows must hold the query's head_dim and k, v rows must be contiguous")
     hkv = k.shape[2] if paged else k.shape[1]
     p = _ffi.PrefillParams()
     p.q, p.q_stride_tok, p.q_stride_head = q.data_ptr(), q.stride(0), q.stride(1)
@@ -197,12 +248,18 @@ def _prefill_params(q, k, v, cu_seqlens_q, out, lse, max_seqlen_q, max_seqlen_kv
     if paged:
         _need(block_table.dtype == torch.int32 and block_table.stride(1) == 1, "block_table must be int32 rows")
         _need(seq_lens_kv is not None and seq_lens_kv.dtype == torch.int32, "paged mode needs int32 seq_lens_kv")
+        _need(block_table.device == q.device and seq_lens_kv.device == q.device, f"block_table, seq_lens_kv must be on {q.device}")
+        _need(block_table.dim() == 2 and block_table.shape[0] >= cu_seqlens_q.numel() - 1,
+              "block_table must be [B, max_pages]")
+        _need(seq_lens_kv.numel() >= cu_seqlens_q.numel() - 1, "seq_lens_kv must hold B lengths")
         p.k_stride_page, p.k_stride_tok, p.k_stride_head = k.stride(0), k.stride(1), k.stride(2)
         p.v_stride_page, p.v_stride_tok, p.v_stride_head = v.stride(0), v.stride(1), v.stride(2)
         p.seq_lens_kv, p.block_table = seq_lens_kv.data_ptr(), block_table.data_ptr()
         p.block_table_stride, p.page_size, p.num_pages = block_table.stride(0), k.shape[1], k.shape[0]
     else:
         _need(cu_seqlens_kv is not None and cu_seqlens_kv.dtype == torch.int32, "dense mode needs int32 cu_seqlens_kv")
+        _need(cu_seqlens_kv.device == q.device and cu_seqlens_kv.numel() == cu_seqlens_q.numel(),
+              f"cu_seqlens_kv must be on {q.device} and hold B + 1 offsets")
         p.k_stride_tok, p.k_stride_head = k.stride(0), k.stride(1)
         p.v_stride_tok, p.v_stride_head = v.stride(0), v.stride(1)
         p.cu_seqlens_kv = cu_seqlens_kv.data_ptr()
@@ -212,6 +269,8 @@ def _prefill_params(q, k, v, cu_seqlens_q, out, lse, max_seqlen_q, max_seqlen_kv
     p.max_seqlen_q, p.max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
     p.softmax_scale, p.causal = float(softmax_scale), int(bool(causal))
     if out is not None:
+        _check_out(out, (tq, hq, dv), (_BF16,), q.device, "out")
+        _need(_rows_contiguous(out), "out rows must be contiguous")
         p.o, p.o_stride_tok, p.o_stride_head = out.data_ptr(), out.stride(0), out.stride(1)
     else:                                   # sizing only: the layout a fresh output gets
         p.o, p.o_stride_tok, p.o_stride_head = 0, hq * dv, dv
@@ -256,7 +315,7 @@ def prefill(q, k, v, cu_seqlens_q, *, max_seqlen_q, max_seqlen_kv, softmax_scale
     if need:
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous CUDA tensor")
+        _need(workspace.device == q.device and workspace.is_contiguous(), f"workspace must be a contiguous tensor on {q.device}")
         p.workspace, p.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _ffi.check(_ffi.load().attn_prefill(ctypes.byref(p), _stream(q.device)), "attn_prefill")
     return (out, lse) if return_lse else out
@@ -274,8 +333,11 @@ def merge_lse(o_parts: torch.Tensor, lse_parts: torch.Tensor, *, out_dtype=_BF16
     _need(o_parts.is_contiguous() and lse_parts.is_contiguous(), "partials must be contiguous")
     s, r, dv = o_parts.shape
     _need(tuple(lse_parts.shape) == (s, r), "lse_parts must be [S, R]")
+    _need(o_parts.is_cuda and lse_parts.device == o_parts.device, "partials must be CUDA tensors on one device")
     if out is None:
         out = torch.empty((r, dv), dtype=out_dtype, device=o_parts.device)
+    _check_out(out, (r, dv), (torch.bfloat16, torch.float32), o_parts.device, "out")
+    _need(out.is_contiguous(), "out must be contiguous")
     code = {torch.bfloat16: _ffi.ATTN_BF16, torch.float32: _ffi.ATTN_FP32}[out.dtype]
     lse = torch.empty((r,), dtype=torch.float32, device=o_parts.device) if return_lse else None
     _ffi.check(_ffi.load().attn_merge_lse(o_parts.data_ptr(), lse_parts.data_ptr(), s, r, dv,
@@ -310,6 +372,21 @@ def cache_append(k_new, v_new, k_cache, v_cache, slot_mapping, *, layer_base_row
     _need((v_new is None) == (v_cache is None), "v_new and v_cache go together")
     kc = _as_4d_cache(k_cache)
     code = _kv_code(kc, kv_dtype)
+    dev = k_new.device
+    _need(k_new.dim() == 3 and kc.dim() == 4, "k_new must be [N, Hkv, D] and k_cache [pages, page_size, Hkv, D]")
+    _need(kc.device == dev and slot_mapping.device == dev, f"k_cache and slot_mapping must be on {dev}")
+    _need(tuple(k_new.shape[1:]) == tuple(kc.shape[2:]) and _rows_contiguous(k_new) and _rows_contiguous(kc),
+          "k_new rows must match the cache's heads and channels, both contiguous")
+    _need(slot_mapping.dim() == 1 and slot_mapping.numel() == k_new.shape[0] and slot_mapping.is_contiguous(),
+          "slot_mapping must hold one contiguous int64 slot per new token")
+    if v_new is not None:
+        vc4 = _as_4d_cache(v_cache)
+        _need(v_new.device == dev and v_cache.device == dev, f"v_new and v_cache must be on {dev}")
+        _need(v_new.dim() == 3 and vc4.dim() == 4 and v_new.shape[0] == k_new.shape[0]
+              and tuple(v_new.shape[1:]) == tuple(vc4.shape[2:]) and tuple(vc4.shape[:3]) == tuple(kc.shape[:3])
+              and _rows_contiguous(v_new) and _rows_contiguous(vc4),
+              "v_new and v_cache must match k_new and k_cache in tokens, rows and heads, rows contiguous")
+        _need(vc4.dtype == kc.dtype, "k_cache and v_cache must share one dtype")
     ps, ksp, kst, ksh = _cache_rows(kc)
     p = _ffi.CacheAppendParams()
     p.k_new, p.k_new_stride_tok, p.k_new_stride_head = k_new.data_ptr(), k_new.stride(0), k_new.stride(1)
@@ -340,10 +417,18 @@ def mla_kv_pack_fp8(k_nope, k_rope, v, *, k_scale=1.0, v_scale=1.0, k_out=None, 
         k_rope = k_rope[:, 0, :]
     t, h, dn = k_nope.shape
     dr, dv = k_rope.shape[1], v.shape[2]
+    dev = k_nope.device
+    _need(k_rope.device == dev and v.device == dev, f"k_rope and v must be on {dev}")
+    _need(k_rope.dim() == 2 and k_rope.shape[0] == t and v.dim() == 3 and tuple(v.shape[:2]) == (t, h),
+          "k_rope must be [T, dr] and v [T, H, dv]")
+    _need(_rows_contiguous(k_nope) and _rows_contiguous(k_rope) and _rows_contiguous(v), "input rows must be contiguous")
     if k_out is None:
-        k_out = torch.empty((t, h, dn + dr), dtype=torch.float8_e4m3fn, device=k_nope.device)
+        k_out = torch.empty((t, h, dn + dr), dtype=torch.float8_e4m3fn, device=dev)
     if v_out is None:
-        v_out = torch.empty((t, h, dv), dtype=torch.float8_e4m3fn, device=k_nope.device)
+        v_out = torch.empty((t, h, dv), dtype=torch.float8_e4m3fn, device=dev)
+    _check_out(k_out, (t, h, dn + dr), (torch.float8_e4m3fn, torch.uint8), dev, "k_out")
+    _check_out(v_out, (t, h, dv), (torch.float8_e4m3fn, torch.uint8), dev, "v_out")
+    _need(_rows_contiguous(k_out) and _rows_contiguous(v_out), "output rows must be contiguous")
     p = _ffi.MlaKvPackParams()
     p.k_nope, p.k_nope_stride_tok, p.k_nope_stride_head = k_nope.data_ptr(), k_nope.stride(0), k_nope.stride(1)
     p.k_rope, p.k_rope_stride_tok = k_rope.data_ptr(), k_rope.stride(0)

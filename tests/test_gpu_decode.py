@@ -335,3 +335,36 @@ def test_merge_lse_without_rows():
     o, lse = sap.merge_lse(o_parts, lse_parts)
     torch.cuda.synchronize()
     assert tuple(o.shape) == (0, 128) and tuple(lse.shape) == (0,)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks what the C ABI cannot see (devices, ranks, the
+    sizes the kernels index with) and raises before anything is enqueued."""
+    case = inputs.decode_case(batch=2, q_len=1, hq=8, hkv=2, d=128, dv=128, page_size=16,
+                              seq_lens=[37, 100], seed=5)
+    c = case.to(DEV)
+    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale)
+    bad = [
+        dict(out=torch.empty((2, 1, 8, 64), dtype=torch.bfloat16, device=DEV)),     # too few channels
+        dict(out=torch.empty((2, 1, 8, 128), dtype=torch.float32, device=DEV)),     # wrong dtype
+        dict(out=torch.empty((2, 1, 8, 128), dtype=torch.bfloat16)),                # host memory
+        dict(lse=torch.empty((2, 1, 4), dtype=torch.float32, device=DEV)),          # too few heads
+    ]
+    for extra in bad:
+        with pytest.raises(ValueError):
+            sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, **kw, **extra)
+    with pytest.raises(ValueError):                                                 # K rows narrower than q
+        sap.decode_paged(c.q, c.k_cache[..., :64], c.v_cache, c.block_table, c.seq_lens, **kw)
+    with pytest.raises(ValueError):                                                 # a table row short
+        sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table[:1], c.seq_lens, **kw)
+    with pytest.raises(ValueError):
+        sap.decode_paged_noalloc(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, **kw,
+                                 out=torch.empty((2, 1, 8, 64), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        sap.merge_lse(torch.zeros((2, 4, 128), device=DEV), torch.zeros((2, 4), device=DEV),
+                      out=torch.empty((4, 64), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    # the same call with matching tensors runs
+    out = sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, **kw)
+    ref, _ = oracle_decode(case)
+    compare(f64(out.cpu()), ref)

@@ -162,3 +162,24 @@ def test_ragged_paged_prefill_80k_block_edges():
     print("case", case.name, flush=True)
     out, lse = _run(case)
     print(_edge_rows_check(case, out, lse))
+
+
+def test_binding_rejects_mismatched_tensors():
+    """Prefill's binding checks devices, ranks and sizes before anything is
+    enqueued (the C ABI sees only pointers and strides)."""
+    case = inputs.prefill_case(q_lens=[40], kv_lens=[90], hq=4, hkv=2, d=128, seed=61, causal=True)
+    c = case.to(DEV)
+    kw = dict(max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale, causal=True,
+              cu_seqlens_kv=c.cu_seqlens_kv)
+    with pytest.raises(ValueError):                                   # output with too few rows
+        sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, **kw, out=torch.empty((39, 4, 128), dtype=torch.bfloat16,
+                                                                         device=DEV))
+    with pytest.raises(ValueError):                                   # K narrower than Q
+        sap.prefill(c.q, c.k[..., :64], c.v, c.cu_seqlens_q, **kw)
+    with pytest.raises(ValueError):                                   # K and V of different lengths
+        sap.prefill(c.q, c.k, c.v[:-1], c.cu_seqlens_q, **kw)
+    with pytest.raises(ValueError):                                   # K on the host
+        sap.prefill(c.q, c.k.cpu(), c.v, c.cu_seqlens_q, **kw)
+    out, lse = _run(case)
+    ref, lref = oracle_prefill(case)
+    compare(f64(out.cpu()), ref, lse.cpu().numpy(), lref)
