@@ -59,3 +59,27 @@ def test_random_decode_with_and_without_the_total_hint(seed):
             got = np.stack([f64(out[i, t, h]) for i, t, h in rows])
             gl = np.array([float(lse[i, t, h]) for i, t, h in rows])
             print(compare(got, ref, gl, lref))
+
+
+@pytest.mark.parametrize("batch", [512, 513, 700])
+def test_batches_at_and_past_the_key_range_limit(batch):
+    """Key ranges serve up to 512 requests (the kernels scan seq_lens, eight
+    entries per lane); a larger batch is planned as per-request splits, with
+    and without the host's total of the keys. Every row against the oracle."""
+    rng = np.random.default_rng(3000 + batch)
+    lens = rng.integers(0, 700, size=batch).tolist()
+    lens[int(rng.integers(batch))] = 700
+    case = inputs.decode_case(batch=batch, q_len=1, hq=8, hkv=2, d=64, dv=64, page_size=16, seq_lens=lens,
+                              seed=4000 + batch, layout="random")
+    c = case.to(DEV)
+    ref, lref = oracle_decode(case)
+    for total in (0, int(sum(lens))):
+        p = sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
+                              softmax_scale=c.scale, total_kv_tokens=total)
+        plan = sap.decode_plan(p)
+        print(f"batch {batch} total {total}: {plan['num_splits']} x {plan['split_tokens']}, "
+              f"{plan['key_ranges']} key ranges", flush=True)
+        assert (plan["key_ranges"] > 0) == (batch <= 512)
+        out, lse = sap.decode_paged(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, max_seq_len=c.max_seq_len,
+                                    softmax_scale=c.scale, return_lse=True, total_kv_tokens=total)
+        print(compare(f64(out.cpu()), ref, lse.cpu().numpy(), lref))
