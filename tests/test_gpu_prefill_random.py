@@ -73,3 +73,22 @@ def test_random_prefill_short_histories(seed):
     out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, **kv, **kw)
     ref, lref = oracle_prefill(case)
     print(compare(f64(out.cpu()), ref, lse.cpu().numpy(), lref))
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_many_short_chunks(splits):
+    """A serving-shaped batch: 64 requests of 1-20 new tokens each over
+    histories of up to 1500 keys (GQA 32/8, paged), so almost every query
+    tile is partial and most workgroups of the grid find no rows. Every row
+    against the oracle."""
+    rng = np.random.default_rng(5000 + splits)
+    q_lens = rng.integers(1, 21, size=64).tolist()
+    kv_lens = [q + int(rng.integers(0, 1501)) for q in q_lens]
+    case = inputs.prefill_case(q_lens=q_lens, kv_lens=kv_lens, hq=32, hkv=8, d=128, seed=6000 + splits, causal=True,
+                               paged=True, page_size=64, name=f"chunks-{splits}")
+    c = case.to(DEV)
+    out, lse = sap.prefill(c.q, c.k, c.v, c.cu_seqlens_q, seq_lens_kv=c.seq_lens_kv, block_table=c.block_table,
+                           max_seqlen_q=c.max_seqlen_q, max_seqlen_kv=c.max_seqlen_kv, softmax_scale=c.scale,
+                           causal=True, return_lse=True, kv_splits=splits)
+    ref, lref = oracle_prefill(case)
+    print(f"splits {splits}: {sum(q_lens)} query tokens", compare(f64(out.cpu()), ref, lse.cpu().numpy(), lref))
