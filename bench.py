@@ -306,6 +306,7 @@ def ceilings_lib():
     lib.ceil_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_bf16_varied.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ceil_mfma_fma_overlap.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
     return lib
 
 
@@ -380,6 +381,30 @@ def measured_peaks() -> dict:
             "mfma_bf16_loop_varied_operands_TFLOPs": round(mfma_flops / (varied_ms * 1e-3) / 1e12, 1),
             "torch_copy_GBs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
             "hipblaslt_bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+
+
+def overlap_probe() -> dict:
+    """How far MFMA and FMA work of two waves sharing a SIMD overlap: one
+    wave per SIMD of back-to-back bf16 MFMAs (32x32x16, or 16x16x32 for the
+    same flops), one of eight independent FMA chains, each alone and both
+    together; best of three launches of 256 workgroups, in ms."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    lib = ceilings_lib()
+    blocks = 256
+    sink = torch.zeros(blocks * 512, dtype=torch.float32, device=dev)
+    res = {}
+    for kind, name in ((0, "32x32x16"), (1, "16x16x32")):
+        for mode, what in ((1, "mfma"), (2, "fma"), (3, "both")):
+            def launch():
+                if lib.ceil_mfma_fma_overlap(sink.data_ptr(), kind, mode, 4096, 8192, blocks, stream.cuda_stream) != 0:
+                    raise RuntimeError("ceil_mfma_fma_overlap failed")
+            launch()
+            res[f"{name}_{what}_ms"] = round(min(time_events(launch, 1, stream) for _ in range(3)), 4)
+        alone = max(res[f"{name}_mfma_ms"], res[f"{name}_fma_ms"])
+        res[f"{name}_fma_time_exposed"] = round((res[f"{name}_both_ms"] - alone) / res[f"{name}_fma_ms"], 3)
+    return res
 
 
 def input_sha256(tensors) -> str:
@@ -677,6 +702,8 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=6, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR", "COPY_BYTES"),
                     help="write profiles/traffic_<WORKLOAD>.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--overlap-probe", action="store_true",
+                    help="time matrix and vector waves alone and together on each SIMD (the ceilings library)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("WORKLOAD", "TRACE_DIR", "STEPS"),
                     help="write profiles/kernel_trace_<WORKLOAD>.md from a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
@@ -689,6 +716,9 @@ def main() -> int:
         return 0
     if args.counter_summary:
         print(counter_summary(args.counter_summary[0], args.counter_summary[1]))
+        return 0
+    if args.overlap_probe:
+        print(json.dumps(overlap_probe()))
         return 0
     if args.copy_calibration:
         import torch

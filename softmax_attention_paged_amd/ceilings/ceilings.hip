@@ -23,6 +23,16 @@
 //     instruction as they do in a real contraction (the loop above feeds the
 //     same two operands to every MFMA). iters must be a positive multiple
 //     of 8; otherwise the same arguments and returns.
+//   int ceil_mfma_fma_overlap(float *sink, int kind, int mode, int n_mfma,
+//                             int n_fma, int blocks, hipStream_t stream);
+//     how far matrix and vector work of different waves overlap on one
+//     SIMD: workgroups of eight waves, waves 0-3 (one per SIMD) run n_mfma
+//     rounds of 32x32x16 (kind 0, four chains) or 16x16x32 (kind 1, eight
+//     chains) bf16 MFMAs, the same number of flops either way, and waves
+//     4-7 run n_fma rounds of eight independent FMA chains; mode 1 runs the
+//     matrix waves only, 2 the vector waves only, 3 both. sink holds
+//     blocks * 512 floats (written only on a value the loops never give).
+//     Returns 0, -1 on bad arguments, or the HIP error code.
 
 #include <hip/hip_runtime.h>
 
@@ -33,6 +43,7 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
@@ -111,6 +122,53 @@ __global__ __launch_bounds__(kThreads) void mfma_varied_kernel(float *sink, int 
   if (lane_is_zero()) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = s;
 }
 
+template <int KIND>
+__global__ __launch_bounds__(512) void overlap_kernel(float *sink, int mode, int n_mfma, int n_fma) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool matrix_wave = wave < 4;
+  if (matrix_wave ? !(mode & 1) : !(mode & 2)) return;
+  float out = 0.f;
+  if (matrix_wave) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = static_cast<__bf16>(0.001f * (lane + e));
+      b[e] = static_cast<__bf16>(0.002f * (lane - e));
+    }
+    if constexpr (KIND == 0) {
+      f32x16 c0{}, c1{}, c2{}, c3{};
+      for (int i = 0; i < n_mfma; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) out += c0[i] + c1[i] + c2[i] + c3[i];
+    } else {
+      f32x4 c[8] = {};
+      for (int i = 0; i < n_mfma; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    }
+  } else {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.001f * (lane + j);
+    const float m = 0.999f, add = 0.0001f * lane;
+    for (int i = 0; i < n_fma; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(x[j], m, add);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out += x[j];
+  }
+  if (out == 12345.678f) sink[blockIdx.x * 512 + threadIdx.x] = out;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,6 +191,15 @@ int ceil_mfma_bf16(float *sink, int iters, int blocks, hipStream_t stream) {
 int ceil_mfma_bf16_varied(float *sink, int iters, int blocks, hipStream_t stream) {
   if (!sink || iters < 8 || iters % 8 || blocks < 1) return -1;
   hipLaunchKernelGGL(mfma_varied_kernel, dim3(blocks), dim3(kThreads), 0, stream, sink, iters);
+  return static_cast<int>(hipGetLastError());
+}
+
+int ceil_mfma_fma_overlap(float *sink, int kind, int mode, int n_mfma, int n_fma, int blocks, hipStream_t stream) {
+  if (!sink || kind < 0 || kind > 1 || mode < 1 || mode > 3 || n_mfma < 1 || n_fma < 1 || blocks < 1) return -1;
+  if (kind == 0)
+    hipLaunchKernelGGL(overlap_kernel<0>, dim3(blocks), dim3(512), 0, stream, sink, mode, n_mfma, n_fma);
+  else
+    hipLaunchKernelGGL(overlap_kernel<1>, dim3(blocks), dim3(512), 0, stream, sink, mode, n_mfma, n_fma);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -53,6 +53,10 @@ def test_ceiling_kernels_library_loads_and_rejects_bad_arguments():
     assert lib.ceil_mfma_bf16_varied(FAKE, 0, 8, None) == -1
     assert lib.ceil_mfma_bf16_varied(None, 8, 8, None) == -1
     assert lib.ceil_mfma_bf16_varied(FAKE, 8, 0, None) == -1
+    lib.ceil_mfma_fma_overlap.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    for bad in ((None, 0, 1, 8, 8, 4), (FAKE, 2, 1, 8, 8, 4), (FAKE, 0, 0, 8, 8, 4), (FAKE, 0, 4, 8, 8, 4),
+                (FAKE, 0, 3, 0, 8, 4), (FAKE, 0, 3, 8, 0, 4), (FAKE, 1, 3, 8, 8, 0)):
+        assert lib.ceil_mfma_fma_overlap(*bad, None) == -1
 
 
 def test_ctypes_mirrors_match_the_c_compiler_layout(tmp_path):
