@@ -1,8 +1,10 @@
-// Ceilings of the GPU measured with two plain kernels, for the benchmark's
+// Ceilings of the GPU measured with plain kernels, for the benchmark's
 // secondary denominators (beside the published peaks): how fast a kernel can
-// stream reads from HBM, and how fast the matrix cores run a bf16
-// 32x32x16 MFMA loop with no memory traffic. Not part of the attention
-// library: built into its own shared object, loaded by the benchmark only.
+// stream reads from HBM, how fast the matrix cores run a bf16 32x32x16 MFMA
+// loop with no memory traffic (with fixed operands, and with operands that
+// change every instruction), and how far the matrix and vector work of two
+// waves on one SIMD overlap. Not part of the attention library: built into
+// its own shared object, loaded by the benchmark only.
 //
 //   int ceil_stream_read(const void *src, size_t bytes, unsigned *sink,
 //                        int blocks, hipStream_t stream);
