@@ -307,6 +307,7 @@ def ceilings_lib():
     lib.ceil_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_bf16_varied.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.ceil_mfma_fma_overlap.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 5 + [ctypes.c_void_p]
+    lib.ceil_lds_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -333,7 +334,8 @@ def measured_peaks() -> dict:
     """Ceilings measured on this GPU, as secondary denominators: a 1 GiB
     streaming read and a bf16 32x32x16 MFMA loop (the ceiling kernels; the
     loop once with fixed operands and once with operands that change every
-    instruction, as a real contraction's do), and
+    instruction, as a real contraction's do; LDS reads of 16 bytes per lane,
+    plain and transposing), and
     for context a 1 GiB torch copy (bytes read + written) and a bf16 8192^3
     GEMM through torch.matmul (hipBLASLt)."""
     import torch
@@ -357,11 +359,20 @@ def measured_peaks() -> dict:
         if lib.ceil_mfma_bf16_varied(sink.data_ptr(), iters, blocks, stream.cuda_stream) != 0:
             raise RuntimeError("ceil_mfma_bf16_varied failed")
 
-    for f in (read, mfma, mfma_varied):
+    lds_iters, lds_blocks = 4096, 2048     # two 64 KB workgroups per CU
+    lds_sink = torch.zeros(lds_blocks * 256, dtype=torch.int32, device=dev)
+
+    def lds(kind):
+        if lib.ceil_lds_read(lds_sink.data_ptr(), kind, lds_iters, lds_blocks, stream.cuda_stream) != 0:
+            raise RuntimeError("ceil_lds_read failed")
+
+    for f in (read, mfma, mfma_varied, lambda: lds(0), lambda: lds(1)):
         f()
     read_ms = time_events(read, 10, stream)
     mfma_ms = time_events(mfma, 5, stream)
     varied_ms = time_events(mfma_varied, 5, stream)
+    lds_ms = [time_events(lambda: lds(k), 5, stream) for k in (0, 1)]
+    lds_bytes = lds_blocks * 256 * 16 * lds_iters
     y = torch.empty_like(x)
     y.copy_(x)
     copy_ms = time_events(lambda: y.copy_(x), 10, stream)
@@ -379,6 +390,8 @@ def measured_peaks() -> dict:
     return {"stream_read_GBs": round((1 << 30) / (read_ms * 1e-3) / 1e9, 1),
             "mfma_bf16_loop_TFLOPs": round(mfma_flops / (mfma_ms * 1e-3) / 1e12, 1),
             "mfma_bf16_loop_varied_operands_TFLOPs": round(mfma_flops / (varied_ms * 1e-3) / 1e12, 1),
+            "lds_read_b128_TBs": round(lds_bytes / (lds_ms[0] * 1e-3) / 1e12, 1),
+            "lds_read_b64_tr_b16_TBs": round(lds_bytes / (lds_ms[1] * 1e-3) / 1e12, 1),
             "torch_copy_GBs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
             "hipblaslt_bf16_gemm_8192_TFLOPs": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
 

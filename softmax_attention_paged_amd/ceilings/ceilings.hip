@@ -35,6 +35,15 @@
 //     matrix waves only, 2 the vector waves only, 3 both. sink holds
 //     blocks * 512 floats (written only on a value the loops never give).
 //     Returns 0, -1 on bad arguments, or the HIP error code.
+//   int ceil_lds_read(unsigned *sink, int kind, int iters, int blocks,
+//                     hipStream_t stream);
+//     LDS read bandwidth: workgroups of four waves fill 64 KB of LDS, then
+//     each lane issues iters reads of 16 bytes (kind 0, ds_read_b128) or
+//     two transposing 8-byte reads (kind 1, ds_read_b64_tr_b16), eight in
+//     flight, the lanes of a wave on consecutive addresses (no bank
+//     conflicts); every workgroup reads blocks * 256 * 16 * iters bytes in
+//     all. iters must be a positive multiple of 8; sink holds blocks * 256
+//     words (written only on a value the loop never gives).
 
 #include <hip/hip_runtime.h>
 
@@ -171,6 +180,37 @@ __global__ __launch_bounds__(512) void overlap_kernel(float *sink, int mode, int
   if (out == 12345.678f) sink[blockIdx.x * 512 + threadIdx.x] = out;
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int KIND>
+__global__ __launch_bounds__(256) void lds_read_kernel(unsigned *sink, int iters) {
+  constexpr int kWords = 16384;                       // 64 KB
+  __shared__ __attribute__((aligned(16))) unsigned buf[kWords];
+  for (int i = threadIdx.x; i < kWords; i += 256) buf[i] = static_cast<unsigned>(i) * 2654435761u;
+  __syncthreads();
+  const unsigned base = threadIdx.x * 16u;            // 256 lanes x 16 bytes = 4 KB per round
+  unsigned acc = 0;
+  for (int i = 0; i < iters; i += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const unsigned off = (base + static_cast<unsigned>(i + u) * 4096u) & 0xffffu;
+      const char *p = reinterpret_cast<const char *>(buf) + off;
+      if constexpr (KIND == 0) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      } else {
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+        const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(reinterpret_cast<uintptr_t>(p + 8)));
+        acc ^= static_cast<unsigned>(a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w);
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +242,15 @@ int ceil_mfma_fma_overlap(float *sink, int kind, int mode, int n_mfma, int n_fma
     hipLaunchKernelGGL(overlap_kernel<0>, dim3(blocks), dim3(512), 0, stream, sink, mode, n_mfma, n_fma);
   else
     hipLaunchKernelGGL(overlap_kernel<1>, dim3(blocks), dim3(512), 0, stream, sink, mode, n_mfma, n_fma);
+  return static_cast<int>(hipGetLastError());
+}
+
+int ceil_lds_read(unsigned *sink, int kind, int iters, int blocks, hipStream_t stream) {
+  if (!sink || kind < 0 || kind > 1 || iters < 8 || iters % 8 || blocks < 1) return -1;
+  if (kind == 0)
+    hipLaunchKernelGGL(lds_read_kernel<0>, dim3(blocks), dim3(256), 0, stream, sink, iters);
+  else
+    hipLaunchKernelGGL(lds_read_kernel<1>, dim3(blocks), dim3(256), 0, stream, sink, iters);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -57,6 +57,9 @@ def test_ceiling_kernels_library_loads_and_rejects_bad_arguments():
     for bad in ((None, 0, 1, 8, 8, 4), (FAKE, 2, 1, 8, 8, 4), (FAKE, 0, 0, 8, 8, 4), (FAKE, 0, 4, 8, 8, 4),
                 (FAKE, 0, 3, 0, 8, 4), (FAKE, 0, 3, 8, 0, 4), (FAKE, 1, 3, 8, 8, 0)):
         assert lib.ceil_mfma_fma_overlap(*bad, None) == -1
+    lib.ceil_lds_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    for bad in ((None, 0, 8, 4), (FAKE, 2, 8, 4), (FAKE, 0, 12, 4), (FAKE, 1, 0, 4), (FAKE, 0, 8, 0)):
+        assert lib.ceil_lds_read(*bad, None) == -1
 
 
 def test_ctypes_mirrors_match_the_c_compiler_layout(tmp_path):
