@@ -674,13 +674,14 @@ def secondary_append(steps: int) -> dict:
 def secondary_tiny_decode(steps: int) -> dict:
     """The tiny paged GQA decode (2 requests of 37 and 100 keys, 8/2 heads,
     D 64, 16-row pages): launch-bound, so timed as graph replays; reported as
-    latency per call (split kernel + merge), with no roofline."""
+    latency per call under the planner's own plan (requests this short run as
+    one unsplit launch), with no roofline."""
     import torch
     import softmax_attention_paged_amd as sap
     from softmax_attention_paged_amd import inputs
     case = inputs.gqa_decode_tiny()
     c = case.to("cuda:0")
-    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale, num_splits=2)
+    kw = dict(max_seq_len=c.max_seq_len, softmax_scale=c.scale)
     plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens, **kw))
     ws = torch.empty(max(plan["workspace_bytes"], 16), dtype=torch.uint8, device=c.q.device)
     out = torch.empty((2, 1, 8, 64), dtype=torch.bfloat16, device=c.q.device)
@@ -689,7 +690,9 @@ def secondary_tiny_decode(steps: int) -> dict:
     ms = float(np.median([time_graph(fn, max(steps, 20)) for _ in range(5)]))
     eager = time_settled(fn, max(steps, 20), torch.cuda.current_stream())
     return {"workload": case.name, "us_per_call_graph": round(ms * 1e3, 2), "us_per_call_eager": round(eager * 1e3, 2),
-            "num_splits": plan["num_splits"], "note": "launch-bound: two kernels (split + merge) per call"}
+            "num_splits": plan["num_splits"], "key_ranges": plan["key_ranges"],
+            "note": "launch-bound: " + ("one kernel per call" if plan["workspace_bytes"] == 0
+                                        else "two kernels (split + merge) per call")}
 
 
 def main() -> int:

@@ -104,6 +104,13 @@ constexpr int kMinRangeTiles = 8;
 // streams read the paged pool more efficiently, down to the point where
 // too few requests are in flight.
 constexpr int kRangeWavesPerCU = 8;
+// Longest walk (tiles of 32 keys) for which a decode runs unsplit when every
+// unit is resident at once: one launch, no partials. Graph replays on one
+// GPU (batches 1-64, 8/2 heads at D 64 and 40/8 at D 128, lengths from half
+// the longest up to it): up to 256 keys the unsplit launch took 3.9-24.5 us
+// against 4.9-27.5 us for key ranges and their merge (0.28-0.90 of the
+// time); from 512 keys the key ranges were faster (1.1-5.4x).
+constexpr int kUnsplitMaxTiles = 8;
 
 attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) {
   if (!p) return fail(ATTN_ERR_INVALID_ARG, "params is NULL");
@@ -210,7 +217,7 @@ DecodePlan plan_decode(const attn_decode_params *p) {
   const int64_t base_units = (int64_t)p->batch * p->num_kv_heads * pl.q_groups;
   const int tile = pl.mla ? attn::kMlaTileTokens : attn::kGqaTileTokens;
   const int cus = num_cus();
-  int splits;
+  int splits = 0;
   if (p->num_splits > 0) {
     splits = p->num_splits;
   } else if (pl.mla) {
@@ -241,7 +248,12 @@ DecodePlan plan_decode(const attn_decode_params *p) {
     const bool ext = p->window_enabled || p->packed_q;
     const int span = window_span(p);
     const int64_t req_tiles = cdiv(std::max(span, 1), tile) + 1;   // a request's tiles, window alignment included
-    if (p->batch <= attn::kKeyRangeMaxBatch && (int64_t)p->batch * req_tiles < (int64_t(1) << 30)) {
+    const int64_t resident = (int64_t)cus * attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext);
+    if (cdiv(std::max(span, 1), tile) <= kUnsplitMaxTiles && base_units <= resident) {
+      // short requests: the key ranges' scans of seq_lens and the merge
+      // launch cost more than the balance they buy
+      splits = 1;
+    } else if (p->batch <= attn::kKeyRangeMaxBatch && (int64_t)p->batch * req_tiles < (int64_t(1) << 30)) {
       const int64_t per = (int64_t)p->num_kv_heads * pl.q_groups;
       const int64_t slots = (int64_t)cus * std::min(kRangeWavesPerCU, attn::decode_gqa_waves_per_cu(p->head_dim_qk, ext));
       int64_t upper = (int64_t)p->batch * req_tiles;
@@ -257,8 +269,7 @@ DecodePlan plan_decode(const attn_decode_params *p) {
       return pl;
     }
     // Otherwise one single-wave unit per (request, KV head, q-group, split).
-    splits = 0;
-    if (p->total_kv_tokens > 0) {
+    if (splits == 0 && p->total_kv_tokens > 0) {
       // With the host's total of the keys: the split length L for which every
       // unit is resident at once. A request walking n keys has at most
       // n / L + 1 units per (KV head, q-group), so with

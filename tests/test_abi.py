@@ -330,6 +330,33 @@ def test_gqa_split_planner_with_total_keys_fits_one_round(batch, max_len, total,
     assert plan(p)[0] == _ffi.ATTN_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("max_len,batch,d,expect_unsplit", [
+    (256, 64, 128, True), (257, 64, 128, False), (1, 1, 64, True), (200, 384, 128, True),
+    (200, 385, 128, False), (256, 512, 64, True), (288, 512, 64, False), (224, 256, 256, True),
+    (224, 257, 256, False)])
+def test_short_decodes_run_unsplit(max_len, batch, d, expect_unsplit):
+    # a GQA decode whose max_seq_len bound is at most 8 tiles of 32 keys, with
+    # every (request, KV head, q-group) unit resident at once (resident waves:
+    # 256 CUs x 16 / 12 / 8 at D 64 / 128 / 256), runs as one unsplit launch
+    # without partials; otherwise the planner keeps its key ranges (or splits
+    # past 512 requests)
+    hkv = 8
+    p = decode_params(num_q_heads=5 * hkv, num_kv_heads=hkv, head_dim_qk=d, head_dim_v=d, q_len=1, batch=batch,
+                      max_seq_len=max_len, page_size=128, num_pages=(max_len // 128 + 1) * batch,
+                      block_table_stride=max_len // 128 + 1, k_stride_page=128 * hkv * d, k_stride_tok=hkv * d,
+                      k_stride_head=d, v_stride_page=128 * hkv * d, v_stride_tok=hkv * d, v_stride_head=d)
+    st, info = plan(p)
+    assert st == 0
+    if expect_unsplit:
+        assert (info.key_ranges, info.num_splits, info.workspace_bytes) == (0, 1, 0)
+        assert info.num_units == batch * hkv
+    else:
+        assert info.key_ranges > 0 or info.num_splits > 1
+    if max_len >= 64:
+        p.num_splits = 2             # a caller's split count still wins
+        assert plan(p)[1].num_splits == 2
+
+
 @pytest.mark.parametrize("batch,max_len,total,hkv,d,q_len", [
     (64, 8192, 256194, 8, 128, 1), (64, 8192, 0, 8, 128, 1), (8, 65536, 300000, 8, 128, 1),
     (17, 513, 2000, 2, 64, 1), (200, 4096, 400000, 8, 256, 1), (64, 8192, 1000, 8, 128, 1),
@@ -347,6 +374,10 @@ def test_gqa_key_range_plan(batch, max_len, total, hkv, d, q_len):
     p.total_kv_tokens = total
     st, info = plan(p)
     assert st == 0
+    if -(-max(max_len, 1) // 32) <= 8 and batch * hkv * info.q_groups <= 256 * {64: 16, 128: 12, 256: 8}[d]:
+        # no request walks more than 8 tiles and every unit is resident: unsplit
+        assert (info.key_ranges, info.num_splits, info.workspace_bytes) == (0, 1, 0)
+        return
     slots = 256 * 8                  # two waves per SIMD stream the key ranges
     upper = batch * (-(-max(max_len, 1) // 32) + 1)
     if total:
@@ -440,11 +471,15 @@ def test_window_plans_splits_over_the_window():
     st, g = plan(decode_params(batch=513, max_seq_len=256, num_pages=16, block_table_stride=16, window_enabled=1,
                                window_left=1000))
     assert st == 0 and g.num_splits * g.split_tokens >= 256     # a window wider than the history
-    # key ranges: the tile bound per request follows the window (100 + 4 + 31
-    # keys: 5 tiles + 1 of alignment), so K is capped at one per 8 of them
+    # key ranges: the tile bound per request follows the window (300 + 4 + 31
+    # keys: 11 tiles + 1 of alignment), so K is capped at one per 8 of them
+    st, kr = plan(decode_params(batch=4, max_seq_len=8192, num_pages=512, block_table_stride=512, q_len=4,
+                                window_enabled=1, window_left=300))
+    assert st == 0 and kr.key_ranges == -(-4 * (-(-(300 + 4 + 31) // 32) + 1) // 8)
+    # a window of 100 keys walks at most 5 tiles: one unsplit launch
     st, kr = plan(decode_params(batch=4, max_seq_len=8192, num_pages=512, block_table_stride=512, q_len=4,
                                 window_enabled=1, window_left=100))
-    assert st == 0 and kr.key_ranges == -(-4 * (-(-(100 + 4 + 31) // 32) + 1) // 8)
+    assert st == 0 and (kr.key_ranges, kr.num_splits, kr.workspace_bytes) == (0, 1, 0)
 
 
 

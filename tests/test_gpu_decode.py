@@ -4,6 +4,7 @@ Every case calls the HIP library through the C ABI (via the ctypes binding)
 and compares element by element with the oracle on the same seeded inputs.
 """
 
+import dataclasses
 import numpy as np
 import pytest
 import torch
@@ -189,15 +190,18 @@ _KEY_RANGE_CASES = {
     # 300 short requests, a fifth of them empty: ranges of ~3 tiles hold
     # several whole requests each (written final) and cut others
     "many_short_with_empty": dict(batch=300, q_len=1, hq=8, hkv=2, d=64, page_size=16,
-                                  seq_lens=_lens(_KR, 300, 1, 40, zeros=0.2)),
+                                  seq_lens=_lens(_KR, 300, 1, 40, zeros=0.2), max_pages=32, bound=512),
     # two query groups per KV head (G 8, F 2), causal: the last tile of a
     # request is empty for the first query group's rows
     "causal_q4_two_groups": dict(batch=5, q_len=4, hq=16, hkv=2, d=128, page_size=16, causal=True,
                                  seq_lens=[1, 2, 3000, 33, 1500]),
     # the largest batch the kernels scan, and one past it (per-request splits)
-    "batch_512": dict(batch=512, q_len=1, hq=4, hkv=1, d=64, page_size=16, seq_lens=_lens(_KR, 512, 0, 100)),
+    # (these three pass a max_seq_len bound of 512: with a bound of at most
+    # 8 tiles the planner runs short requests unsplit)
+    "batch_512": dict(batch=512, q_len=1, hq=4, hkv=1, d=64, page_size=16, seq_lens=_lens(_KR, 512, 0, 100),
+                      max_pages=32, bound=512),
     "batch_513_splits": dict(batch=513, q_len=1, hq=4, hkv=1, d=64, page_size=16,
-                             seq_lens=_lens(_KR, 513, 0, 100)),
+                             seq_lens=_lens(_KR, 513, 0, 100), max_pages=32, bound=512),
     "d256_ragged": dict(batch=9, q_len=1, hq=16, hkv=4, d=256, page_size=64,
                         seq_lens=[0, 4096, 17, 2000, 31, 32, 33, 700, 1]),
 }
@@ -207,7 +211,10 @@ _KEY_RANGE_CASES = {
 def test_key_ranges_match_oracle(name):
     kw = dict(_KEY_RANGE_CASES[name])
     d = kw.pop("d")
+    bound = kw.pop("bound", 0)
     case = inputs.decode_case(dv=d, d=d, seed=300 + len(name), layout="noncontiguous", **kw)
+    if bound:
+        case = dataclasses.replace(case, max_seq_len=bound)
     c = case.to(DEV)
     plan = sap.decode_plan(sap.decode_params(c.q, c.k_cache, c.v_cache, c.block_table, c.seq_lens,
                                              max_seq_len=c.max_seq_len, softmax_scale=c.scale, causal=c.causal))
