@@ -638,14 +638,6 @@ void *scratch_ptr() {
   return ptr;
 }
 
-}  // namespace
-
-extern "C" {
-
-}  // extern "C"
-
-namespace {
-
 attn_status_t decode_call(const attn_decode_params *p, hipStream_t stream, int phase) {
   attn_status_t st = validate_decode(p, true);
   if (st != ATTN_OK) return st;
