@@ -95,8 +95,12 @@ struct DecodePlan {
 };
 
 // Shortest key range the planner cuts (tiles of 32 keys): a range pays a
-// query load and an output write per request it touches.
-constexpr int kMinRangeTiles = 8;
+// query load and an output write per request it touches. Graph replays on one
+// GPU (batches 1-64, bounds 512-4096 keys, 40/8 heads at D 128 and 8/2 at
+// D 64): a minimum of 2 tiles ran 0.61-1.0 of the time of a minimum of 8
+// (4 requests <= 1024 keys at D 128: 13.1 against 20.6 us), 4 tiles in
+// between; batches that fill the range cap (the 64 x 8192 decode) unchanged.
+constexpr int kMinRangeTiles = 2;
 // Waves per CU the key ranges are cut for: two per SIMD. Measured on the
 // 64-request decode (lengths uniform on 256..8192, Hkv 8, D 128, three
 // resident per SIMD): 7, 7.5, 8, 8.5, 9 and 12 waves per CU ran 0.1905,

@@ -364,7 +364,7 @@ def test_short_decodes_run_unsplit(max_len, batch, d, expect_unsplit):
 def test_gqa_key_range_plan(batch, max_len, total, hkv, d, q_len):
     # up to 512 requests the GQA plan cuts the batch's 32-key tiles into K
     # equal ranges: K = 8 waves per CU / (Hkv q_groups), at most 512, and
-    # at most one per 8 tiles of the batch (bounded by max_seq_len, or by the
+    # at most one per 2 tiles of the batch (bounded by max_seq_len, or by the
     # host total when given); partial slots K + batch per row of a request
     hq = hkv * 4
     p = decode_params(num_q_heads=hq, num_kv_heads=hkv, head_dim_qk=d, head_dim_v=d, q_len=q_len, batch=batch,
@@ -382,7 +382,7 @@ def test_gqa_key_range_plan(batch, max_len, total, hkv, d, q_len):
     upper = batch * (-(-max(max_len, 1) // 32) + 1)
     if total:
         upper = min(upper, -(-total // 32) + batch)
-    k = max(1, min(slots // (hkv * info.q_groups), 512, -(-upper // 8)))
+    k = max(1, min(slots // (hkv * info.q_groups), 512, -(-upper // 2)))
     assert info.key_ranges == k
     assert info.num_splits == 0 and info.split_tokens == 0
     assert info.num_units == k * hkv * info.q_groups
@@ -472,10 +472,10 @@ def test_window_plans_splits_over_the_window():
                                window_left=1000))
     assert st == 0 and g.num_splits * g.split_tokens >= 256     # a window wider than the history
     # key ranges: the tile bound per request follows the window (300 + 4 + 31
-    # keys: 11 tiles + 1 of alignment), so K is capped at one per 8 of them
+    # keys: 11 tiles + 1 of alignment), so K is capped at one per 2 of them
     st, kr = plan(decode_params(batch=4, max_seq_len=8192, num_pages=512, block_table_stride=512, q_len=4,
                                 window_enabled=1, window_left=300))
-    assert st == 0 and kr.key_ranges == -(-4 * (-(-(300 + 4 + 31) // 32) + 1) // 8)
+    assert st == 0 and kr.key_ranges == -(-4 * (-(-(300 + 4 + 31) // 32) + 1) // 2)
     # a window of 100 keys walks at most 5 tiles: one unsplit launch
     st, kr = plan(decode_params(batch=4, max_seq_len=8192, num_pages=512, block_table_stride=512, q_len=4,
                                 window_enabled=1, window_left=100))
