@@ -113,7 +113,9 @@ constexpr int kRangeWavesPerCU = 8;
 // GPU (batches 1-64, 8/2 heads at D 64 and 40/8 at D 128, lengths from half
 // the longest up to it): up to 256 keys the unsplit launch took 3.9-24.5 us
 // against 4.9-27.5 us for key ranges and their merge (0.28-0.90 of the
-// time); from 512 keys the key ranges were faster (1.1-5.4x).
+// time); from 512 keys the key ranges were faster (1.1-5.4x). Measured
+// against key ranges of at least 8 tiles; the 2-tile minimum below it is
+// faster at these sizes, so the limit may be lower at D 128.
 constexpr int kUnsplitMaxTiles = 8;
 
 attn_status_t validate_decode(const attn_decode_params *p, bool check_pointers) {
