@@ -114,7 +114,7 @@ constexpr int kRangeWavesPerCU = 8;
 // the longest up to it): up to 256 keys the unsplit launch took 3.9-24.5 us
 // against 4.9-27.5 us for key ranges and their merge (0.28-0.90 of the
 // time); from 512 keys the key ranges were faster (1.1-5.4x). Measured
-// against key ranges of at least 8 tiles; the 2-tile minimum below it is
+// against key ranges of at least 8 tiles; the 2-tile minimum above is
 // faster at these sizes, so the limit may be lower at D 128.
 constexpr int kUnsplitMaxTiles = 8;
 
